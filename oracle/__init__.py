@@ -1,0 +1,200 @@
+"""CPU oracle for MoE token dispatch / combine -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does, and
+this package imports nothing from the product library.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, built with gcc); this file
+only builds it, loads it with ctypes and marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from collections import namedtuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_CAPACITY = -2
+
+QUANT_NONE = 0
+QUANT_INT8 = 2
+QUANT_MXFP8 = 4
+
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+             "-shared", "-fPIC", "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc into ``oracle/libmoe_oracle.so``."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    global _lib
+    _lib = None
+    return _LIB_PATH
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        i32, i64 = ctypes.c_int, ctypes.c_int64
+        L.oracle_recv_capacity_bound.argtypes = [i32, i32, i32, i32]
+        L.oracle_recv_capacity_bound.restype = i64
+        L.oracle_check_layout_args.argtypes = [i32, i32, i32, i32, i32, i64]
+        L.oracle_check_layout_args.restype = i32
+        L.oracle_check_rows_args.argtypes = [i32, i32, i32, i64, i32]
+        L.oracle_check_rows_args.restype = i32
+        L.oracle_layout.argtypes = [_P, i32, i32, i32, i32, i32, i64] + [_P] * 8
+        L.oracle_layout.restype = i32
+        L.oracle_dispatch.argtypes = [_P, i32, i32, i32, _P, _P, i64, i32, _P, _P, _P]
+        L.oracle_dispatch.restype = i32
+        L.oracle_combine.argtypes = [_P, i64, i32, i32, i32, _P, _P, _P]
+        L.oracle_combine.restype = i32
+        L.oracle_cast_to_fp8_e4m3fn_array.argtypes = [_P, i64, _P]
+        L.oracle_cast_to_fp8_e4m3fn_array.restype = None
+        L.oracle_quant_int8_rows.argtypes = [_P, i32, i32, _P, _P]
+        L.oracle_quant_int8_rows.restype = None
+        L.oracle_quant_mxfp8_rows.argtypes = [_P, i32, i32, _P, _P]
+        L.oracle_quant_mxfp8_rows.restype = None
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code):
+        super().__init__(f"oracle returned status {code}")
+        self.code = code
+
+
+def recv_capacity_bound(T: int, K: int, E: int, a: int) -> int:
+    return int(lib().oracle_recv_capacity_bound(T, K, E, a))
+
+
+def check_layout_args(T, K, E, R, a, cap) -> int:
+    return int(lib().oracle_check_layout_args(T, K, E, R, a, cap))
+
+
+def check_rows_args(T, H, K, cap, quant_mode) -> int:
+    return int(lib().oracle_check_rows_args(T, H, K, cap, quant_mode))
+
+
+Layout = namedtuple("Layout", [
+    "num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
+    "num_recv_tokens_per_expert", "expert_offsets", "token_row", "recv_src",
+    "error_flag", "recv_capacity"])
+
+
+def layout(topk_idx: np.ndarray, num_experts: int, num_ranks: int, expert_alignment: int = 1,
+           recv_capacity: int | None = None) -> Layout:
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    E, R, a = num_experts, num_ranks, expert_alignment
+    cap = recv_capacity_bound(T, K, E, a) if recv_capacity is None else recv_capacity
+    ntpr = np.zeros(R, np.int32)
+    ntpe = np.zeros(E, np.int32)
+    itr = np.zeros((T, R), np.int32)
+    nrtpe = np.zeros(E, np.int32)
+    off = np.zeros(E + 1, np.int32)
+    row = np.zeros((T, K), np.int32)
+    src = np.zeros(max(cap, 0), np.int32)
+    flag = np.zeros(1, np.int32)
+    rc = lib().oracle_layout(_ptr(idx), T, K, E, R, a, cap, _ptr(ntpr), _ptr(ntpe), _ptr(itr),
+                             _ptr(nrtpe), _ptr(off), _ptr(row), _ptr(src), _ptr(flag))
+    if rc != OK:
+        raise OracleError(rc)
+    return Layout(ntpr, ntpe, itr, nrtpe, off, row, src, int(flag[0]), cap)
+
+
+def dispatch(x_bits: np.ndarray, token_row: np.ndarray, recv_capacity: int,
+             topk_weights: np.ndarray | None = None, quant_mode: int = QUANT_NONE,
+             recv_x: np.ndarray | None = None, recv_scales: np.ndarray | None = None,
+             with_weights: bool = False):
+    """Returns (recv_x, recv_scales, recv_weights).  Buffers may be passed in
+    pre-filled with a sentinel; rows that hold no entry are left untouched."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    row = np.ascontiguousarray(token_row, dtype=np.int32)
+    K = row.shape[1]
+    cap = recv_capacity
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    if recv_x is None:
+        dt = np.uint16 if quant_mode == QUANT_NONE else (np.int8 if quant_mode == QUANT_INT8 else np.uint8)
+        recv_x = np.zeros((cap, H), dt)
+    if recv_scales is None:
+        if quant_mode == QUANT_INT8:
+            recv_scales = np.zeros(cap, np.float32)
+        elif quant_mode == QUANT_MXFP8:
+            recv_scales = np.zeros((cap, H // 32), np.uint8)
+    recv_w = np.zeros(cap, np.float32) if with_weights else None
+    rc = lib().oracle_dispatch(_ptr(x), T, H, K, _ptr(row), _ptr(w), cap, quant_mode,
+                               _ptr(recv_x), _ptr(recv_scales), _ptr(recv_w))
+    if rc != OK:
+        raise OracleError(rc)
+    return recv_x, recv_scales, recv_w
+
+
+def combine(y_bits: np.ndarray, token_row: np.ndarray, topk_weights: np.ndarray | None = None) -> np.ndarray:
+    """fp64 weighted sum [T, H]."""
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    cap, H = y.shape
+    row = np.ascontiguousarray(token_row, dtype=np.int32)
+    T, K = row.shape
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    out = np.zeros((T, H), np.float64)
+    rc = lib().oracle_combine(_ptr(y), cap, T, H, K, _ptr(row), _ptr(w), _ptr(out))
+    if rc != OK:
+        raise OracleError(rc)
+    return out
+
+
+def cast_to_fp8_e4m3fn(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.zeros(v.shape, np.uint8)
+    lib().oracle_cast_to_fp8_e4m3fn_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def quant_int8_rows(x_bits: np.ndarray):
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    q = np.zeros((T, H), np.int8)
+    s = np.zeros(T, np.float32)
+    lib().oracle_quant_int8_rows(_ptr(x), T, H, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_mxfp8_rows(x_bits: np.ndarray):
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    q = np.zeros((T, H), np.uint8)
+    s = np.zeros((T, H // 32), np.uint8)
+    lib().oracle_quant_mxfp8_rows(_ptr(x), T, H, _ptr(q), _ptr(s))
+    return q, s
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())

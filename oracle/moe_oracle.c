@@ -1,0 +1,448 @@
+/*
+ * moe_oracle.c -- plain CPU oracle for MoE token dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load or call this file.  It shares no code, header,
+ * table or constant generator with the HIP library, and includes nothing
+ * from it.  It is deliberately slow and literal: every step is the plain
+ * definition of what the pages describe, in the order they describe it.
+ *
+ * Sources (cited by page title and section):
+ *   [NMA]  sgl-kernel-npu deep_ep "Normal Mode API" page: dispatch
+ *          Parameters / Internal Logic / Return Values / Constraints,
+ *          and the combine section.
+ *   [CANN] Huawei CANN "aclnnMoeDistributeDispatchV2" page: Formula
+ *          Cases 1, 3 and 5, and the numbered Constraints.
+ *   [EPBM] Modular MAX "EPBatchManager" page: ep_dispatch() and
+ *          ep_combine().
+ *
+ * Precision: the quantisers run in fp32 because [CANN] Formula Case 3 fixes
+ * the working type (xFp32 = CastToFp32(X)); the MX step is exact power-of-two
+ * scaling followed by an fp8 cast.  The combine sum is not given a precision
+ * by any page, so the oracle forms it in fp64 and returns fp64.
+ *
+ * Pinning: every function here is pinned by CPU tests against closed forms,
+ * invariants, brute force on tiny inputs and library routines (tests named
+ * test_oracle_*).  No function is "parity unpinned".
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
+ * OpenMP only splits the independent per-token loops; results do not depend
+ * on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Status codes.  Same numbering as the library's public header, written out
+ * again here on purpose (the oracle includes nothing from the library). */
+enum {
+    ORC_OK = 0,
+    ORC_ERR_INVALID_ARG = -1,
+    ORC_ERR_CAPACITY = -2,
+};
+
+/* Quantisation modes, numbered as the quantMode of [CANN] Formula. */
+enum { ORC_QUANT_NONE = 0, ORC_QUANT_INT8 = 2, ORC_QUANT_MXFP8 = 4 };
+
+/* ------------------------------------------------------------------------- */
+/* Argument rules (host-side validation the library must reproduce).          */
+/* ------------------------------------------------------------------------- */
+
+/* Worst-case number of expert-grouped receive rows: every (t, k) entry valid
+ * (T*K rows) and every expert padded by at most alignment-1 rows.  This is
+ * the single-GPU form of the receive capacity "A" of [CANN] Constraint 7.
+ * Returns -1 on invalid arguments. */
+int64_t oracle_recv_capacity_bound(int T, int K, int E, int a)
+{
+    if (T < 0 || K < 1 || E < 1 || a < 1)
+        return -1;
+    return (int64_t)T * K + (int64_t)E * (a - 1);
+}
+
+/* Layout arguments.  Ranges: top-k in (0, 16] and experts in (0, 512]
+ * ([NMA] Constraints; [CANN] Constraint 7 "K"); experts divide evenly over
+ * ranks ([CANN] Constraint 7 "localExpertNum"); T >= 0; alignment >= 1;
+ * row indices must fit int32. */
+int oracle_check_layout_args(int T, int K, int E, int R, int a, int64_t cap)
+{
+    if (T < 0 || K < 1 || K > 16 || E < 1 || E > 512 || R < 1 || R > E || E % R != 0 ||
+        a < 1)
+        return ORC_ERR_INVALID_ARG;
+    int64_t bound = oracle_recv_capacity_bound(T, K, E, a);
+    if (bound > INT32_MAX)
+        return ORC_ERR_INVALID_ARG;
+    if (cap < bound || cap > INT32_MAX)
+        return ORC_ERR_CAPACITY;
+    return ORC_OK;
+}
+
+/* Dispatch / combine arguments.  H a positive multiple of 32 ([CANN]
+ * Constraint 7 "H"; 32 is also the MX block, [NMA] Return Values) and at
+ * most 16384. */
+int oracle_check_rows_args(int T, int H, int K, int64_t cap, int quant_mode)
+{
+    if (T < 0 || K < 1 || K > 16 || H < 32 || H > 16384 || H % 32 != 0 || cap < 0 ||
+        cap > INT32_MAX)
+        return ORC_ERR_INVALID_ARG;
+    if (quant_mode != ORC_QUANT_NONE && quant_mode != ORC_QUANT_INT8 &&
+        quant_mode != ORC_QUANT_MXFP8)
+        return ORC_ERR_INVALID_ARG;
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Layout: per-rank / per-expert counts, aligned expert offsets, stable rows  */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [NMA] dispatch Parameters: num_tokens_per_rank [R] int32 (tokens each rank
+ * receives), is_token_in_rank [T, R], num_tokens_per_expert [E], topk_idx
+ * [T, K] int64 with -1 = no expert, expert_alignment; [NMA] Return Values:
+ * num_recv_tokens_per_expert_list, aligned.  [EPBM] ep_dispatch() Returns:
+ * expert_start_indices, row offsets of an expert-grouped buffer.  [CANN]
+ * Constraint 1: deterministic.
+ *
+ * Readings: rank(e) = e / (E / R); an entry outside [-1, E) is an error,
+ * flagged in bit 0 of *error_flag and treated as -1; rows within an expert
+ * follow ascending t*K + k; every expert's row count is rounded up to a
+ * multiple of the alignment (an empty expert keeps zero rows); recv_src of a
+ * row is the flat index t*K + k it holds, or -1 for a padding / unused row.
+ *
+ * Outputs (caller-allocated):
+ *   ntpr[R], ntpe[E] (entries per expert), itr[T*R] (0/1), nrtpe[E] (aligned),
+ *   off[E+1], token_row[T*K] (-1 invalid), recv_src[cap], error_flag[1].
+ */
+int oracle_layout(const int64_t *topk_idx, int T, int K, int E, int R, int a, int64_t cap,
+                  int32_t *ntpr, int32_t *ntpe, int32_t *itr, int32_t *nrtpe, int32_t *off,
+                  int32_t *token_row, int32_t *recv_src, int32_t *error_flag)
+{
+    int rc = oracle_check_layout_args(T, K, E, R, a, cap);
+    if (rc != ORC_OK)
+        return rc;
+    const int L = E / R; /* localExpertNum, [CANN] Constraint 7 */
+    const int64_t M = (int64_t)T * K;
+    int32_t flag = 0;
+
+    /* expert id of each entry after range checking */
+    int32_t *eid = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M > 0 ? M : 1));
+    if (!eid)
+        return ORC_ERR_INVALID_ARG;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t e = topk_idx[i];
+        if (e < -1 || e >= E) {
+            flag |= 1;
+            e = -1;
+        }
+        eid[i] = (int32_t)e;
+    }
+
+    /* count entries per expert */
+    for (int e = 0; e < E; ++e)
+        ntpe[e] = 0;
+    for (int64_t i = 0; i < M; ++i)
+        if (eid[i] >= 0)
+            ntpe[eid[i]] += 1;
+
+    /* is_token_in_rank and tokens per rank */
+    for (int r = 0; r < R; ++r)
+        ntpr[r] = 0;
+    for (int t = 0; t < T; ++t) {
+        for (int r = 0; r < R; ++r)
+            itr[(int64_t)t * R + r] = 0;
+        for (int k = 0; k < K; ++k) {
+            int e = eid[(int64_t)t * K + k];
+            if (e >= 0)
+                itr[(int64_t)t * R + e / L] = 1;
+        }
+        for (int r = 0; r < R; ++r)
+            ntpr[r] += itr[(int64_t)t * R + r];
+    }
+
+    /* aligned counts ("/" is integer division, [CANN] Constraint 11) and
+     * their exclusive prefix sum */
+    off[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        nrtpe[e] = ((ntpe[e] + a - 1) / a) * a;
+        off[e + 1] = off[e] + nrtpe[e];
+    }
+
+    /* stable counting sort of the entries into the expert segments */
+    for (int64_t row = 0; row < cap; ++row)
+        recv_src[row] = -1;
+    int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    if (!cursor) {
+        free(eid);
+        return ORC_ERR_INVALID_ARG;
+    }
+    for (int e = 0; e < E; ++e)
+        cursor[e] = off[e];
+    for (int64_t i = 0; i < M; ++i) {
+        int e = eid[i];
+        if (e < 0) {
+            token_row[i] = -1;
+            continue;
+        }
+        int32_t row = cursor[e]++;
+        token_row[i] = row;
+        recv_src[row] = (int32_t)i;
+    }
+    free(cursor);
+    free(eid);
+    *error_flag = flag;
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Element codecs                                                             */
+/* ------------------------------------------------------------------------- */
+
+/* CastToFp32 of a bf16 value: the 16 bits are the top half of an fp32. */
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* CastToFp8 for float8_e4m3fn ([NMA] Return Values names the type; [CANN]
+ * Formula Case 5 the cast).  e4m3fn: 1 sign bit, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, 0x7F/0xFF are NaN, largest finite value
+ * 1.75 * 2^8 = 448, smallest normal 2^-6, subnormals are multiples of 2^-9.
+ * Rounding is to nearest, ties to even (the default IEEE mode); magnitudes
+ * above 448 saturate to 448 (the "fn" format has no infinity).  The sign of
+ * zero is kept.  Computed in double, where every step below is exact except
+ * the one explicit rounding. */
+uint8_t oracle_cast_to_fp8_e4m3fn(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a > 448.0)
+        a = 448.0;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: a = q * 2^-9 with q in 0..8 (q = 8 is 2^-6, the
+         * smallest normal, whose code is also 8) */
+        double q = nearbyint(a * 512.0);
+        return (uint8_t)(sign | (uint8_t)q);
+    }
+    int e2;
+    double f = frexp(a, &e2);            /* a = f * 2^e2, f in [0.5, 1) */
+    int exponent = e2 - 1;               /* a = (1 + m/8) * 2^exponent   */
+    double m = nearbyint((2.0 * f - 1.0) * 8.0);
+    if (m == 8.0) {                      /* mantissa rounded up into the next binade */
+        m = 0.0;
+        exponent += 1;
+    }
+    return (uint8_t)(sign | (uint8_t)(((exponent + 7) << 3) | (int)m));
+}
+
+/* Encode n values (test hook for the exhaustive encoder pin). */
+void oracle_cast_to_fp8_e4m3fn_array(const float *v, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_cast_to_fp8_e4m3fn((double)v[i]);
+}
+
+/* [CANN] Formula Case 3 (quantMode 2, per-token dynamic quantisation), for
+ * one token row, without smoothing scales:
+ *   xFp32         = CastToFp32(X)
+ *   dynamicScales = dstTypeMax / Max(Abs(xFp32))       dstTypeMax = 127 (int8)
+ *   quantOut      = CastToInt8(xFp32 * dynamicScales)  round half to even
+ *   scale out     = 1.0 / dynamicScales
+ * all in fp32.  Reading for the degenerate row: when dynamicScales is not
+ * finite (an all-zero row, or a maximum so small that 127/max overflows) the
+ * codes are 0 and the scale is 1.0/dynamicScales = 0. */
+static void quant_int8_row(const uint16_t *x, int H, int8_t *quantOut, float *scale_out)
+{
+    float maxabs = 0.0f;
+    for (int h = 0; h < H; ++h) {
+        float xFp32 = bf16_to_f32(x[h]);
+        float ab = fabsf(xFp32);
+        if (ab > maxabs)
+            maxabs = ab;
+    }
+    const float dstTypeMax = 127.0f;
+    float dynamicScales = dstTypeMax / maxabs;
+    if (!isfinite(dynamicScales)) {
+        for (int h = 0; h < H; ++h)
+            quantOut[h] = 0;
+    } else {
+        for (int h = 0; h < H; ++h) {
+            float xFp32 = bf16_to_f32(x[h]);
+            float prod = xFp32 * dynamicScales; /* one fp32 multiply */
+            float q = rintf(prod);              /* ties to even */
+            quantOut[h] = (int8_t)q;
+        }
+    }
+    *scale_out = 1.0f / dynamicScales;
+}
+
+/* [CANN] Formula Case 5 (quantMode 4, MXFP8), for one token row, per block of
+ * 32 consecutive elements (the block size of [NMA] Return Values):
+ *   sharedExp     = Floor(log2(max(|x|))) - emax      emax = 8 for e4m3fn (448 = 1.75*2^8)
+ *   dynamicScales = 2^sharedExp
+ *   quantOut      = CastToFp8(X / dynamicScales)
+ * Readings: the block maximum is taken of |x|; sharedExp is clamped below at
+ * -127, the smallest exponent an e8m0 byte holds, and an all-zero block uses
+ * -127; the stored float8_e8m0fnu scale is 2^sharedExp, i.e. the byte
+ * sharedExp + 127, so that x ~= code * 2^sharedExp. */
+static void quant_mxfp8_row(const uint16_t *x, int H, uint8_t *quantOut, uint8_t *scales_out)
+{
+    const int emax = 8;
+    for (int blk = 0; blk < H / 32; ++blk) {
+        const uint16_t *xb = x + 32 * blk;
+        double maxabs = 0.0;
+        for (int j = 0; j < 32; ++j) {
+            double ab = fabs((double)bf16_to_f32(xb[j]));
+            if (ab > maxabs)
+                maxabs = ab;
+        }
+        int sharedExp = -127;
+        if (maxabs > 0.0) {
+            sharedExp = (int)floor(log2(maxabs)) - emax;
+            if (sharedExp < -127)
+                sharedExp = -127;
+        }
+        double dynamicScales = ldexp(1.0, sharedExp);
+        for (int j = 0; j < 32; ++j)
+            quantOut[32 * blk + j] =
+                oracle_cast_to_fp8_e4m3fn((double)bf16_to_f32(xb[j]) / dynamicScales);
+        scales_out[blk] = (uint8_t)(sharedExp + 127);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Dispatch                                                                   */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Dispatch copies every token to each of its selected experts' rows of the
+ * expert-grouped receive buffer ([NMA] dispatch description; [CANN]
+ * Description and Formula Case 1: expandXOut holds the tokens; [EPBM]
+ * ep_dispatch(): output_tokens "ready for grouped matmul").  Quantisation,
+ * when asked for, is applied to the source token once and the same codes and
+ * scale go to all of its rows ([CANN] Formula: quantOut is formed from X
+ * before the exchange).
+ *
+ * x: bf16 bits [T, H].  token_row: [T*K] from oracle_layout.  topk_weights:
+ * [T*K] or NULL.  recv_x: [cap, H] of uint16 (bf16), int8 or uint8 (e4m3)
+ * elements.  recv_scales: NULL (bf16), float [cap] (int8) or uint8
+ * [cap * H/32] (MXFP8, row-major).  recv_weights: [cap] or NULL; receives the
+ * weight of the (t, k) entry a row holds.  Rows not named by token_row are
+ * left untouched.
+ */
+int oracle_dispatch(const uint16_t *x, int T, int H, int K, const int32_t *token_row,
+                    const float *topk_weights, int64_t cap, int quant_mode, void *recv_x,
+                    void *recv_scales, float *recv_weights)
+{
+    int rc = oracle_check_rows_args(T, H, K, cap, quant_mode);
+    if (rc != ORC_OK)
+        return rc;
+    if (T > 0 && (!x || !token_row || !recv_x))
+        return ORC_ERR_INVALID_ARG;
+    if (T > 0 && quant_mode != ORC_QUANT_NONE && !recv_scales)
+        return ORC_ERR_INVALID_ARG;
+
+#pragma omp parallel
+    {
+        int8_t *q8 = (int8_t *)malloc((size_t)H);
+        uint8_t *qf8 = (uint8_t *)malloc((size_t)H);
+        uint8_t *sc8 = (uint8_t *)malloc((size_t)H / 32);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            const uint16_t *xt = x + (int64_t)t * H;
+            float s_int8 = 0.0f;
+            if (quant_mode == ORC_QUANT_INT8)
+                quant_int8_row(xt, H, q8, &s_int8);
+            else if (quant_mode == ORC_QUANT_MXFP8)
+                quant_mxfp8_row(xt, H, qf8, sc8);
+            for (int k = 0; k < K; ++k) {
+                int32_t row = token_row[(int64_t)t * K + k];
+                if (row < 0 || row >= cap)
+                    continue;
+                if (quant_mode == ORC_QUANT_NONE) {
+                    memcpy((uint16_t *)recv_x + (int64_t)row * H, xt, sizeof(uint16_t) * (size_t)H);
+                } else if (quant_mode == ORC_QUANT_INT8) {
+                    memcpy((int8_t *)recv_x + (int64_t)row * H, q8, (size_t)H);
+                    ((float *)recv_scales)[row] = s_int8;
+                } else {
+                    memcpy((uint8_t *)recv_x + (int64_t)row * H, qf8, (size_t)H);
+                    memcpy((uint8_t *)recv_scales + (int64_t)row * (H / 32), sc8, (size_t)H / 32);
+                }
+                if (recv_weights)
+                    recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;
+            }
+        }
+        free(q8);
+        free(qf8);
+        free(sc8);
+    }
+    return ORC_OK;
+}
+
+/* Test hooks: the per-token quantisers on their own. */
+void oracle_quant_int8_rows(const uint16_t *x, int T, int H, int8_t *q, float *scales)
+{
+    for (int t = 0; t < T; ++t)
+        quant_int8_row(x + (int64_t)t * H, H, q + (int64_t)t * H, scales + t);
+}
+
+void oracle_quant_mxfp8_rows(const uint16_t *x, int T, int H, uint8_t *q, uint8_t *scales)
+{
+    for (int t = 0; t < T; ++t)
+        quant_mxfp8_row(x + (int64_t)t * H, H, q + (int64_t)t * H, scales + (int64_t)t * (H / 32));
+}
+
+/* ------------------------------------------------------------------------- */
+/* Combine                                                                    */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Combine brings each token's expert outputs back and takes their weighted
+ * sum ([NMA] combine Description: "multiply by weights and sum"; [EPBM]
+ * ep_combine(): weighted sum of routed expert outputs, result
+ * (num_local_tokens, hidden)):
+ *   out[t, h] = sum over valid k of  w[t, k] * y[token_row[t, k], h]
+ * with w = 1 when no weights are given ([NMA] combine Parameters:
+ * topk_weights is optional).  Formed in fp64, k ascending; a token with no
+ * valid entry gets 0.  y: bf16 bits [cap, H]; out: double [T, H].
+ */
+int oracle_combine(const uint16_t *y, int64_t cap, int T, int H, int K, const int32_t *token_row,
+                   const float *topk_weights, double *out)
+{
+    int rc = oracle_check_rows_args(T, H, K, cap, ORC_QUANT_NONE);
+    if (rc != ORC_OK)
+        return rc;
+    if (T > 0 && (!y || !token_row || !out))
+        return ORC_ERR_INVALID_ARG;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        double *o = out + (int64_t)t * H;
+        for (int h = 0; h < H; ++h)
+            o[h] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            int32_t row = token_row[(int64_t)t * K + k];
+            if (row < 0 || row >= cap)
+                continue;
+            double w = topk_weights ? (double)topk_weights[(int64_t)t * K + k] : 1.0;
+            const uint16_t *yr = y + (int64_t)row * H;
+            for (int h = 0; h < H; ++h)
+                o[h] += w * (double)bf16_to_f32(yr[h]);
+        }
+    }
+    return ORC_OK;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

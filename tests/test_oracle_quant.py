@@ -1,0 +1,305 @@
+"""Pins for the oracle's dispatch and its two quantisers.
+
+int8 (per-token dynamic, CANN aclnnMoeDistributeDispatchV2 Formula Case 3):
+  closed-form rows (integer rows, power-of-two scaled rows, half-way ties),
+  an exact-rational evaluation of the fp32 formula on sample rows, the
+  degenerate rows, and invariants (max code 127, reconstruction bound,
+  monotonicity) at workload scale.
+MXFP8 e4m3 (Formula Case 5):
+  the element cast against torch's float8_e4m3fn cast on every bf16 value and
+  on random fp32 values, a round trip of every finite code through the
+  format definition, the block exponent against frexp, a worked block, and
+  invariants (block maximum lands in the top binade; reconstruction bound).
+dispatch: rows are copies of the per-token result at the layout's rows.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from combine_moe_get_dispatch_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FACTS = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+
+
+def bf16(vals):
+    return W.f32_to_bf16_bits(np.asarray(vals, np.float32))
+
+
+def row32(vals, H=32):
+    v = np.zeros(H, np.float32)
+    v[:len(vals)] = vals
+    return bf16(v)[None, :]
+
+
+# ----------------------------------------------------------------------------- int8
+
+def fp32_round(q: Fraction) -> Fraction:
+    """Exact rational -> nearest fp32 (normal range), ties to even."""
+    if q == 0:
+        return Fraction(0)
+    s = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert -126 <= e <= 127
+    ulp = Fraction(2) ** (e - 23)
+    n = a / ulp
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return s * fl * ulp
+
+
+def rne_int(q: Fraction) -> int:
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl
+
+
+def exact_int8(xrow_f32):
+    xs = [Fraction(float(v)) for v in xrow_f32]
+    m = max(abs(v) for v in xs)
+    ds = fp32_round(Fraction(127) / m)
+    q = [rne_int(fp32_round(v * ds)) for v in xs]
+    s = fp32_round(1 / ds)
+    return q, float(s)
+
+
+def test_int8_integer_rows(orc):
+    # max |x| = 127 gives dynamicScales = 127/127 = 1 exactly: codes are x, scale 1.
+    rng = np.random.default_rng(1)
+    v = rng.integers(-127, 128, size=(16, 64)).astype(np.float32)
+    v[:, 7] = 127
+    v[::2, 7] = -127
+    q, s = orc.quant_int8_rows(bf16(v))
+    np.testing.assert_array_equal(q, v.astype(np.int8))
+    np.testing.assert_array_equal(s, np.ones(16, np.float32))
+
+
+@pytest.mark.parametrize("j", [-30, -7, -1, 1, 5, 20, 60])
+def test_int8_power_of_two_rows(orc, j):
+    # x = v * 2^j with max |v| = 127: dynamicScales = 2^-j exactly, codes = v, scale = 2^j.
+    rng = np.random.default_rng(j + 100)
+    v = rng.integers(-127, 128, size=(4, 96)).astype(np.float32)
+    v[:, 0] = 127
+    q, s = orc.quant_int8_rows(bf16(v * np.float32(2.0 ** j)))
+    np.testing.assert_array_equal(q, v.astype(np.int8))
+    np.testing.assert_array_equal(s, np.full(4, 2.0 ** j, np.float32))
+
+
+def test_int8_ties_round_half_to_even(orc):
+    # dynamicScales = 1 (max 127): x*1 = x, so x.5 values are exact ties.
+    q, s = orc.quant_int8_rows(row32([127, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, -3.5, 126.5]))
+    assert q[0, :9].tolist() == [127, 2, 4, -2, 0, 2, 0, -4, 126]
+    assert s[0] == 1.0
+
+
+def test_int8_hand_worked_row(orc):
+    # max = 3: 127/3 = 42 + 1/3; fp32 keeps 18 fraction bits of 1/3 = 0.0101..01|0101..
+    # (rest < half) -> dynamicScales = 42 + (1 - 2^-18)/3.  3 * that = 127 - 2^-18 is
+    # exactly half-way between fp32 neighbours 127 - 2^-17 and 127 -> even -> 127.0.
+    # 1 * ds = 42.33 -> 42; -0.5 * ds = -21.17 -> -21; 0.25 * ds = 10.58 -> 11.
+    q, s = orc.quant_int8_rows(row32([3.0, 1.0, -0.5, 0.25]))
+    assert q[0, :4].tolist() == [127, 42, -21, 11]
+    assert (q[0, 4:] == 0).all()
+    ds = Fraction(42) + (1 - Fraction(1, 2 ** 18)) / 3
+    assert float(ds) == float(np.float32(127.0) / np.float32(3.0))
+    assert s[0] == float(fp32_round(1 / ds))
+
+
+def test_int8_exact_rational_evaluation(orc):
+    """The fp32 formula evaluated in exact rationals with IEEE rounding steps."""
+    rng = np.random.default_rng(7)
+    x = bf16(rng.standard_normal((6, 64)).astype(np.float32) * np.float32(3.0))
+    q, s = orc.quant_int8_rows(x)
+    xf = W.bf16_bits_to_f32(x)
+    for t in range(x.shape[0]):
+        eq, es = exact_int8(xf[t])
+        assert q[t].tolist() == eq
+        assert s[t] == np.float32(es)
+
+
+def test_int8_degenerate_rows(orc):
+    # all-zero row and a row so small that 127/max overflows fp32: codes 0, scale 1/inf = 0
+    tiny = np.float32(2.0 ** -126)
+    q, s = orc.quant_int8_rows(np.concatenate([row32([0.0]), row32([tiny, -tiny])]))
+    assert (q == 0).all()
+    assert s.tolist() == [0.0, 0.0]
+    # just above the overflow threshold the row is quantised normally
+    q, s = orc.quant_int8_rows(row32([np.float32(2.0 ** -120), 0.0]))
+    assert q[0, 0] == 127 and s[0] > 0
+
+
+def test_int8_invariants_at_workload_scale(orc):
+    w = W.WORKLOADS[2]
+    inp = W.generate(w, num_tokens=256)
+    q, s = orc.quant_int8_rows(inp.x_bits)
+    x = W.bf16_bits_to_f32(inp.x_bits).astype(np.float64)
+    qa = q.astype(np.float64)
+    assert (np.abs(q).max(axis=1) == FACTS["int8_dst_type_max"]["value"]).all()
+    assert ((np.sign(qa) == np.sign(x)) | (q == 0)).all()
+    err = np.abs(x - qa * s[:, None].astype(np.float64))
+    assert (err <= s[:, None] * (0.5 + 2.0 ** -15)).all()
+    m = np.abs(x).max(axis=1)
+    np.testing.assert_allclose(s.astype(np.float64) * 127.0, m, rtol=2.0 ** -22)
+    order = np.argsort(x, axis=1)
+    assert (np.diff(np.take_along_axis(q, order, axis=1).astype(np.int32), axis=1) >= 0).all()
+
+
+# ----------------------------------------------------------------------------- e4m3
+
+def e4m3fn_value(code: int) -> float:
+    """Value of an e4m3fn code from the format definition: sign, 4-bit exponent
+    with bias 7, 3-bit mantissa; exponent field 0 is subnormal (m * 2^-9)."""
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    return s * (m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+
+def test_e4m3_every_finite_code_round_trips(orc):
+    codes = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    vals = np.array([e4m3fn_value(c) for c in codes], np.float32)
+    np.testing.assert_array_equal(orc.cast_to_fp8_e4m3fn(vals), np.array(codes, np.uint8))
+    assert e4m3fn_value(0x7E) == FACTS["e4m3fn_max_normal"]["value"]
+
+
+def test_e4m3_all_bf16_values_vs_torch(orc):
+    """Every finite bf16 pattern (every 8-bit-significand fp32 value, which is
+    the whole domain of the MX element cast) against torch's RNE cast after
+    saturation to +-448."""
+    import torch
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    b = b[((b >> 7) & 0xFF) != 0xFF]
+    v = W.bf16_bits_to_f32(b)
+    got = orc.cast_to_fp8_e4m3fn(v)
+    ref = torch.from_numpy(np.clip(v, -448.0, 448.0)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_random_fp32_vs_torch(orc):
+    import torch
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal(1 << 20) * np.exp2(rng.uniform(-14, 10, 1 << 20))).astype(np.float32)
+    got = orc.cast_to_fp8_e4m3fn(v)
+    ref = torch.from_numpy(np.clip(v, -448.0, 448.0)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_saturates_instead_of_nan(orc):
+    got = orc.cast_to_fp8_e4m3fn(np.array([448, 463.9, 464, 479, 480, 511, 1e30, np.inf, -500], np.float32))
+    assert got.tolist() == [0x7E] * 8 + [0xFE]
+
+
+# ----------------------------------------------------------------------------- MXFP8 blocks
+
+def test_mx_hand_worked_block(orc):
+    # block max 3: floor(log2 3) = 1, sharedExp = 1 - emax(8) = -7, byte -7 + 127 = 120.
+    # x / 2^-7: 3 -> 384 = 1.5 * 2^8 -> (15<<3)|4 = 0x7C; 1 -> 128 = 2^7 -> 0x70;
+    # -0.5 -> -64 = -(2^6) -> 0x80|0x68 = 0xE8; 0.01171875 (3 * 2^-8) -> 1.5 = 0x3C.
+    q, s = orc.quant_mxfp8_rows(row32([3.0, 1.0, -0.5, 0.01171875]))
+    assert s[0].tolist() == [120]
+    assert q[0, :4].tolist() == [0x7C, 0x70, 0xE8, 0x3C]
+    assert (q[0, 4:] == 0).all()
+
+
+def test_mx_scale_exponent_vs_frexp(orc):
+    inp = W.generate(W.WORKLOADS[3], num_tokens=128)
+    q, s = orc.quant_mxfp8_rows(inp.x_bits)
+    x = W.bf16_bits_to_f32(inp.x_bits).astype(np.float64)
+    T, H = x.shape
+    m = np.abs(x.reshape(T, H // 32, 32)).max(axis=2)
+    _, e = np.frexp(m)                      # m = f * 2^e, f in [0.5, 1): floor(log2 m) = e - 1
+    emax = FACTS["e4m3fn_emax"]["value"]
+    se = np.where(m > 0, np.maximum(e - 1 - emax, -127), -127)
+    np.testing.assert_array_equal(s.astype(np.int64), se + 127)
+
+
+def test_mx_invariants_at_workload_scale(orc):
+    inp = W.generate(W.WORKLOADS[3], num_tokens=512)
+    q, s = orc.quant_mxfp8_rows(inp.x_bits)
+    T, H = q.shape
+    x = W.bf16_bits_to_f32(inp.x_bits).astype(np.float64).reshape(T, H // 32, 32)
+    se = s.astype(np.int64) - 127
+    dec_lut = np.array([e4m3fn_value(c) if (c & 0x7F) != 0x7F else np.nan for c in range(256)])
+    dec = dec_lut[q].reshape(T, H // 32, 32)
+    # the block maximum scales into [256, 512): its code has exponent field 15
+    amax = np.argmax(np.abs(x), axis=2)
+    top = np.take_along_axis(q.reshape(T, H // 32, 32), amax[..., None], axis=2)[..., 0]
+    assert (((top & 0x7F) >> 3) == 15).all()
+    # reconstruction: half an e4m3 ulp of the scaled value, or the saturation gap (<= 64)
+    v = x / np.exp2(se)[..., None]
+    ebin = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6)))
+    half_ulp = np.exp2(ebin - 4)
+    sat = np.abs(v) > 448
+    err = np.abs(v - dec)
+    assert (err[~sat] <= half_ulp[~sat]).all()
+    assert (err[sat] <= 64).all()
+    assert sat.any(axis=2).mean() > 0.05  # the saturation reading is exercised by these blocks
+
+
+def test_mx_zero_and_tiny_blocks(orc):
+    x = np.zeros((1, 64), np.uint16)
+    x[0, 1] = 0x8000                      # -0.0
+    x[0, 33] = 0x0001                     # smallest bf16 subnormal, 2^-133
+    q, s = orc.quant_mxfp8_rows(x)
+    assert s[0].tolist() == [0, 0]        # sharedExp clamped to -127
+    assert q[0, 1] == 0x80 and (np.delete(q[0, :32], 1) == 0).all()
+    assert q[0, 33] == 0x08               # 2^-133 / 2^-127 = 2^-6, the smallest normal
+    big = bf16(np.full((1, 32), 3.0e38, np.float32))
+    q2, s2 = orc.quant_mxfp8_rows(big)
+    assert s2[0, 0] == 127 + 127 - 8
+
+
+# ----------------------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("quant", [0, 2, 4])
+def test_dispatch_rows_are_per_token_results(orc, quant):
+    w = W.Workload("t", 48, 128, 12, 3, 4, 8, quant, drop_prob=0.2, seed_index=11)
+    inp = W.generate(w)
+    lay = orc.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    cap = lay.recv_capacity
+    H = w.hidden
+    if quant == 0:
+        sentinel = np.full((cap, H), 0xFFFF, np.uint16)
+        sc = None
+    elif quant == 2:
+        sentinel = np.full((cap, H), 0x55, np.int8)
+        sc = np.full(cap, -7.0, np.float32)
+    else:
+        sentinel = np.full((cap, H), 0x7F, np.uint8)
+        sc = np.full((cap, H // 32), 0xFF, np.uint8)
+    rx, rs, rw = orc.dispatch(inp.x_bits, lay.token_row, cap, inp.topk_weights, quant,
+                              recv_x=sentinel.copy(), recv_scales=None if sc is None else sc.copy(),
+                              with_weights=True)
+    if quant == 2:
+        tq, ts = orc.quant_int8_rows(inp.x_bits)
+    elif quant == 4:
+        tq, ts = orc.quant_mxfp8_rows(inp.x_bits)
+    else:
+        tq, ts = inp.x_bits, None
+    used = np.zeros(cap, bool)
+    for t in range(w.num_tokens):
+        for k in range(w.num_topk):
+            r = lay.token_row[t, k]
+            if r < 0:
+                continue
+            used[r] = True
+            np.testing.assert_array_equal(rx[r], tq[t])
+            if ts is not None:
+                np.testing.assert_array_equal(rs[r], ts[t])
+            assert rw[r] == inp.topk_weights[t, k]
+    np.testing.assert_array_equal(rx[~used], sentinel[~used])
+    if sc is not None:
+        np.testing.assert_array_equal(rs[~used], sc[~used])
