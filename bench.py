@@ -1,0 +1,213 @@
+"""Benchmark: MoE dispatch + combine on one MI355X.
+
+One step = moe_get_dispatch_layout -> moe_dispatch -> moe_combine on one HIP
+stream, over the whole batch (identity experts: the combine input is the
+receive buffer itself for bf16, or its bf16 dequantisation -- made once,
+outside the timed region -- for int8 / MXFP8).  Inputs are resident in HBM
+before timing starts.  W untimed warm-up steps, then exactly K timed steps
+bracketed by torch.cuda.synchronize().  HIP events recorded on the stream the
+kernels run on give each stage's average duration.
+
+Prints ONE JSON line.  `value` = effective HBM GB/s = algorithmic bytes per
+step * K / elapsed; algorithmic bytes count x read once, each valid expanded
+row written once and read once, the output written once, and the index
+traffic (padding rows are never touched and not counted).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="bf16_4096x7168_e256_top8")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU time budget for the oracle baseline (0 = skip)")
+    p.add_argument("--no-check", action="store_true", help="skip the post-run sanity check")
+    return p.parse_args()
+
+
+def stage_bytes(T, H, K, R, E, V, cap, quant):
+    """Algorithmic bytes of each stage (see module docstring)."""
+    s_q = 2 if quant == 0 else 1
+    sigma = 0 if quant == 0 else (4 if quant == 2 else H // 32)
+    layout = 8 * T * K + 4 * T * R + 4 * R + 8 * E + 4 * (E + 1) + 4 * T * K + 4 * cap + 4
+    dispatch = 2 * T * H + 4 * T * K + V * (H * s_q + sigma)
+    combine = 2 * V * H + 8 * T * K + 2 * T * H
+    return {"layout": layout, "dispatch": dispatch, "combine": combine}
+
+
+def cpu_baseline(inp, w, quant, budget_s, bytes_fn):
+    """The oracle, as it is, on the same workload, repeated until the time
+    budget is used (at least once)."""
+    import numpy as np
+    import oracle
+    E, R, a = w.num_experts, w.num_ranks, w.expert_alignment
+    reps, total_bytes = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        ol = oracle.layout(inp.topk_idx, E, R, a)
+        rx, rs, _ = oracle.dispatch(inp.x_bits, ol.token_row, ol.recv_capacity, None, quant)
+        if quant == 0:
+            y = rx
+        else:
+            y = np.zeros((ol.recv_capacity, w.hidden), np.uint16)   # expert output stand-in
+        oracle.combine(y, ol.token_row, inp.topk_weights)
+        reps += 1
+        V = int((inp.topk_idx >= 0).sum())
+        total_bytes += sum(bytes_fn(V, ol.recv_capacity).values())
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(total_bytes / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"full workload ({w.num_tokens} tokens), layout+dispatch+combine, {reps} repetition(s) "
+                      f"in {el:.1f} s", "tokens_per_s": round(reps * w.num_tokens / el, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this library runs the path on a single GPU, virtual ranks are expert partitions)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from combine_moe_get_dispatch_amd import build_lib
+    if not os.path.exists(build_lib.LIB_PATH):
+        build_lib.build(verbose=True)
+    import combine_moe_get_dispatch_amd as moe
+    from combine_moe_get_dispatch_amd import workloads as W
+
+    w = W.BY_NAME[args.workload]
+    T, H, K, E, R, a, quant = (w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
+                               w.expert_alignment, w.quant_mode)
+    dev = torch.device("cuda", 0)
+    inp = W.generate(w)
+    V = int((inp.topk_idx >= 0).sum())
+
+    idx = torch.from_numpy(inp.topk_idx).to(dev)
+    x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    wt = torch.from_numpy(inp.topk_weights).to(dev)
+    lay = moe.allocate_layout(T, K, E, R, a, device=dev)
+    cap = lay.recv_capacity
+    rx, rs, _ = moe.allocate_recv(lay, H, quant)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    # identity expert output (made once, outside the timed region)
+    moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)
+    moe.moe_dispatch(x, lay, None, quant, recv_x=rx, recv_scales=rs)
+    if quant == 0:
+        y = rx
+    elif quant == 2:
+        y = (rx.float() * rs[:, None]).to(torch.bfloat16)
+    else:
+        y = (rx.float().view(cap, H // 32, 32) * torch.exp2(rs.float() - 127.0)[:, :, None]).view(cap, H)
+        y = torch.nan_to_num(y).to(torch.bfloat16)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)
+        if ev is not None:
+            ev[1].record()
+        moe.moe_dispatch(x, lay, None, quant, recv_x=rx, recv_scales=rs)
+        if ev is not None:
+            ev[2].record()
+        moe.moe_combine(y, lay, wt, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps; events on the stream the kernels use
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    st = {"layout": [], "dispatch": [], "combine": []}
+    for ev in events:
+        st["layout"].append(ev[0].elapsed_time(ev[1]) * 1e3)
+        st["dispatch"].append(ev[1].elapsed_time(ev[2]) * 1e3)
+        st["combine"].append(ev[2].elapsed_time(ev[3]) * 1e3)
+    avg_us = {k: float(np.mean(v)) for k, v in st.items()}
+    med_us = {k: float(np.median(v)) for k, v in st.items()}
+
+    sb = stage_bytes(T, H, K, R, E, V, cap, quant)
+    step_bytes = sum(sb.values())
+    ms_per_step = elapsed / args.steps * 1e3
+    gbs = step_bytes * args.steps / elapsed / 1e9
+    tokens_per_s = T * args.steps / elapsed
+
+    dom = max(("dispatch", "combine"), key=lambda k: avg_us[k])
+    achieved = sb[dom] / (avg_us[dom] * 1e-6) / 1e9
+
+    if not args.no_check:
+        # cheap sanity check after timing: every dispatched row is its token
+        src = lay.recv_src.long()
+        u = src >= 0
+        if quant == 0:
+            assert torch.equal(rx.view(torch.int16)[u], x.view(torch.int16)[src[u] // K])
+        assert int(lay.error_flag.item()) == 0
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(inp, w, quant, args.cpu_seconds,
+                           lambda v, c: stage_bytes(T, H, K, R, E, v, c, quant))
+
+    qname = {0: "bf16", 2: "int8", 4: "mxfp8_e4m3"}[quant]
+    rec = {
+        "metric": "dispatch+combine effective HBM GB/s and tokens/s (% of peak) at 4096x7168 top-8",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if quant == 0 else f"bf16->{qname}",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.describe(), "num_tokens": T, "hidden": H,
+                   "num_experts": E, "num_virtual_ranks": R, "top_k": K, "expert_alignment": a,
+                   "quant": qname, "valid_entries": V, "recv_capacity": cap,
+                   "parallelism": "single GPU (virtual expert ranks)"},
+        "tokens_per_s": round(tokens_per_s, 1),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": step_bytes,
+        "stage_bytes": sb,
+        "stage_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
+        "stage_median_us": {k: round(v, 2) for k, v in med_us.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,263 @@
+"""MoE token dispatch / combine on one AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libmoe_dispatch_combine.so``
+(declared in ``include/moe_dispatch_combine.h``).  The three calls keep the
+C names:
+
+    layout = moe_get_dispatch_layout(topk_idx, num_experts, num_ranks, expert_alignment)
+    recv_x, recv_scales, recv_weights = moe_dispatch(x, layout, topk_weights, quant_mode)
+    out = moe_combine(expert_out, layout, topk_weights)
+
+This module only checks tensor metadata and passes device pointers and
+torch's current HIP stream to the library; every step of the path runs in
+the library's HIP kernels.  There is no CPU fallback: if the library is not
+built, the first call raises.  torch is used for device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_dispatch_combine.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_CAPACITY = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+
+QUANT_NONE = 0
+QUANT_INT8_PER_TOKEN = 2
+QUANT_MXFP8_E4M3 = 4
+
+FLAG_BAD_EXPERT_ID = 1
+
+__all__ = [
+    "moe_get_dispatch_layout", "moe_dispatch", "moe_combine", "moe_recv_capacity_bound",
+    "moe_layout_workspace_bytes", "DispatchLayout", "allocate_layout", "allocate_recv",
+    "num_recv_tokens_per_expert_list", "MoeError", "lib",
+    "QUANT_NONE", "QUANT_INT8_PER_TOKEN", "QUANT_MXFP8_E4M3",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, func: str, code: int):
+        msg = lib().moe_status_string(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{func} failed with status {code}: {msg}")
+        self.code = code
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with combine_moe_get_dispatch_amd.build_lib.build() "
+                "(hipcc, gfx950). There is no CPU fallback.")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.moe_recv_capacity_bound.argtypes = [i32, i32, i32, i32]
+        L.moe_recv_capacity_bound.restype = i64
+        L.moe_layout_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.moe_layout_workspace_bytes.restype = sz
+        L.moe_get_dispatch_layout.argtypes = [P, i32, i32, i32, i32, i32, i64] + [P] * 8 + [P, sz, P]
+        L.moe_get_dispatch_layout.restype = i32
+        L.moe_dispatch.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
+        L.moe_dispatch.restype = i32
+        L.moe_combine.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
+        L.moe_combine.restype = i32
+        L.moe_status_string.argtypes = [i32]
+        L.moe_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def moe_recv_capacity_bound(num_tokens: int, num_topk: int, num_experts: int,
+                            expert_alignment: int) -> int:
+    return int(lib().moe_recv_capacity_bound(num_tokens, num_topk, num_experts, expert_alignment))
+
+
+def moe_layout_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int, num_ranks: int) -> int:
+    return int(lib().moe_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks))
+
+
+@dataclasses.dataclass
+class DispatchLayout:
+    """Outputs of moe_get_dispatch_layout; (expert_offsets, token_row,
+    recv_src) plus the sizes form the handle combine needs."""
+    num_tokens_per_rank: torch.Tensor          # int32 [R]
+    num_tokens_per_expert: torch.Tensor        # int32 [E]
+    is_token_in_rank: torch.Tensor             # int32 [T, R]
+    num_recv_tokens_per_expert: torch.Tensor   # int32 [E], aligned
+    expert_offsets: torch.Tensor               # int32 [E + 1]
+    token_row: torch.Tensor                    # int32 [T, K]
+    recv_src: torch.Tensor                     # int32 [cap]
+    error_flag: torch.Tensor                   # int32 [1]
+    workspace: torch.Tensor                    # uint8 [workspace bytes]
+    num_tokens: int
+    num_topk: int
+    num_experts: int
+    num_ranks: int
+    expert_alignment: int
+    recv_capacity: int
+
+
+def allocate_layout(num_tokens: int, num_topk: int, num_experts: int, num_ranks: int,
+                    expert_alignment: int = 1, recv_capacity: Optional[int] = None,
+                    device=None) -> DispatchLayout:
+    device = torch.device("cuda") if device is None else torch.device(device)
+    T, K, E, R, a = num_tokens, num_topk, num_experts, num_ranks, expert_alignment
+    bound = moe_recv_capacity_bound(T, K, E, a)
+    if bound < 0:
+        raise ValueError("invalid layout sizes")
+    cap = bound if recv_capacity is None else int(recv_capacity)
+    ws = moe_layout_workspace_bytes(T, K, E, R)
+    i32 = dict(dtype=torch.int32, device=device)
+    return DispatchLayout(
+        torch.empty(R, **i32), torch.empty(E, **i32), torch.empty((T, R), **i32),
+        torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty((T, K), **i32),
+        torch.empty(max(cap, 0), **i32), torch.empty(1, **i32),
+        torch.empty(max(ws, 1), dtype=torch.uint8, device=device),
+        T, K, E, R, a, cap)
+
+
+def moe_get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                            expert_alignment: int = 1, recv_capacity: Optional[int] = None,
+                            out: Optional[DispatchLayout] = None) -> DispatchLayout:
+    """Counts, aligned expert offsets and stable expert-grouped rows for
+    ``topk_idx`` (int64 [T, K], -1 = no expert)."""
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [num_tokens, num_topk]")
+    T, K = topk_idx.shape
+    _check(topk_idx, "topk_idx", torch.int64)
+    if out is None:
+        out = allocate_layout(T, K, num_experts, num_ranks, expert_alignment, recv_capacity,
+                              topk_idx.device)
+    elif (out.num_tokens, out.num_topk, out.num_experts, out.num_ranks, out.expert_alignment) != (
+            T, K, num_experts, num_ranks, expert_alignment):
+        raise ValueError("preallocated layout was made for other sizes")
+    rc = lib().moe_get_dispatch_layout(
+        _ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, out.recv_capacity,
+        _ptr(out.num_tokens_per_rank), _ptr(out.num_tokens_per_expert), _ptr(out.is_token_in_rank),
+        _ptr(out.num_recv_tokens_per_expert), _ptr(out.expert_offsets), _ptr(out.token_row),
+        _ptr(out.recv_src), _ptr(out.error_flag), _ptr(out.workspace), out.workspace.numel(),
+        _stream(topk_idx.device))
+    if rc != MOE_OK:
+        raise MoeError("moe_get_dispatch_layout", rc)
+    return out
+
+
+def num_recv_tokens_per_expert_list(layout: DispatchLayout) -> list:
+    """Aligned rows per expert as a host list (waits for the GPU)."""
+    return layout.num_recv_tokens_per_expert.cpu().tolist()
+
+
+def allocate_recv(layout: DispatchLayout, hidden: int, quant_mode: int = QUANT_NONE,
+                  with_weights: bool = False):
+    dev = layout.token_row.device
+    cap = layout.recv_capacity
+    if quant_mode == QUANT_NONE:
+        rx, rs = torch.empty((cap, hidden), dtype=torch.bfloat16, device=dev), None
+    elif quant_mode == QUANT_INT8_PER_TOKEN:
+        rx = torch.empty((cap, hidden), dtype=torch.int8, device=dev)
+        rs = torch.empty(cap, dtype=torch.float32, device=dev)
+    elif quant_mode == QUANT_MXFP8_E4M3:
+        rx = torch.empty((cap, hidden), dtype=torch.float8_e4m3fn, device=dev)
+        rs = torch.empty((cap, hidden // 32), dtype=torch.uint8, device=dev)
+    else:
+        raise ValueError(f"unsupported quant_mode {quant_mode}")
+    rw = torch.empty(cap, dtype=torch.float32, device=dev) if with_weights else None
+    return rx, rs, rw
+
+
+_RECV_DTYPE = {QUANT_NONE: torch.bfloat16, QUANT_INT8_PER_TOKEN: torch.int8,
+               QUANT_MXFP8_E4M3: torch.float8_e4m3fn}
+
+
+def moe_dispatch(x: torch.Tensor, layout: DispatchLayout, topk_weights: Optional[torch.Tensor] = None,
+                 quant_mode: int = QUANT_NONE, recv_x: Optional[torch.Tensor] = None,
+                 recv_scales: Optional[torch.Tensor] = None,
+                 recv_weights: Optional[torch.Tensor] = None, with_weights: bool = False):
+    """Copy (and optionally quantise) every token of ``x`` (bf16 [T, H]) into
+    its experts' rows.  Returns (recv_x, recv_scales, recv_weights)."""
+    T, K, cap = layout.num_tokens, layout.num_topk, layout.recv_capacity
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError(f"x must be [{T}, hidden]")
+    H = x.shape[1]
+    dev = x.device
+    _check(x, "x", torch.bfloat16, device=dev)
+    if topk_weights is not None:
+        _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    if quant_mode not in _RECV_DTYPE:
+        raise ValueError(f"unsupported quant_mode {quant_mode}")
+    if recv_x is None:
+        recv_x, rs, rw = allocate_recv(layout, H, quant_mode, with_weights and recv_weights is None)
+        recv_scales = rs if recv_scales is None else recv_scales
+        recv_weights = rw if recv_weights is None else recv_weights
+    _check(recv_x, "recv_x", _RECV_DTYPE[quant_mode], (cap, H), dev)
+    if quant_mode == QUANT_INT8_PER_TOKEN:
+        _check(recv_scales, "recv_scales", torch.float32, (cap,), dev)
+    elif quant_mode == QUANT_MXFP8_E4M3:
+        _check(recv_scales, "recv_scales", torch.uint8, (cap, H // 32), dev)
+    if recv_weights is not None:
+        _check(recv_weights, "recv_weights", torch.float32, (cap,), dev)
+    rc = lib().moe_dispatch(_ptr(x), T, H, K, _ptr(layout.token_row), _ptr(topk_weights), cap,
+                            quant_mode, _ptr(recv_x), _ptr(recv_scales), _ptr(recv_weights),
+                            _stream(dev))
+    if rc != MOE_OK:
+        raise MoeError("moe_dispatch", rc)
+    return recv_x, recv_scales, recv_weights
+
+
+def moe_combine(expert_out: torch.Tensor, layout: DispatchLayout,
+                topk_weights: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = bf16(sum_k w[t,k] * expert_out[row(t,k)]), fp32 accumulation."""
+    T, K, cap = layout.num_tokens, layout.num_topk, layout.recv_capacity
+    if expert_out.dim() != 2 or expert_out.shape[0] != cap:
+        raise ValueError(f"expert_out must be [{cap}, hidden]")
+    H = expert_out.shape[1]
+    dev = expert_out.device
+    _check(expert_out, "expert_out", torch.bfloat16, device=dev)
+    if topk_weights is not None:
+        _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, H), dev)
+    rc = lib().moe_combine(_ptr(expert_out), cap, T, H, K, _ptr(layout.token_row),
+                           _ptr(topk_weights), _ptr(out), _stream(dev))
+    if rc != MOE_OK:
+        raise MoeError("moe_combine", rc)
+    return out

@@ -1,0 +1,126 @@
+// combine.hip -- top-k weighted sum of every token's expert-output rows.
+//
+// What is computed (Normal Mode API page, combine: "multiply by weights and
+// sum"; EPBatchManager page, ep_combine(): output (num_local_tokens, hidden)):
+//   out[t] = bf16( sum_k  w[t,k] * y[row(t,k)] )
+// as an fp32 fused multiply-add chain in ascending k, rounded once to bf16
+// (half to even).  Entries whose row is -1 (dropped) are skipped; no weights
+// means weight 1.
+//
+// Design (gfx950): one workgroup of 256 threads per token.  A lane owns 8
+// hidden elements (one 16-byte vector) per step; it issues the loads of all K
+// rows for that vector before the first FMA, so K independent 16-byte reads
+// per lane are in flight (K <= 16 gives at most 64 VGPRs of staging).  The
+// expanded rows are read exactly once; the rows of one token are scattered
+// over the receive buffer, but each load instruction of a wave reads 1 KiB
+// contiguous bytes of one row.  Row indices and weights are uniform per
+// workgroup and live in scalar registers.
+#include "device_common.h"
+#include "launch.h"
+
+#include "../../include/moe_dispatch_combine.h"
+
+namespace moe {
+
+constexpr int kCombineThreads = 256;
+
+template <int VPT, int KMAX>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const u32x4 *__restrict__ y, int nvec, int K, const int32_t *__restrict__ token_row,
+    const float *__restrict__ topk_weights, int64_t cap, u32x4 *__restrict__ out)
+{
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    int rows[KMAX];
+    float wts[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        rows[k] = -1;
+        wts[k] = 0.0f;
+        if (k < K) {
+            const int r = token_row[(int64_t)t * K + k];
+            rows[k] = (r >= 0 && r < cap) ? r : -1;
+            wts[k] = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int i = tid + j * kCombineThreads;
+        if (i >= nvec)
+            break;
+        u32x4 yv[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (rows[k] >= 0)
+                yv[k] = __builtin_nontemporal_load(y + (int64_t)rows[k] * nvec + i);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (rows[k] < 0)
+                continue;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc[2 * c] = __builtin_fmaf(wts[k], bf16_lo(yv[k][c]), acc[2 * c]);
+                acc[2 * c + 1] = __builtin_fmaf(wts[k], bf16_hi(yv[k][c]), acc[2 * c + 1]);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            o[c] = pack_bf16x2(acc[2 * c], acc[2 * c + 1]);
+        out[(int64_t)t * nvec + i] = o;
+    }
+}
+
+template <int VPT>
+static void launch_combine_k(int kmax, dim3 grid, hipStream_t stream, const u32x4 *y, int nvec,
+                             int K, const int32_t *token_row, const float *w, int64_t cap,
+                             u32x4 *out)
+{
+    const dim3 block(kCombineThreads);
+    switch (kmax) {
+    case 1:
+        hipLaunchKernelGGL((combine_kernel<VPT, 1>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
+        break;
+    case 2:
+        hipLaunchKernelGGL((combine_kernel<VPT, 2>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
+        break;
+    case 4:
+        hipLaunchKernelGGL((combine_kernel<VPT, 4>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
+        break;
+    case 8:
+        hipLaunchKernelGGL((combine_kernel<VPT, 8>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
+        break;
+    default:
+        hipLaunchKernelGGL((combine_kernel<VPT, 16>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
+        break;
+    }
+}
+
+hipError_t launch_combine(const void *y, int64_t cap, int T, int H, int K,
+                          const int32_t *token_row, const float *topk_weights, void *out,
+                          hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    const int nvec = H / 8;
+    const int vpt = (nvec + kCombineThreads - 1) / kCombineThreads;
+    const int kmax = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : 16;
+    const dim3 grid(T);
+    const u32x4 *yv = (const u32x4 *)y;
+    u32x4 *ov = (u32x4 *)out;
+    if (vpt <= 1)
+        launch_combine_k<1>(kmax, grid, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
+    else if (vpt <= 2)
+        launch_combine_k<2>(kmax, grid, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
+    else if (vpt <= 4)
+        launch_combine_k<4>(kmax, grid, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
+    else
+        launch_combine_k<8>(kmax, grid, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
+    return hipGetLastError();
+}
+
+} // namespace moe

@@ -1,0 +1,61 @@
+// launch.h -- internal interface between the C ABI (moe_api.hip) and the
+// kernel launchers.  Arguments reaching these functions are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// How the layout splits the T*K routing entries into chunks of whole tokens.
+// Every chunk is handled by one workgroup in both layout kernels.  The
+// limits keep one chunk's working set in LDS: its expert ids as int16
+// (kMaxChunkEntries) and its token x rank membership bytes (kMaxChunkFlags).
+constexpr int kLayoutTargetChunks = 64;
+constexpr int kMaxChunkEntries = 8192;
+constexpr int kMaxChunkFlags = 16384;
+
+struct LayoutPlan {
+    int tokens_per_chunk;
+    int num_chunks;
+    size_t workspace_bytes; // count table [chunks][E] + rank table [chunks][R] + flags [chunks]
+};
+
+inline LayoutPlan plan_layout(int T, int K, int E, int R)
+{
+    LayoutPlan p{0, 0, 0};
+    if (T <= 0)
+        return p;
+    int tpc = (T + kLayoutTargetChunks - 1) / kLayoutTargetChunks;
+    if (tpc > kMaxChunkEntries / K)
+        tpc = kMaxChunkEntries / K;
+    if (tpc > kMaxChunkFlags / R)
+        tpc = kMaxChunkFlags / R;
+    if (tpc < 1)
+        tpc = 1;
+    p.tokens_per_chunk = tpc;
+    p.num_chunks = (T + tpc - 1) / tpc;
+    p.workspace_bytes = (size_t)p.num_chunks * (size_t)(E + R + 1) * sizeof(int32_t);
+    return p;
+}
+
+struct LayoutArgs {
+    const int64_t *topk_idx;
+    int T, K, E, R, a;
+    int64_t cap;
+    int32_t *ntpr, *ntpe, *itr, *nrtpe, *off, *token_row, *recv_src, *error_flag;
+    int32_t *workspace;
+};
+
+hipError_t launch_layout(const LayoutArgs &args, const LayoutPlan &plan, hipStream_t stream);
+
+hipError_t launch_dispatch(const void *x, int T, int H, int K, const int32_t *token_row,
+                           const float *topk_weights, int64_t cap, int quant_mode, void *recv_x,
+                           void *recv_scales, float *recv_weights, hipStream_t stream);
+
+hipError_t launch_combine(const void *y, int64_t cap, int T, int H, int K,
+                          const int32_t *token_row, const float *topk_weights, void *out,
+                          hipStream_t stream);
+
+} // namespace moe

@@ -1,0 +1,171 @@
+// moe_api.hip -- the C ABI declared in include/moe_dispatch_combine.h.
+//
+// Each entry point validates its arguments on the host first and returns a
+// negative status without touching HIP when they are wrong; only then does it
+// queue kernels on the caller's stream.  Nothing is allocated and nothing
+// waits for the GPU.
+#include "launch.h"
+
+#include "../../include/moe_dispatch_combine.h"
+
+#include <climits>
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_layout_sizes(int T, int K, int E, int R, int a, int64_t cap)
+{
+    if (T < 0 || K < 1 || K > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS || R < 1 || R > E ||
+        E % R != 0 || a < 1)
+        return MOE_ERR_INVALID_ARG;
+    const int64_t bound = (int64_t)T * K + (int64_t)E * (a - 1);
+    if (bound > INT32_MAX)
+        return MOE_ERR_INVALID_ARG;
+    if (cap < bound || cap > INT32_MAX)
+        return MOE_ERR_CAPACITY;
+    return MOE_OK;
+}
+
+int check_rows_sizes(int T, int H, int K, int64_t cap, int quant_mode)
+{
+    if (T < 0 || K < 1 || K > MOE_MAX_TOPK || H < MOE_HIDDEN_MULTIPLE || H > MOE_MAX_HIDDEN ||
+        H % MOE_HIDDEN_MULTIPLE != 0 || cap < 0 || cap > INT32_MAX)
+        return MOE_ERR_INVALID_ARG;
+    if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_INT8_PER_TOKEN &&
+        quant_mode != MOE_QUANT_MXFP8_E4M3)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int64_t moe_recv_capacity_bound(int num_tokens, int num_topk, int num_experts, int expert_alignment)
+{
+    if (num_tokens < 0 || num_topk < 1 || num_experts < 1 || expert_alignment < 1)
+        return -1;
+    return (int64_t)num_tokens * num_topk + (int64_t)num_experts * (expert_alignment - 1);
+}
+
+size_t moe_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_ranks)
+{
+    if (num_tokens < 0 || num_topk < 1 || num_topk > MOE_MAX_TOPK || num_experts < 1 ||
+        num_experts > MOE_MAX_EXPERTS || num_ranks < 1 || num_ranks > num_experts ||
+        num_experts % num_ranks != 0)
+        return 0;
+    return plan_layout(num_tokens, num_topk, num_experts, num_ranks).workspace_bytes;
+}
+
+int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_topk,
+                            int num_experts, int num_ranks, int expert_alignment,
+                            int64_t recv_capacity, int32_t *num_tokens_per_rank,
+                            int32_t *num_tokens_per_expert, int32_t *is_token_in_rank,
+                            int32_t *num_recv_tokens_per_expert, int32_t *expert_offsets,
+                            int32_t *token_row, int32_t *recv_src, int32_t *error_flag,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const int T = num_tokens, K = num_topk, E = num_experts, R = num_ranks, a = expert_alignment;
+    int rc = check_layout_sizes(T, K, E, R, a, recv_capacity);
+    if (rc != MOE_OK)
+        return rc;
+    if (!num_tokens_per_rank || !num_tokens_per_expert || !num_recv_tokens_per_expert ||
+        !expert_offsets || !error_flag)
+        return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!topk_idx || !is_token_in_rank || !token_row))
+        return MOE_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && !recv_src)
+        return MOE_ERR_INVALID_ARG;
+    const LayoutPlan plan = plan_layout(T, K, E, R);
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+        return MOE_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 3u) != 0)
+        return MOE_ERR_WORKSPACE;
+
+    LayoutArgs args;
+    args.topk_idx = topk_idx;
+    args.T = T;
+    args.K = K;
+    args.E = E;
+    args.R = R;
+    args.a = a;
+    args.cap = recv_capacity;
+    args.ntpr = num_tokens_per_rank;
+    args.ntpe = num_tokens_per_expert;
+    args.itr = is_token_in_rank;
+    args.nrtpe = num_recv_tokens_per_expert;
+    args.off = expert_offsets;
+    args.token_row = token_row;
+    args.recv_src = recv_src;
+    args.error_flag = error_flag;
+    args.workspace = (int32_t *)workspace;
+    return launch_layout(args, plan, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_dispatch(const void *x, int num_tokens, int hidden, int num_topk,
+                 const int32_t *token_row, const float *topk_weights, int64_t recv_capacity,
+                 int quant_mode, void *recv_x, void *recv_scales, float *recv_weights,
+                 hipStream_t stream)
+{
+    const int T = num_tokens, H = hidden, K = num_topk;
+    int rc = check_rows_sizes(T, H, K, recv_capacity, quant_mode);
+    if (rc != MOE_OK)
+        return rc;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !token_row || !recv_x || !aligned16(x) || !aligned16(recv_x))
+        return MOE_ERR_INVALID_ARG;
+    if (quant_mode != MOE_QUANT_NONE && !recv_scales)
+        return MOE_ERR_INVALID_ARG;
+    if (quant_mode == MOE_QUANT_INT8_PER_TOKEN && ((uintptr_t)recv_scales & 3u) != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (recv_weights && ((uintptr_t)recv_weights & 3u) != 0)
+        return MOE_ERR_INVALID_ARG;
+    return launch_dispatch(x, T, H, K, token_row, topk_weights, recv_capacity, quant_mode, recv_x,
+                           recv_scales, recv_weights, stream) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
+int moe_combine(const void *expert_out, int64_t recv_capacity, int num_tokens, int hidden,
+                int num_topk, const int32_t *token_row, const float *topk_weights, void *out,
+                hipStream_t stream)
+{
+    const int T = num_tokens, H = hidden, K = num_topk;
+    int rc = check_rows_sizes(T, H, K, recv_capacity, MOE_QUANT_NONE);
+    if (rc != MOE_OK)
+        return rc;
+    if (T == 0)
+        return MOE_OK;
+    if (!token_row || !out || !aligned16(out) || !aligned16(expert_out))
+        return MOE_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && !expert_out)
+        return MOE_ERR_INVALID_ARG;
+    return launch_combine(expert_out, recv_capacity, T, H, K, token_row, topk_weights, out,
+                          stream) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
+const char *moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK:
+        return "ok";
+    case MOE_ERR_INVALID_ARG:
+        return "invalid argument";
+    case MOE_ERR_CAPACITY:
+        return "receive capacity below the worst-case row count (or not below 2^31)";
+    case MOE_ERR_WORKSPACE:
+        return "layout workspace missing, misaligned or too small";
+    case MOE_ERR_HIP:
+        return "HIP kernel launch failed";
+    default:
+        return "unknown status";
+    }
+}
+
+} // extern "C"

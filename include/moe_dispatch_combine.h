@@ -1,0 +1,185 @@
+/*
+ * moe_dispatch_combine.h -- C ABI of the MoE token dispatch / combine library
+ * for AMD Instinct MI355X (gfx950).  Library: libmoe_dispatch_combine.so.
+ *
+ * One step of a Mixture-of-Experts layer's token routing on one GPU:
+ *
+ *   moe_get_dispatch_layout   counts and a stable expert-grouped row for every
+ *                             (token, k) routing entry
+ *   moe_dispatch              copy (optionally quantise) every token into the
+ *                             rows of its selected experts
+ *   moe_combine               top-k weighted sum of every token's expert rows
+ *
+ * Sources, by page title and section:
+ *   sgl-kernel-npu deep_ep "Normal Mode API": dispatch Parameters, Return
+ *     Values and Constraints; combine Description / Parameters.
+ *   Huawei CANN "aclnnMoeDistributeDispatchV2": Formula Cases 1, 3 and 5;
+ *     Constraints 1 (deterministic), 7 (shapes), 11 (integer division); the
+ *     two-phase "workspace size, then run" calling pattern.
+ *   Modular MAX "EPBatchManager": ep_dispatch() and ep_combine() Returns.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must point to GPU memory that the
+ *     caller owns and keeps alive until the work queued on `stream` is done.
+ *     The library allocates no memory and keeps no state between calls.
+ *   - All work is queued on `stream` (NULL = the default stream); no call
+ *     waits for the GPU.
+ *   - Return value: MOE_OK, or a negative MOE_ERR_* code.  Argument errors are
+ *     detected on the host before any HIP call, so nothing is queued when an
+ *     error is returned.  MOE_ERR_HIP reports a failed kernel launch.
+ *   - Row indices are int32; byte offsets inside the library are 64-bit, so a
+ *     receive buffer may exceed 4 GiB.
+ *   - Everything is deterministic: the same inputs give bit-identical outputs
+ *     (CANN page, Constraint 1).
+ */
+#ifndef MOE_DISPATCH_COMBINE_H
+#define MOE_DISPATCH_COMBINE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* a size, range or pointer argument is invalid */
+#define MOE_ERR_CAPACITY (-2)    /* recv_capacity below moe_recv_capacity_bound()  */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required     */
+#define MOE_ERR_HIP (-4)         /* a HIP launch failed                            */
+
+/* Quantisation modes, numbered like quantMode in the CANN page's Formula. */
+#define MOE_QUANT_NONE 0           /* bf16 rows (Formula Case 1)                          */
+#define MOE_QUANT_INT8_PER_TOKEN 2 /* int8 rows + fp32 scale per row (Formula Case 3)      */
+#define MOE_QUANT_MXFP8_E4M3 4     /* e4m3fn rows + e8m0 byte per 32 elements (Case 5)     */
+
+/* Bits of the device error flag written by moe_get_dispatch_layout. */
+#define MOE_FLAG_BAD_EXPERT_ID 1 /* some topk_idx entry was outside [-1, num_experts) */
+
+/* Limits.  Top-k and expert counts are the ranges of the Normal Mode API page
+ * (Constraints: num_topk in (0, 16], num_experts in (0, 512]); hidden must be
+ * a multiple of 32 (CANN page, Constraint 7 "H"; also the MX block). */
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_HIDDEN 16384
+#define MOE_HIDDEN_MULTIPLE 32
+#define MOE_MX_BLOCK 32
+
+/*
+ * Worst-case number of receive rows: T*K entries plus at most
+ * expert_alignment-1 padding rows for each of the E experts.  It is the
+ * single-GPU form of the receive capacity "A" (CANN page, Constraint 7).
+ * Returns -1 if an argument is out of range (T < 0, K < 1, E < 1, a < 1).
+ */
+int64_t moe_recv_capacity_bound(int num_tokens, int num_topk, int num_experts,
+                                int expert_alignment);
+
+/*
+ * Bytes of device workspace moe_get_dispatch_layout needs for these sizes
+ * (first phase of the CANN page's two-phase pattern).  0 if the arguments are
+ * invalid or num_tokens is 0.  The workspace needs no initialisation; its
+ * contents after the call are unspecified.
+ */
+size_t moe_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts, int num_ranks);
+
+/*
+ * Dispatch layout (Normal Mode API page, dispatch Parameters and Return
+ * Values; EPBatchManager page, ep_dispatch() Returns).
+ *
+ * Input (device): topk_idx int64 [T, K], row-major; -1 = no expert.
+ * Sizes: T >= 0, 1 <= K <= 16, 1 <= E <= 512, 1 <= R <= E with E % R == 0
+ *   (experts are split into R virtual ranks of L = E / R consecutive experts;
+ *   expert e belongs to rank e / L), expert_alignment a >= 1,
+ *   recv_capacity >= moe_recv_capacity_bound(T, K, E, a) and < 2^31.
+ * Outputs (device, all overwritten):
+ *   num_tokens_per_rank        int32 [R]    distinct tokens with an entry in rank r
+ *   num_tokens_per_expert      int32 [E]    valid entries routed to expert e
+ *   is_token_in_rank           int32 [T, R] 1 if token t has an entry in rank r, else 0
+ *   num_recv_tokens_per_expert int32 [E]    num_tokens_per_expert rounded up to a
+ *                                           multiple of a (0 stays 0)
+ *   expert_offsets             int32 [E+1]  exclusive prefix sum of the aligned counts;
+ *                                           expert e owns rows [off[e], off[e+1])
+ *   token_row                  int32 [T, K] row of entry (t, k), or -1 if dropped
+ *   recv_src                   int32 [recv_capacity]  t*K + k of the entry a row holds,
+ *                                           -1 for padding rows and unused rows
+ *   error_flag                 int32 [1]    MOE_FLAG_* bits; 0 if all ids were valid
+ * Within an expert, rows follow ascending t*K + k.  An id outside [-1, E) sets
+ * MOE_FLAG_BAD_EXPERT_ID and the entry is treated as -1.
+ * Workspace: device, >= moe_layout_workspace_bytes(T, K, E, R) bytes (may be
+ * NULL when that is 0).
+ * Errors: MOE_ERR_INVALID_ARG (ranges, NULL outputs), MOE_ERR_CAPACITY,
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP.
+ */
+int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_topk,
+                            int num_experts, int num_ranks, int expert_alignment,
+                            int64_t recv_capacity, int32_t *num_tokens_per_rank,
+                            int32_t *num_tokens_per_expert, int32_t *is_token_in_rank,
+                            int32_t *num_recv_tokens_per_expert, int32_t *expert_offsets,
+                            int32_t *token_row, int32_t *recv_src, int32_t *error_flag,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Dispatch (Normal Mode API page, dispatch; CANN page, Formula Cases 1, 3, 5;
+ * EPBatchManager page, ep_dispatch()).
+ *
+ * For every entry (t, k) with row = token_row[t, k] in [0, recv_capacity):
+ *   MOE_QUANT_NONE:           recv_x[row, :] = x[t, :]                 (bf16 bits)
+ *   MOE_QUANT_INT8_PER_TOKEN: dynamicScales = 127 / max|x[t, :]| in fp32,
+ *                             recv_x[row, h] = round_half_even(x[t, h] * dynamicScales)
+ *                             recv_scales[row] = 1.0f / dynamicScales  (fp32)
+ *                             (a row whose dynamicScales is not finite gets codes 0
+ *                             and scale 0)
+ *   MOE_QUANT_MXFP8_E4M3:     per 32-element block j: sharedExp =
+ *                             max(floor(log2 max|x|) - 8, -127) (-127 for a zero block),
+ *                             recv_x[row, h] = e4m3fn(x[t, h] / 2^sharedExp), rounded
+ *                             half to even and saturated to +-448,
+ *                             recv_scales[row * H/32 + j] = sharedExp + 127 (e8m0)
+ *   recv_weights[row] = topk_weights[t, k] (1.0f if topk_weights is NULL), when
+ *   recv_weights is not NULL.
+ * Quantisation is done once per token; all copies share codes and scales.
+ * Rows no entry names (padding, unused) are not written.
+ * Inputs (device): x bf16 [T, H]; token_row int32 [T, K] from
+ *   moe_get_dispatch_layout; topk_weights fp32 [T, K] or NULL.
+ * Outputs (device): recv_x [recv_capacity, H] of bf16 / int8 / e4m3fn;
+ *   recv_scales NULL (bf16) / fp32 [recv_capacity] / uint8 [recv_capacity, H/32];
+ *   recv_weights fp32 [recv_capacity] or NULL.
+ * Sizes: T >= 0, 32 <= H <= 16384 with H % 32 == 0, 1 <= K <= 16,
+ *   0 <= recv_capacity < 2^31.
+ * x, recv_x and recv_scales must be 16-byte aligned.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP.
+ */
+int moe_dispatch(const void *x, int num_tokens, int hidden, int num_topk,
+                 const int32_t *token_row, const float *topk_weights, int64_t recv_capacity,
+                 int quant_mode, void *recv_x, void *recv_scales, float *recv_weights,
+                 hipStream_t stream);
+
+/*
+ * Combine (Normal Mode API page, combine: "multiply by weights and sum";
+ * EPBatchManager page, ep_combine(): output (num_local_tokens, hidden)).
+ *
+ *   out[t, :] = bf16( sum over k with 0 <= token_row[t, k] < recv_capacity of
+ *                     topk_weights[t, k] * expert_out[token_row[t, k], :] )
+ * The sum is an fp32 fused multiply-add chain in ascending k, rounded once to
+ * bf16 (half to even); weights are 1 when topk_weights is NULL; a token with
+ * no valid entry gets +0.
+ * Inputs (device): expert_out bf16 [recv_capacity, H]; token_row int32 [T, K];
+ *   topk_weights fp32 [T, K] or NULL.
+ * Output (device): out bf16 [T, H].
+ * Sizes and alignment as for moe_dispatch (expert_out and out 16-byte aligned).
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP.
+ */
+int moe_combine(const void *expert_out, int64_t recv_capacity, int num_tokens, int hidden,
+                int num_topk, const int32_t *token_row, const float *topk_weights, void *out,
+                hipStream_t stream);
+
+/* Static text for a status code. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DISPATCH_COMBINE_H */

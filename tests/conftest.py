@@ -18,3 +18,13 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name every GPU case on the real stderr before it runs, so that a run
+    that dies on the GPU still says which case it was in."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,125 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and its host-side argument checks agree with the oracle's rules.
+No kernel is launched here: every call below fails validation (or is a pure
+host query) before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_dispatch_combine.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from combine_moe_get_dispatch_amd import build_lib
+    if build_lib.is_stale():
+        build_lib.build(verbose=False)
+    import combine_moe_get_dispatch_amd as m
+    return m.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("moe_get_dispatch_layout", "moe_dispatch", "moe_combine",
+              "moe_layout_workspace_bytes", "moe_recv_capacity_bound", "moe_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from combine_moe_get_dispatch_amd import LIB_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c11", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        "-I/opt/rocm/include", "-x", "c", HEADER], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_capacity_and_workspace_queries(L, orc):
+    for args in [(4096, 8, 256, 1), (8192, 8, 256, 128), (32768, 16, 512, 128), (0, 4, 8, 4),
+                 (-1, 4, 8, 4), (8, 0, 8, 1), (8, 2, 8, 0)]:
+        assert L.moe_recv_capacity_bound(*args) == orc.recv_capacity_bound(*args)
+    assert L.moe_layout_workspace_bytes(0, 8, 256, 8) == 0
+    assert L.moe_layout_workspace_bytes(4096, 8, 256, 7) == 0
+    ws = L.moe_layout_workspace_bytes(4096, 8, 256, 8)
+    assert 0 < ws < 1 << 20 and ws % 4 == 0
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(L.moe_status_string(code), bytes)
+
+
+BAD = ctypes.c_void_p(0x1000)   # never dereferenced: every call below is rejected on the host
+
+
+def _layout_call(L, T, K, E, R, a, cap, ptrs=True, ws=BAD, ws_bytes=1 << 30):
+    p = BAD if ptrs else None
+    return L.moe_get_dispatch_layout(p, T, K, E, R, a, cap, p, p, p, p, p, p, p, p, ws, ws_bytes, None)
+
+
+LAYOUT_CASES = [
+    (8, 0, 4, 2, 1), (8, 17, 4, 2, 1), (8, 2, 513, 1, 1), (8, 2, 0, 1, 1), (8, 2, 6, 4, 1),
+    (8, 2, 6, 7, 1), (8, 2, 6, 0, 1), (8, 2, 6, 3, 0), (-1, 2, 6, 3, 1),
+]
+
+
+@pytest.mark.parametrize("T,K,E,R,a", LAYOUT_CASES)
+def test_layout_rejects_like_the_oracle(L, orc, T, K, E, R, a):
+    cap = max(orc.recv_capacity_bound(T, K, max(E, 1), max(a, 1)), 0)
+    expect = orc.check_layout_args(T, K, E, R, a, cap)
+    assert expect != 0
+    assert _layout_call(L, T, K, E, R, a, cap) == expect
+
+
+def test_layout_capacity_errors(L, orc):
+    bound = orc.recv_capacity_bound(100, 4, 16, 8)
+    assert _layout_call(L, 100, 4, 16, 4, 8, bound - 1) == -2 == orc.check_layout_args(100, 4, 16, 4, 8, bound - 1)
+    assert _layout_call(L, 100, 4, 16, 4, 8, 1 << 31) == orc.check_layout_args(100, 4, 16, 4, 8, 1 << 31)
+    assert _layout_call(L, 1 << 28, 16, 16, 4, 8, 1 << 31) == -1
+
+
+def test_layout_rejects_null_outputs_and_small_workspace(L):
+    cap = 100 * 4 + 16 * 7
+    assert _layout_call(L, 100, 4, 16, 4, 8, cap, ptrs=False) == -1
+    need = L.moe_layout_workspace_bytes(100, 4, 16, 4)
+    assert _layout_call(L, 100, 4, 16, 4, 8, cap, ws=None) == -3
+    assert _layout_call(L, 100, 4, 16, 4, 8, cap, ws_bytes=need - 1) == -3
+
+
+ROWS_CASES = [(16, 48, 4, 0), (16, 16, 4, 0), (16, 16416, 4, 0), (16, 1024, 4, 1), (16, 1024, 4, 3),
+              (16, 1024, 0, 0), (16, 1024, 17, 0), (-1, 1024, 4, 0), (16, 1024, 4, 5)]
+
+
+@pytest.mark.parametrize("T,H,K,q", ROWS_CASES)
+def test_dispatch_and_combine_reject_like_the_oracle(L, orc, T, H, K, q):
+    expect = orc.check_rows_args(T, H, K, 1000, q)
+    assert expect != 0
+    assert L.moe_dispatch(BAD, T, H, K, BAD, BAD, 1000, q, BAD, BAD, BAD, None) == expect
+    if q == 0:
+        assert L.moe_combine(BAD, 1000, T, H, K, BAD, BAD, BAD, None) == expect
+
+
+def test_dispatch_pointer_rules(L):
+    assert L.moe_dispatch(None, 4, 64, 2, BAD, None, 100, 0, BAD, None, None, None) == -1
+    assert L.moe_dispatch(ctypes.c_void_p(0x1008), 4, 64, 2, BAD, None, 100, 0, BAD, None, None, None) == -1
+    assert L.moe_dispatch(BAD, 4, 64, 2, BAD, None, 100, 2, BAD, None, None, None) == -1
+    assert L.moe_dispatch(None, 0, 64, 2, None, None, 100, 0, None, None, None, None) == 0
+    assert L.moe_combine(BAD, 100, 4, 64, 2, BAD, None, ctypes.c_void_p(0x1004), None) == -1
+    assert L.moe_combine(None, 100, 0, 64, 2, None, None, None, None) == 0

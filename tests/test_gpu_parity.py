@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: layout, indices, rows, codes and scales bit-exact (whole buffers,
+including the sentinel left in rows nobody writes); combine within
+|g - r| <= 2^-8 |r| + (K+1) 2^-24 sum|w y| of the fp64 oracle, and, with
+identity experts, max relative error <= 1e-2.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_get_dispatch_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import combine_moe_get_dispatch_amd as moe
+    from gpu_util import (DEV, assert_layout_equal, bf16_dev, bf16_host_bits, check_combine,
+                          combine_bound, dequant_identity_expert, gpu_layout, layout_to_host,
+                          oracle_poisoned, poisoned_recv, recv_to_host)
+
+
+def run_full_case(x_bits, idx, wts, E, R, a, quant, north_star=True):
+    T, H = x_bits.shape
+    K = idx.shape[1]
+    ol = oracle.layout(idx, E, R, a)
+    lay = gpu_layout(idx, E, R, a)
+    gl = layout_to_host(lay)
+    assert_layout_equal(gl, ol)
+
+    cap = ol.recv_capacity
+    orx, ors = oracle_poisoned(cap, H, quant)
+    orx, ors, orw = oracle.dispatch(x_bits, ol.token_row, cap, wts, quant, recv_x=orx,
+                                    recv_scales=ors, with_weights=True)
+    rx, rs, rw = poisoned_recv(lay, H, quant)
+    x_dev = bf16_dev(x_bits)
+    w_dev = torch.from_numpy(wts).to(DEV)
+    moe.moe_dispatch(x_dev, lay, w_dev, quant, recv_x=rx, recv_scales=rs, recv_weights=rw)
+    grx = recv_to_host(rx, quant)
+    np.testing.assert_array_equal(grx, orx)
+    if quant == 2:
+        np.testing.assert_array_equal(rs.cpu().numpy().view(np.uint32), ors.view(np.uint32))
+    elif quant == 4:
+        np.testing.assert_array_equal(rs.cpu().numpy(), ors)
+    used = ol.recv_src >= 0
+    np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
+    assert (rw.cpu().numpy()[~used] == -3.0).all()
+
+    # combine with identity experts
+    y_bits = dequant_identity_expert(orx, ors, quant)
+    y_dev = bf16_dev(y_bits) if quant != 0 else rx
+    out = moe.moe_combine(y_dev, lay, w_dev)
+    exact = oracle.combine(y_bits, ol.token_row, wts)
+    S = combine_bound(y_bits, ol.token_row, wts, K)
+    return check_combine(bf16_host_bits(out), exact, S, K, north_star=north_star)
+
+
+@pytest.mark.parametrize("w", W.WORKLOADS[:4], ids=[w.name for w in W.WORKLOADS[:4]])
+def test_workload_full_parity(w):
+    inp = W.generate(w)
+    rel = run_full_case(inp.x_bits, inp.topk_idx, inp.topk_weights, w.num_experts, w.num_ranks,
+                        w.expert_alignment, w.quant_mode)
+    print(f"{w.name}: combine max relative error {rel:.3e}")
+
+
+def test_large_workload_layout_full_rows_sampled():
+    """32768 x 7168, 512 experts, top-16: layout compared in full; every
+    dispatched row checked on the GPU against its source token; a sample of
+    tokens compared with the oracle's rows and combine."""
+    w = W.WORKLOADS[4]
+    inp = W.generate(w)
+    T, H, K = w.num_tokens, w.hidden, w.num_topk
+    ol = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    lay = gpu_layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    assert_layout_equal(layout_to_host(lay), ol)
+    rx, _, rw = poisoned_recv(lay, H, 0)
+    x_dev = bf16_dev(inp.x_bits)
+    w_dev = torch.from_numpy(inp.topk_weights).to(DEV)
+    moe.moe_dispatch(x_dev, lay, w_dev, 0, recv_x=rx, recv_weights=rw)
+    # every valid row equals its token; every other row still holds the sentinel
+    src = lay.recv_src.long()
+    used = src >= 0
+    rows_i16 = rx.view(torch.int16)
+    x_i16 = x_dev.view(torch.int16)
+    step = 65536
+    for lo in range(0, lay.recv_capacity, step):
+        s = src[lo:lo + step]
+        u = used[lo:lo + step]
+        blk = rows_i16[lo:lo + step]
+        assert torch.equal(blk[u], x_i16[s[u] // K])
+        assert (blk[~u] == -1).all()
+    # oracle on a token sample
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(T, 512, replace=False))
+    rows = ol.token_row[sample]
+    sub_rows = np.arange(rows.size, dtype=np.int32).reshape(rows.shape)
+    orx, _, _ = oracle.dispatch(inp.x_bits[sample], sub_rows, rows.size)
+    grx = bf16_host_bits(rx[torch.from_numpy(rows.reshape(-1).astype(np.int64)).to(DEV)])
+    np.testing.assert_array_equal(grx, orx)
+    out = moe.moe_combine(rx, lay, w_dev)
+    exact = oracle.combine(orx, sub_rows, inp.topk_weights[sample])
+    S = combine_bound(orx, sub_rows, inp.topk_weights[sample], K)
+    check_combine(bf16_host_bits(out[torch.from_numpy(sample).to(DEV)]), exact, S, K)
+
+
+def _routing(rng, T, K, E, dup=False, drop=0.0):
+    if dup:
+        idx = rng.integers(0, E, size=(T, K))
+    else:
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :K]
+    idx = idx.astype(np.int64)
+    if drop:
+        idx[rng.random((T, K)) < drop] = -1
+    w = rng.random((T, K)).astype(np.float32)
+    return np.ascontiguousarray(idx), w
+
+
+EDGE = [
+    # name, T, H, E, R, K, a, quant, dup, drop
+    ("ragged_tail", 4161, 96, 64, 8, 6, 5, 0, False, 0.0),
+    ("h32", 257, 32, 8, 2, 3, 1, 4, False, 0.1),
+    ("h1056_int8", 300, 1056, 32, 4, 4, 16, 2, True, 0.2),
+    ("k1_e_eq_r", 513, 256, 16, 16, 1, 1, 0, False, 0.0),
+    ("k16_e512", 700, 128, 512, 512, 16, 1, 0, False, 0.0),
+    ("max_hidden_mx", 40, 16384, 128, 8, 8, 32, 4, False, 0.0),
+    ("max_hidden_int8", 40, 16384, 128, 8, 8, 32, 2, False, 0.0),
+    ("align_gt_counts", 50, 64, 16, 4, 2, 256, 0, False, 0.0),
+    ("duplicates", 333, 64, 4, 2, 8, 3, 0, True, 0.0),
+    ("all_dropped", 64, 64, 8, 2, 4, 4, 0, False, 1.0),
+    ("one_token", 1, 7168, 256, 8, 8, 128, 2, False, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_cases(case):
+    name, T, H, E, R, K, a, quant, dup, drop = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    idx, wts = _routing(rng, T, K, E, dup, drop)
+    wts[idx < 0] = 0.0
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    run_full_case(x, idx, wts, E, R, a, quant)
+
+
+def test_skewed_routing_all_to_one_expert():
+    rng = np.random.default_rng(4)
+    T, K, E = 6000, 4, 64
+    idx = np.zeros((T, K), np.int64)
+    idx[:, 1:] = rng.integers(0, E, size=(T, K - 1))
+    wts = rng.random((T, K)).astype(np.float32)
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, 64)).astype(np.float32))
+    run_full_case(x, idx, wts, E, 4, 7, 0, north_star=False)
+
+
+def test_out_of_range_ids_flagged():
+    rng = np.random.default_rng(6)
+    T, K, E = 900, 4, 32
+    idx, wts = _routing(rng, T, K, E)
+    idx[5, 1] = E
+    idx[700, 3] = -9
+    ol = oracle.layout(idx, E, 4, 8)
+    gl = layout_to_host(gpu_layout(idx, E, 4, 8))
+    assert ol.error_flag == 1
+    assert_layout_equal(gl, ol)
+
+
+def test_zero_tokens():
+    idx = np.zeros((0, 4), np.int64)
+    ol = oracle.layout(idx, 16, 4, 8)
+    lay = gpu_layout(idx, 16, 4, 8)
+    assert_layout_equal(layout_to_host(lay), ol)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    rx, rs, rw = moe.moe_dispatch(x, lay, None, 0)
+    out = moe.moe_combine(rx, lay, None)
+    assert out.shape == (0, 64)
+
+
+def test_quant_special_rows():
+    """Zero rows, subnormal rows, rows whose int8 scale overflows, -0, and
+    single outliers, through both quantisers."""
+    H, K, E = 256, 2, 4
+    rows = []
+    rows.append(np.zeros(H, np.float32))
+    r = np.zeros(H, np.float32); r[3] = -0.0; r[100] = 2.0 ** -130; rows.append(r)
+    rows.append(np.full(H, 2.0 ** -127, np.float32))
+    r = np.zeros(H, np.float32); r[7] = 3.0e38; r[8] = -1.0; rows.append(r)
+    rng = np.random.default_rng(8)
+    r = rng.standard_normal(H).astype(np.float32) * 1e-3; r[200] = 5e4; rows.append(r)
+    r = (rng.integers(-127, 128, H)).astype(np.float32); r[0] = 127; rows.append(r)
+    x = W.f32_to_bf16_bits(np.stack(rows))
+    x[1, 3] = 0x8000
+    T = x.shape[0]
+    idx = np.stack([np.arange(T) % E, (np.arange(T) + 1) % E], axis=1).astype(np.int64)
+    wts = np.full((T, K), 0.5, np.float32)
+    for quant in (2, 4):
+        run_full_case(x, idx, wts, E, 2, 1, quant, north_star=False)
+
+
+def test_combine_random_expert_outputs():
+    """Combine alone on arbitrary expert rows (cancellation allowed), with and
+    without weights."""
+    rng = np.random.default_rng(12)
+    T, K, E, H = 2000, 8, 64, 512
+    idx, wts = _routing(rng, T, K, E, drop=0.1)
+    wts = rng.standard_normal((T, K)).astype(np.float32)
+    ol = oracle.layout(idx, E, 8, 4)
+    lay = gpu_layout(idx, E, 8, 4)
+    y = W.random_bf16_rows(ol.recv_capacity, H, 3)
+    y_dev = bf16_dev(y)
+    for w in (wts, None):
+        out = moe.moe_combine(y_dev, lay, None if w is None else torch.from_numpy(w).to(DEV))
+        exact = oracle.combine(y, ol.token_row, w)
+        S = combine_bound(y, ol.token_row, w, K)
+        check_combine(bf16_host_bits(out), exact, S, K, north_star=False)
+
+
+def test_deterministic_repeat():
+    w = W.WORKLOADS[2]
+    inp = W.generate(w, num_tokens=2048)
+    outs = []
+    for _ in range(2):
+        lay = gpu_layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment)
+        rx, rs, _ = moe.moe_dispatch(bf16_dev(inp.x_bits), lay, None, 2)
+        y = (rx.float() * rs[:, None]).to(torch.bfloat16)
+        out = moe.moe_combine(y, lay, torch.from_numpy(inp.topk_weights).to(DEV))
+        outs.append((layout_to_host(lay), rx.cpu(), rs.cpu(), out.cpu()))
+    a, b = outs
+    for k in a[0]:
+        np.testing.assert_array_equal(a[0][k], b[0][k])
+    used = a[0]["recv_src"] >= 0
+    assert torch.equal(a[1][used], b[1][used]) and torch.equal(a[2][used], b[2][used])
+    assert torch.equal(a[3].view(torch.int16), b[3].view(torch.int16))
