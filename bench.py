@@ -5,8 +5,13 @@ stream, over the whole batch (identity experts: the combine input is the
 receive buffer itself for bf16, or its bf16 dequantisation -- made once,
 outside the timed region -- for int8 / MXFP8).  Inputs are resident in HBM
 before timing starts.  W untimed warm-up steps, then exactly K timed steps
-bracketed by torch.cuda.synchronize().  HIP events recorded on the stream the
-kernels run on give each stage's average duration.
+bracketed by torch.cuda.synchronize().
+
+Stage durations come from HIP events recorded, inside the timed region, on
+the stream the kernels run on, around each stage of every Nth step
+(--event-every).  The events are created with hipEventDisableSystemFence, so
+a record does not flush caches to system scope; recording them on a sample
+of steps keeps their cost out of the headline.
 
 Prints ONE JSON line.  `value` = effective HBM GB/s = algorithmic bytes per
 step * K / elapsed; algorithmic bytes count x read once, each valid expanded
@@ -16,6 +21,8 @@ traffic (padding rows are never touched and not counted).
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +33,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+KERNEL_SOURCES = {
+    "dispatch": ["dispatch.hip", "device_common.h", "launch.h"],
+    "combine": ["combine.hip", "device_common.h", "launch.h"],
+    "layout": ["layout.hip", "device_common.h", "launch.h"],
+}
 
 
 def parse():
@@ -36,7 +49,12 @@ def parse():
     p.add_argument("--workload", default="bf16_4096x7168_e256_top8")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU time budget for the oracle baseline (0 = skip)")
+    p.add_argument("--event-every", type=int, default=10,
+                   help="record stage events on every Nth timed step")
     p.add_argument("--no-check", action="store_true", help="skip the post-run sanity check")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after timing, run 3 torch copies of 256 MiB: a kernel of known traffic "
+                        "that hardware byte counters (FETCH_SIZE / WRITE_SIZE) are scaled against")
     return p.parse_args()
 
 
@@ -48,6 +66,87 @@ def stage_bytes(T, H, K, R, E, V, cap, quant):
     dispatch = 2 * T * H + 4 * T * K + V * (H * s_q + sigma)
     combine = 2 * V * H + 8 * T * K + 2 * T * H
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
+
+
+def kernel_source_sha(stage: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, "combine_moe_get_dispatch_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 counter
+    summary (profiles/<stage>_<workload>_counters.txt), or None when there is
+    none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_sha(stage):
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class StageEvents:
+    """Timing events on torch's current stream.  Uses HIP events created with
+    hipEventDisableSystemFence through the HIP runtime torch already loaded;
+    falls back to torch.cuda.Event if that is not possible."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.hip = None
+        try:
+            path = [l.split()[-1] for l in open("/proc/self/maps").read().split("\n")
+                    if "libamdhip64" in l][0]
+            hip = ctypes.CDLL(path)
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            e = ctypes.c_void_p()
+            if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0:
+                self.hip = hip
+                self.kind = "hipEventDisableSystemFence"
+        except (IndexError, OSError, AttributeError):
+            self.hip = None
+        if self.hip is None:
+            self.kind = "torch.cuda.Event"
+
+    def new(self):
+        if self.hip is None:
+            return self.torch.cuda.Event(enable_timing=True)
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        return e
+
+    def record(self, ev):
+        if self.hip is None:
+            ev.record()
+        else:
+            s = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+            rc = self.hip.hipEventRecord(ev, s)
+            if rc != 0:
+                raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_us(self, a, b):
+        if self.hip is None:
+            return a.elapsed_time(b) * 1e3
+        f = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return f.value * 1e3
 
 
 def cpu_baseline(inp, w, quant, budget_s, bytes_fn):
@@ -121,37 +220,41 @@ def main():
         y = torch.nan_to_num(y).to(torch.bfloat16)
     torch.cuda.synchronize()
 
+    timer = StageEvents(torch)
+
     def step(ev=None):
         if ev is not None:
-            ev[0].record()
+            timer.record(ev[0])
         moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)
         if ev is not None:
-            ev[1].record()
+            timer.record(ev[1])
         moe.moe_dispatch(x, lay, None, quant, recv_x=rx, recv_scales=rs)
         if ev is not None:
-            ev[2].record()
+            timer.record(ev[2])
         moe.moe_combine(y, lay, wt, out=out)
         if ev is not None:
-            ev[3].record()
+            timer.record(ev[3])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps; events on the stream the kernels use
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: exactly K steps; stage events on every Nth step, on the
+    # stream the kernels use
+    every = max(1, args.event_every)
+    events = {i: [timer.new() for _ in range(4)] for i in range(0, args.steps, every)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(events.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     st = {"layout": [], "dispatch": [], "combine": []}
-    for ev in events:
-        st["layout"].append(ev[0].elapsed_time(ev[1]) * 1e3)
-        st["dispatch"].append(ev[1].elapsed_time(ev[2]) * 1e3)
-        st["combine"].append(ev[2].elapsed_time(ev[3]) * 1e3)
+    for ev in events.values():
+        st["layout"].append(timer.elapsed_us(ev[0], ev[1]))
+        st["dispatch"].append(timer.elapsed_us(ev[1], ev[2]))
+        st["combine"].append(timer.elapsed_us(ev[2], ev[3]))
     avg_us = {k: float(np.mean(v)) for k, v in st.items()}
     med_us = {k: float(np.median(v)) for k, v in st.items()}
 
@@ -171,6 +274,14 @@ def main():
         if quant == 0:
             assert torch.equal(rx.view(torch.int16)[u], x.view(torch.int16)[src[u] // K])
         assert int(lay.error_flag.item()) == 0
+
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -201,9 +312,12 @@ def main():
         "stage_bytes": sb,
         "stage_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
         "stage_median_us": {k: round(v, 2) for k, v in med_us.items()},
+        "stage_events": {"kind": timer.kind, "every_nth_step": every, "samples": len(events)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": counter_traffic(w.name, dom),
+                     "algorithmic_bytes_per_launch": sb[dom],
+                     "avg_launch_us": round(avg_us[dom], 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -7,8 +7,9 @@
 // (half to even).  Entries whose row is -1 (dropped) are skipped; no weights
 // means weight 1.
 //
-// Design (gfx950): one workgroup of 256 threads per token.  A lane owns 8
-// hidden elements (one 16-byte vector) per step; it issues the loads of all K
+// Design (gfx950): one workgroup per token, one 16-byte vector (8 hidden
+// elements) per lane (896 lanes for H = 7168; two vectors per lane above
+// H = 8192).  A lane issues the loads of all K
 // rows for that vector before the first FMA, so K independent 16-byte reads
 // per lane are in flight (K <= 16 gives at most 64 VGPRs of staging).  The
 // expanded rows are read exactly once; the rows of one token are scattered
@@ -22,10 +23,8 @@
 
 namespace moe {
 
-constexpr int kCombineThreads = 256;
-
 template <int VPT, int KMAX>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+__global__ __launch_bounds__(kRowMaxThreads) void combine_kernel(
     const u32x4 *__restrict__ y, int nvec, int K, const int32_t *__restrict__ token_row,
     const float *__restrict__ topk_weights, int64_t cap, u32x4 *__restrict__ out)
 {
@@ -45,7 +44,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-        const int i = tid + j * kCombineThreads;
+        const int i = tid + j * (int)blockDim.x;
         if (i >= nvec)
             break;
         u32x4 yv[KMAX];
@@ -76,27 +75,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 }
 
 template <int VPT>
-static void launch_combine_k(int kmax, dim3 grid, hipStream_t stream, const u32x4 *y, int nvec,
-                             int K, const int32_t *token_row, const float *w, int64_t cap,
-                             u32x4 *out)
+static hipError_t launch_combine_k(int kmax, dim3 grid, dim3 block, hipStream_t stream,
+                                   const u32x4 *y, int nvec, int K, const int32_t *token_row,
+                                   const float *w, int64_t cap, u32x4 *out)
 {
-    const dim3 block(kCombineThreads);
     switch (kmax) {
     case 1:
-        hipLaunchKernelGGL((combine_kernel<VPT, 1>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-        break;
+        return launch_kernel(combine_kernel<VPT, 1>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
     case 2:
-        hipLaunchKernelGGL((combine_kernel<VPT, 2>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-        break;
+        return launch_kernel(combine_kernel<VPT, 2>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
     case 4:
-        hipLaunchKernelGGL((combine_kernel<VPT, 4>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-        break;
+        return launch_kernel(combine_kernel<VPT, 4>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
     case 8:
-        hipLaunchKernelGGL((combine_kernel<VPT, 8>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-        break;
+        return launch_kernel(combine_kernel<VPT, 8>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
     default:
-        hipLaunchKernelGGL((combine_kernel<VPT, 16>), grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-        break;
+        return launch_kernel(combine_kernel<VPT, 16>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
     }
 }
 
@@ -107,20 +100,15 @@ hipError_t launch_combine(const void *y, int64_t cap, int T, int H, int K,
     if (T == 0)
         return hipSuccess;
     const int nvec = H / 8;
-    const int vpt = (nvec + kCombineThreads - 1) / kCombineThreads;
+    const int threads = row_block_threads(nvec);
+    const int vpt = (nvec + threads - 1) / threads; // 1 or 2 (H <= 16384)
     const int kmax = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : 16;
-    const dim3 grid(T);
+    const dim3 grid(T), block(threads);
     const u32x4 *yv = (const u32x4 *)y;
     u32x4 *ov = (u32x4 *)out;
-    if (vpt <= 1)
-        launch_combine_k<1>(kmax, grid, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
-    else if (vpt <= 2)
-        launch_combine_k<2>(kmax, grid, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
-    else if (vpt <= 4)
-        launch_combine_k<4>(kmax, grid, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
-    else
-        launch_combine_k<8>(kmax, grid, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
-    return hipGetLastError();
+    if (vpt == 1)
+        return launch_combine_k<1>(kmax, grid, block, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
+    return launch_combine_k<2>(kmax, grid, block, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
 }
 
 } // namespace moe

@@ -11,9 +11,10 @@
 //          q = e4m3fn(x / 2^sharedExp) (ties to even, saturated to 448),
 //          e8m0 byte = sharedExp + 127
 //
-// Design (gfx950): one workgroup of 256 threads per token.  The token row is
-// read from HBM exactly once with 16-byte loads and held in VGPRs (up to 8
-// vectors per lane, H <= 16384); it is quantised there once; then each of the
+// Design (gfx950): one workgroup per token, one 16-byte vector per lane
+// (896 lanes for H = 7168; two vectors per lane above H = 8192).  The token
+// row is read from HBM exactly once and held in VGPRs; it is quantised there
+// once; then each of the
 // K copies is written with 16-byte (bf16) or 8-byte (int8 / e4m3) stores, one
 // contiguous row per wave instruction group.  The stores are nontemporal:
 // every expanded row is written once and only read again by the next stage,
@@ -26,24 +27,23 @@
 
 namespace moe {
 
-constexpr int kDispatchThreads = 256;
-
 // --------------------------------------------------------------------------- bf16
 
 template <int VPT>
-__global__ __launch_bounds__(kDispatchThreads) void dispatch_bf16_kernel(
+__global__ __launch_bounds__(kRowMaxThreads) void dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
     const float *__restrict__ topk_weights, int64_t cap, u32x4 *__restrict__ recv,
     float *__restrict__ recv_weights)
 {
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
     const u32x4 *xt = x + (int64_t)t * nvec;
     u32x4 v[VPT];
     // branch-free loads (index clamped into the row) keep all VPT loads in flight
 #pragma unroll
     for (int j = 0; j < VPT; ++j)
-        v[j] = xt[min(tid + j * kDispatchThreads, nvec - 1)];
+        v[j] = xt[min(tid + j * nthr, nvec - 1)];
     for (int k = 0; k < K; ++k) {
         const int row = token_row[(int64_t)t * K + k];
         if (row < 0 || row >= cap)
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_bf16_kernel(
         u32x4 *dst = recv + (int64_t)row * nvec;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * kDispatchThreads;
+            const int i = tid + j * nthr;
             if (i < nvec)
                 __builtin_nontemporal_store(v[j], dst + i);
         }
@@ -73,19 +73,20 @@ __device__ __forceinline__ uint32_t q8(float f, float ds)
 }
 
 template <int VPT>
-__global__ __launch_bounds__(kDispatchThreads) void dispatch_int8_kernel(
+__global__ __launch_bounds__(kRowMaxThreads) void dispatch_int8_kernel(
     const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
     const float *__restrict__ topk_weights, int64_t cap, u32x2 *__restrict__ recv,
     float *__restrict__ recv_scales, float *__restrict__ recv_weights)
 {
-    __shared__ float s_wmax[kDispatchThreads / kWave];
+    __shared__ float s_wmax[kRowMaxThreads / kWave];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
     const u32x4 *xt = x + (int64_t)t * nvec;
     u32x4 v[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j)
-        v[j] = xt[min(tid + j * kDispatchThreads, nvec - 1)]; // clamped: always in bounds
+        v[j] = xt[min(tid + j * nthr, nvec - 1)]; // clamped: always in bounds
     float m = 0.0f; // a clamped duplicate of a real element cannot change the maximum
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -100,8 +101,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_int8_kernel(
         s_wmax[tid / kWave] = m;
     __syncthreads();
     m = s_wmax[0];
-#pragma unroll
-    for (int w = 1; w < kDispatchThreads / kWave; ++w)
+    for (int w = 1; w < nthr / kWave; ++w)
         m = fmaxf(m, s_wmax[w]);
 
     const float ds = 127.0f / m; // IEEE division (built with correctly rounded fp32 divide)
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_int8_kernel(
         u32x2 *dst = recv + (int64_t)row * nvec;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * kDispatchThreads;
+            const int i = tid + j * nthr;
             if (i < nvec)
                 __builtin_nontemporal_store(q[j], dst + i);
         }
@@ -169,19 +169,20 @@ __device__ __forceinline__ uint32_t e4m3fn_code(float v, uint32_t sign)
 }
 
 template <int VPT>
-__global__ __launch_bounds__(kDispatchThreads) void dispatch_mxfp8_kernel(
+__global__ __launch_bounds__(kRowMaxThreads) void dispatch_mxfp8_kernel(
     const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
     const float *__restrict__ topk_weights, int64_t cap, u32x2 *__restrict__ recv,
     uint8_t *__restrict__ recv_scales, float *__restrict__ recv_weights)
 {
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
     const int nblk = nvec / 4; // 32-element blocks per row; 4 lanes (8 elements each) per block
     const u32x4 *xt = x + (int64_t)t * nvec;
     u32x4 xin[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j)
-        xin[j] = xt[min(tid + j * kDispatchThreads, nvec - 1)]; // clamped: always in bounds
+        xin[j] = xt[min(tid + j * nthr, nvec - 1)]; // clamped: always in bounds
     u32x2 q[VPT];
     uint32_t sbyte[VPT];
 #pragma unroll
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_mxfp8_kernel(
         uint8_t *sdst = recv_scales + (int64_t)row * nblk;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * kDispatchThreads;
+            const int i = tid + j * nthr;
             if (i < nvec) {
                 __builtin_nontemporal_store(q[j], dst + i);
                 if ((i & 3) == 0)
@@ -243,33 +244,30 @@ hipError_t launch_dispatch(const void *x, int T, int H, int K, const int32_t *to
     if (T == 0)
         return hipSuccess;
     const int nvec = H / 8; // 16-byte vectors of bf16 per row
-    const int vpt = (nvec + kDispatchThreads - 1) / kDispatchThreads; // 1..8
-    const dim3 grid(T), block(kDispatchThreads);
+    const int threads = row_block_threads(nvec);
+    const int vpt = (nvec + threads - 1) / threads; // 1 or 2 (H <= 16384)
+    const dim3 grid(T), block(threads);
     const u32x4 *xv = (const u32x4 *)x;
 
 #define MOE_DISPATCH_CASE(V)                                                                       \
     case V:                                                                                        \
         if (quant_mode == MOE_QUANT_NONE)                                                          \
-            hipLaunchKernelGGL(dispatch_bf16_kernel<V>, grid, block, 0, stream, xv, nvec, K,      \
-                               token_row, topk_weights, cap, (u32x4 *)recv_x, recv_weights);       \
-        else if (quant_mode == MOE_QUANT_INT8_PER_TOKEN)                                           \
-            hipLaunchKernelGGL(dispatch_int8_kernel<V>, grid, block, 0, stream, xv, nvec, K,      \
-                               token_row, topk_weights, cap, (u32x2 *)recv_x, (float *)recv_scales, \
-                               recv_weights);                                                      \
-        else                                                                                       \
-            hipLaunchKernelGGL(dispatch_mxfp8_kernel<V>, grid, block, 0, stream, xv, nvec, K,     \
-                               token_row, topk_weights, cap, (u32x2 *)recv_x,                     \
-                               (uint8_t *)recv_scales, recv_weights);                              \
-        break;
+            return launch_kernel(dispatch_bf16_kernel<V>, grid, block, 0, stream, xv, nvec, K,    \
+                                 token_row, topk_weights, cap, (u32x4 *)recv_x, recv_weights);     \
+        if (quant_mode == MOE_QUANT_INT8_PER_TOKEN)                                                \
+            return launch_kernel(dispatch_int8_kernel<V>, grid, block, 0, stream, xv, nvec, K,    \
+                                 token_row, topk_weights, cap, (u32x2 *)recv_x,                   \
+                                 (float *)recv_scales, recv_weights);                              \
+        return launch_kernel(dispatch_mxfp8_kernel<V>, grid, block, 0, stream, xv, nvec, K,       \
+                             token_row, topk_weights, cap, (u32x2 *)recv_x,                       \
+                             (uint8_t *)recv_scales, recv_weights);
 
-    switch (vpt <= 1 ? 1 : vpt <= 2 ? 2 : vpt <= 4 ? 4 : 8) {
+    switch (vpt) {
         MOE_DISPATCH_CASE(1)
         MOE_DISPATCH_CASE(2)
-        MOE_DISPATCH_CASE(4)
-        MOE_DISPATCH_CASE(8)
     }
 #undef MOE_DISPATCH_CASE
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 } // namespace moe

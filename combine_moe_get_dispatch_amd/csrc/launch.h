@@ -6,7 +6,43 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace moe {
+
+// Launch `kernel` and return the status of this launch alone.  (The
+// hipGetLastError() idiom would also report an error some earlier, unrelated
+// HIP call of the caller left pending.)  Arguments are converted to the
+// kernel's parameter types and passed by address, as hipLaunchKernel expects.
+template <typename... KArgs, typename Tuple, size_t... I>
+hipError_t launch_with_tuple(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                             hipStream_t stream, Tuple &params, std::index_sequence<I...>)
+{
+    void *argv[] = {(void *)&std::get<I>(params)..., nullptr};
+    return hipLaunchKernel((const void *)kernel, grid, block, argv, shmem, stream);
+}
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, Args... args)
+{
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> params(static_cast<KArgs>(args)...);
+    return launch_with_tuple(kernel, grid, block, shmem, stream, params,
+                             std::index_sequence_for<KArgs...>{});
+}
+
+// Launch shape of the row kernels (dispatch, combine): one workgroup per
+// token, one 16-byte vector per lane; the workgroup covers the row with
+// ceil(nvec / 64) waves (at most 16), and a lane takes a second vector only
+// when the row has more than 1024 vectors (H > 8192).
+constexpr int kRowMaxThreads = 1024;
+inline int row_block_threads(int nvec)
+{
+    const int t = (nvec + 63) / 64 * 64;
+    return t < kRowMaxThreads ? t : kRowMaxThreads;
+}
 
 // How the layout splits the T*K routing entries into chunks of whole tokens.
 // Every chunk is handled by one workgroup in both layout kernels.  The

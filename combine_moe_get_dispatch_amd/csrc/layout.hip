@@ -101,6 +101,41 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
         flag_tab[chunk] = s_bad;
 }
 
+// Column sums of a [nchunks][W] int32 table (W <= 512), spread over the whole
+// workgroup: kRankThreads / W threads per column, each reading its share of
+// the rows in batches of 8 independent loads (one L2 round trip per batch,
+// instead of one per row).  Adds the full column sum to s_all[col] and, when
+// s_before is given, the sum over rows < `row_end` to s_before[col].
+__device__ __forceinline__ void column_sums(const int32_t *__restrict__ tab, int W, int nchunks,
+                                            int row_end, int *s_all, int *s_before)
+{
+    constexpr int kBatch = 8;
+    const int parts = kRankThreads / W;
+    const int tid = threadIdx.x;
+    if (tid >= parts * W || nchunks == 0)
+        return;
+    const int col = tid % W;
+    const int part = tid / W;
+    int all = 0, before = 0;
+    for (int c0 = part * kBatch; c0 < nchunks; c0 += parts * kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            v[u] = tab[(int64_t)min(c0 + u, nchunks - 1) * W + col]; // clamped: always in bounds
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int c = c0 + u;
+            const int x = c < nchunks ? v[u] : 0;
+            all += x;
+            before += c < row_end ? x : 0;
+        }
+    }
+    if (all)
+        atomicAdd(&s_all[col], all);
+    if (s_before && before)
+        atomicAdd(&s_before[col], before);
+}
+
 __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int a, int tpc, int nchunks,
     int nbits, int64_t cap, const int32_t *__restrict__ cnt_tab, const int32_t *__restrict__ rank_tab,
@@ -111,6 +146,7 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     __shared__ int s_tot[MOE_MAX_EXPERTS];
     __shared__ int s_cb[MOE_MAX_EXPERTS];
     __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_rsum[MOE_MAX_EXPERTS];
     __shared__ int s_wsum[kRankWaves];
     __shared__ int s_w[kRankWaves][MOE_MAX_EXPERTS];
     __shared__ int16_t s_e[kMaxChunkEntries];
@@ -119,30 +155,35 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int chunk = blockIdx.x;
+    const bool has_chunk = chunk < nchunks; // false only when T == 0 (one workgroup then)
+    const int t0 = chunk * tpc;
+    const int nt = has_chunk ? min(tpc, T - t0) : 0;
+    const int ne = nt * K;
+    const int64_t base = (int64_t)t0 * K;
+
+    // (0) issue this chunk's topk_idx loads first, so that their latency
+    // overlaps the table reads below (indices clamped: always in bounds)
+    constexpr int kIdxPerThread = kMaxChunkEntries / kRankThreads;
+    int64_t idx_reg[kIdxPerThread];
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u) // the guard is uniform over the workgroup
+        idx_reg[u] = u * kRankThreads < ne ? topk_idx[base + min(tid + u * kRankThreads, ne - 1)] : -1;
 
     // (1) expert totals over all chunks, and the part of them in chunks before this one
     for (int e = tid; e < E; e += kRankThreads) {
         s_tot[e] = 0;
         s_cb[e] = 0;
     }
+    for (int i = tid; i < kRankWaves * E; i += kRankThreads)
+        s_w[i / E][i % E] = 0;
     __syncthreads();
-    {
-        const int parts = kRankThreads / E; // >= 2 since E <= 512
-        if (tid < parts * E) {
-            const int e = tid % E;
-            const int part = tid / E;
-            const int c_lo = (int)((int64_t)part * nchunks / parts);
-            const int c_hi = (int)((int64_t)(part + 1) * nchunks / parts);
-            int tot = 0, cb = 0;
-            for (int c = c_lo; c < c_hi; ++c) {
-                const int v = cnt_tab[(int64_t)c * E + e];
-                tot += v;
-                cb += (c < chunk) ? v : 0;
-            }
-            if (tot)
-                atomicAdd(&s_tot[e], tot);
-            if (cb)
-                atomicAdd(&s_cb[e], cb);
+    column_sums(cnt_tab, E, nchunks, chunk, s_tot, s_cb);
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u) {
+        const int i = tid + u * kRankThreads;
+        if (i < ne) {
+            const int64_t v = idx_reg[u];
+            s_e[i] = (v < 0 || v >= E) ? (int16_t)-1 : (int16_t)v;
         }
     }
     __syncthreads();
@@ -188,12 +229,13 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
         }
         for (int e = tid; e <= E; e += kRankThreads)
             off[e] = s_off[e];
-        for (int r = tid; r < R; r += kRankThreads) {
-            int s = 0;
-            for (int c = 0; c < nchunks; ++c)
-                s += rank_tab[(int64_t)c * R + r];
-            ntpr[r] = s;
-        }
+        for (int r = tid; r < R; r += kRankThreads)
+            s_rsum[r] = 0;
+        __syncthreads();
+        column_sums(rank_tab, R, nchunks, 0, s_rsum, nullptr);
+        __syncthreads();
+        for (int r = tid; r < R; r += kRankThreads)
+            ntpr[r] = s_rsum[r];
         if (wave == 0) {
             int f = 0;
             for (int c = lane; c < nchunks; c += kWave)
@@ -218,22 +260,10 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
          row += (int64_t)gridDim.x * kRankThreads)
         recv_src[row] = -1;
 
-    if (chunk >= nchunks) // only when T == 0 (a single workgroup then)
+    if (!has_chunk)
         return;
 
-    // (5) rank this chunk's entries
-    const int t0 = chunk * tpc;
-    const int nt = min(tpc, T - t0);
-    const int ne = nt * K;
-    const int64_t base = (int64_t)t0 * K;
-    for (int i = tid; i < ne; i += kRankThreads) {
-        const int64_t v = topk_idx[base + i];
-        s_e[i] = (v < 0 || v >= E) ? (int16_t)-1 : (int16_t)v;
-    }
-    for (int i = tid; i < kRankWaves * E; i += kRankThreads)
-        s_w[i / E][i % E] = 0;
-    __syncthreads();
-
+    // (5) rank this chunk's entries (ids already in s_e)
     // each wave owns a contiguous run of entries, in flat order
     const int per_wave = ((ne + kRankWaves * kWave - 1) / (kRankWaves * kWave)) * kWave;
     const int w_lo = wave * per_wave;
@@ -293,15 +323,17 @@ hipError_t launch_layout(const LayoutArgs &A, const LayoutPlan &P, hipStream_t s
     int32_t *cnt_tab = A.workspace;
     int32_t *rank_tab = cnt_tab ? cnt_tab + (size_t)nchunks * A.E : nullptr;
     int32_t *flag_tab = rank_tab ? rank_tab + (size_t)nchunks * A.R : nullptr;
-    if (nchunks > 0)
-        hipLaunchKernelGGL(layout_count_kernel, dim3(nchunks), dim3(kCountThreads), 0, stream,
-                           A.topk_idx, A.T, A.K, A.E, A.R, L, P.tokens_per_chunk, nbits, A.itr,
-                           cnt_tab, rank_tab, flag_tab);
-    hipLaunchKernelGGL(layout_rank_kernel, dim3(nchunks > 0 ? nchunks : 1), dim3(kRankThreads), 0,
-                       stream, A.topk_idx, A.T, A.K, A.E, A.R, A.a, P.tokens_per_chunk, nchunks,
-                       nbits, A.cap, cnt_tab, rank_tab, flag_tab, A.ntpr, A.ntpe, A.nrtpe, A.off,
-                       A.token_row, A.recv_src, A.error_flag);
-    return hipGetLastError();
+    if (nchunks > 0) {
+        const hipError_t err = launch_kernel(
+            layout_count_kernel, dim3(nchunks), dim3(kCountThreads), 0, stream, A.topk_idx, A.T,
+            A.K, A.E, A.R, L, P.tokens_per_chunk, nbits, A.itr, cnt_tab, rank_tab, flag_tab);
+        if (err != hipSuccess)
+            return err;
+    }
+    return launch_kernel(layout_rank_kernel, dim3(nchunks > 0 ? nchunks : 1), dim3(kRankThreads), 0,
+                         stream, A.topk_idx, A.T, A.K, A.E, A.R, A.a, P.tokens_per_chunk, nchunks,
+                         nbits, A.cap, cnt_tab, rank_tab, flag_tab, A.ntpr, A.ntpe, A.nrtpe, A.off,
+                         A.token_row, A.recv_src, A.error_flag);
 }
 
 } // namespace moe

@@ -233,3 +233,23 @@ def test_deterministic_repeat():
     used = a[0]["recv_src"] >= 0
     assert torch.equal(a[1][used], b[1][used]) and torch.equal(a[2][used], b[2][used])
     assert torch.equal(a[3].view(torch.int16), b[3].view(torch.int16))
+
+
+def test_pending_unrelated_hip_error_does_not_fail_calls():
+    """A HIP error left pending by an unrelated host-side call (a device
+    attribute query for a device that does not exist) must not be reported
+    by the library's own launches."""
+    import ctypes
+    path = [l.split()[-1] for l in open("/proc/self/maps").read().split("\n") if "libamdhip64" in l][0]
+    hip = ctypes.CDLL(path)
+    v = ctypes.c_int()
+    assert hip.hipDeviceGetAttribute(ctypes.byref(v), 0, 9999) != 0     # leaves an error pending
+    rng = np.random.default_rng(1)
+    idx, wts = _routing(rng, 64, 2, 8)
+    lay = gpu_layout(idx, 8, 2, 1)
+    x = bf16_dev(W.f32_to_bf16_bits(rng.standard_normal((64, 64)).astype(np.float32)))
+    rx, _, _ = moe.moe_dispatch(x, lay, None, 0)
+    moe.moe_combine(rx, lay, None)
+    torch.cuda.synchronize()
+    hip.hipGetLastError()                                               # leave no error behind
+    assert_layout_equal(layout_to_host(lay), oracle.layout(idx, 8, 2, 1))
