@@ -253,3 +253,55 @@ def test_pending_unrelated_hip_error_does_not_fail_calls():
     torch.cuda.synchronize()
     hip.hipGetLastError()                                               # leave no error behind
     assert_layout_equal(layout_to_host(lay), oracle.layout(idx, 8, 2, 1))
+
+
+@pytest.mark.parametrize("quant", [0, 2, 4])
+def test_graph_capture_replays_match_eager(quant):
+    """The three calls allocate nothing and never synchronise, so a step can be
+    captured in a HIP graph.  Replay it several times, with eager work and
+    synchronisations in between, and check every replay against the eager
+    result (layout, rows, scales, combine output)."""
+    rng = np.random.default_rng(40 + quant)
+    T, H, K, E, R, a = 300, 512, 4, 32, 4, 8
+    idx, wts = _routing(rng, T, K, E, drop=0.05)
+    x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    idx_d = torch.from_numpy(idx).to(DEV)
+    x = bf16_dev(x_bits)
+    w = torch.from_numpy(wts).to(DEV)
+    lay = moe.allocate_layout(T, K, E, R, a, device=DEV)
+    rx, rs, _ = moe.allocate_recv(lay, H, quant)
+    y = bf16_dev(W.random_bf16_rows(lay.recv_capacity, H, 7))
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        moe.moe_get_dispatch_layout(idx_d, E, R, a, out=lay)
+        moe.moe_dispatch(x, lay, None, quant, recv_x=rx, recv_scales=rs)
+        moe.moe_combine(y, lay, w, out=out)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        used = lay.recv_src >= 0
+        return (lay.token_row.clone(), lay.recv_src.clone(), lay.expert_offsets.clone(),
+                rx.view(torch.uint8)[used].clone(),
+                None if rs is None else rs.view(torch.uint8)[used].clone(),
+                out.view(torch.int16).clone())
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    ref = snapshot()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        for t_ in (lay.token_row, lay.recv_src, lay.expert_offsets, out):
+            t_.fill_(7)
+        rx.view(torch.uint8).fill_(3)
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for a_, b_ in zip(ref, got):
+            if a_ is not None:
+                assert torch.equal(a_, b_)
