@@ -283,7 +283,7 @@ def test_graph_capture_replays_match_eager(quant):
         used = lay.recv_src >= 0
         return (lay.token_row.clone(), lay.recv_src.clone(), lay.expert_offsets.clone(),
                 rx.view(torch.uint8)[used].clone(),
-                None if rs is None else rs.view(torch.uint8)[used].clone(),
+                None if rs is None else (rs.view(torch.int32) if rs.dim() == 1 else rs)[used].clone(),
                 out.view(torch.int16).clone())
 
     s = torch.cuda.Stream()
