@@ -55,7 +55,7 @@ constexpr int kMaxChunkFlags = 16384;
 struct LayoutPlan {
     int tokens_per_chunk;
     int num_chunks;
-    size_t workspace_bytes; // count table [chunks][E] + rank table [chunks][R] + flags [chunks]
+    size_t workspace_bytes; // count table [chunks][E rounded up to 4] + rank table [chunks][R] + flags [chunks]
 };
 
 inline LayoutPlan plan_layout(int T, int K, int E, int R)
@@ -72,7 +72,7 @@ inline LayoutPlan plan_layout(int T, int K, int E, int R)
         tpc = 1;
     p.tokens_per_chunk = tpc;
     p.num_chunks = (T + tpc - 1) / tpc;
-    p.workspace_bytes = (size_t)p.num_chunks * (size_t)(E + R + 1) * sizeof(int32_t);
+    p.workspace_bytes = (size_t)p.num_chunks * (size_t)(((E + 3) & ~3) + R + 1) * sizeof(int32_t);
     return p;
 }
 

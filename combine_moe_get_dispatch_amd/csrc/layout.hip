@@ -30,9 +30,40 @@
 
 namespace moe {
 
-constexpr int kCountThreads = 512;
+constexpr int kCountThreads = 1024;
 constexpr int kRankThreads = 1024;
 constexpr int kRankWaves = kRankThreads / kWave;
+constexpr int kIdxPerThread = kMaxChunkEntries / 1024; // topk_idx entries prefetched per thread
+constexpr int kRankCellsPerThread = 2; // per-chunk rank counts prefetched per thread
+constexpr int kRankSumSlots = 512;     // ranks one workgroup can sum (R <= 512)
+constexpr int kTabRows = 16;           // expert-table rows prefetched per thread
+
+static_assert(kCountThreads == 1024 && kRankThreads == 1024, "prefetch sizes assume 1024 threads");
+
+// Issue this chunk's topk_idx loads (one per thread and pass of 1024 entries;
+// the pass guard is uniform over the workgroup, the index clamped into range).
+__device__ __forceinline__ void prefetch_idx(const int64_t *__restrict__ topk_idx, int64_t base,
+                                             int ne, int64_t (&reg)[kIdxPerThread])
+{
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u)
+        reg[u] = u * 1024 < ne ? topk_idx[base + min((int)threadIdx.x + u * 1024, ne - 1)] : -1;
+}
+
+// Exclusive prefix over the 16 lanes of each lane group of 16 (width-16
+// shuffles); returns the exclusive value, *total gets the group's sum.
+__device__ __forceinline__ int exclusive_scan16(int v, int *total)
+{
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+        const int u = __shfl_up(incl, d, 16);
+        if ((threadIdx.x & 15) >= d)
+            incl += u;
+    }
+    *total = __shfl(incl, 15, 16);
+    return incl - v;
+}
 
 __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int L, int tpc, int nbits,
@@ -51,6 +82,9 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     const int ne = nt * K;
     const int64_t base = (int64_t)t0 * K;
 
+    int64_t idx_reg[kIdxPerThread];
+    prefetch_idx(topk_idx, base, ne, idx_reg); // in flight while LDS is cleared
+
     for (int i = tid; i < E; i += kCountThreads)
         s_hist[i] = 0;
     for (int i = tid; i < R; i += kCountThreads)
@@ -62,11 +96,14 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     __syncthreads();
 
     int bad = 0;
-    for (int i0 = 0; i0 < ne; i0 += kCountThreads) { // uniform trip count: ballots stay convergent
-        const int i = i0 + tid;
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u) {
+        if (u * kCountThreads >= ne) // uniform: ballots below stay convergent
+            break;
+        const int i = tid + u * kCountThreads;
         int e = -1;
         if (i < ne) {
-            const int64_t v = topk_idx[base + i];
+            const int64_t v = idx_reg[u];
             if (v < -1 || v >= E)
                 bad = 1;
             else
@@ -84,56 +121,34 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
         atomicOr(&s_bad, 1);
     __syncthreads();
 
-    int32_t *itr_chunk = itr + (int64_t)t0 * R;
-    for (int p = tid; p < nt * R; p += kCountThreads) {
-        const int f = s_flags[p];
-        itr_chunk[p] = f;
-        if (f)
-            atomicAdd(&s_rcnt[p % R], 1);
+    // is_token_in_rank rows and per-rank token counts: thread (r, part) owns
+    // rank r of tokens part, part + parts, ...; a wave's stores cover
+    // consecutive (token, rank) cells, and each thread adds its count once
+    {
+        const int parts = kCountThreads / R; // >= 2 (R <= 512)
+        if (tid < parts * R) {
+            const int r = tid % R;
+            const int part = tid / R;
+            int32_t *itr_chunk = itr + (int64_t)t0 * R;
+            int cnt = 0;
+            for (int t = part; t < nt; t += parts) {
+                const int f = s_flags[t * R + r];
+                itr_chunk[t * R + r] = f;
+                cnt += f;
+            }
+            if (cnt)
+                atomicAdd(&s_rcnt[r], cnt);
+        }
     }
     __syncthreads();
 
-    for (int e = tid; e < E; e += kCountThreads)
-        cnt_tab[(int64_t)chunk * E + e] = s_hist[e];
+    const int Ep = (E + 3) & ~3; // table rows padded to whole 16-byte vectors
+    for (int e = tid; e < Ep; e += kCountThreads)
+        cnt_tab[(int64_t)chunk * Ep + e] = e < E ? s_hist[e] : 0;
     for (int r = tid; r < R; r += kCountThreads)
         rank_tab[(int64_t)chunk * R + r] = s_rcnt[r];
     if (tid == 0)
         flag_tab[chunk] = s_bad;
-}
-
-// Column sums of a [nchunks][W] int32 table (W <= 512), spread over the whole
-// workgroup: kRankThreads / W threads per column, each reading its share of
-// the rows in batches of 8 independent loads (one L2 round trip per batch,
-// instead of one per row).  Adds the full column sum to s_all[col] and, when
-// s_before is given, the sum over rows < `row_end` to s_before[col].
-__device__ __forceinline__ void column_sums(const int32_t *__restrict__ tab, int W, int nchunks,
-                                            int row_end, int *s_all, int *s_before)
-{
-    constexpr int kBatch = 8;
-    const int parts = kRankThreads / W;
-    const int tid = threadIdx.x;
-    if (tid >= parts * W || nchunks == 0)
-        return;
-    const int col = tid % W;
-    const int part = tid / W;
-    int all = 0, before = 0;
-    for (int c0 = part * kBatch; c0 < nchunks; c0 += parts * kBatch) {
-        int v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-            v[u] = tab[(int64_t)min(c0 + u, nchunks - 1) * W + col]; // clamped: always in bounds
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int c = c0 + u;
-            const int x = c < nchunks ? v[u] : 0;
-            all += x;
-            before += c < row_end ? x : 0;
-        }
-    }
-    if (all)
-        atomicAdd(&s_all[col], all);
-    if (s_before && before)
-        atomicAdd(&s_before[col], before);
 }
 
 __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
@@ -146,8 +161,9 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     __shared__ int s_tot[MOE_MAX_EXPERTS];
     __shared__ int s_cb[MOE_MAX_EXPERTS];
     __shared__ int s_off[MOE_MAX_EXPERTS + 1];
-    __shared__ int s_rsum[MOE_MAX_EXPERTS];
+    __shared__ int s_rsum[kRankSumSlots];
     __shared__ int s_wsum[kRankWaves];
+    __shared__ int s_flag;
     __shared__ int s_w[kRankWaves][MOE_MAX_EXPERTS];
     __shared__ int16_t s_e[kMaxChunkEntries];
 
@@ -155,29 +171,104 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int chunk = blockIdx.x;
+    const int nblocks = gridDim.x;
     const bool has_chunk = chunk < nchunks; // false only when T == 0 (one workgroup then)
     const int t0 = chunk * tpc;
     const int nt = has_chunk ? min(tpc, T - t0) : 0;
     const int ne = nt * K;
     const int64_t base = (int64_t)t0 * K;
 
-    // (0) issue this chunk's topk_idx loads first, so that their latency
-    // overlaps the table reads below (indices clamped: always in bounds)
-    constexpr int kIdxPerThread = kMaxChunkEntries / kRankThreads;
+    // (0) Every global load the workgroup needs is issued here, before the
+    // first barrier (a barrier waits for all outstanding loads), so that the
+    // kernel pays one memory round trip:
+    //   - this chunk's topk_idx entries;
+    //   - the expert-count table [nchunks][Ep] (Ep = E rounded up to 4): a
+    //     thread owns 4 adjacent columns (one 16-byte load per row) and up to
+    //     kTabRows rows; rows beyond parts * kTabRows (very many chunks only)
+    //     are read in later passes;
+    //   - the per-chunk counts of the ranks this workgroup sums (ranks
+    //     r = chunk, chunk + nblocks, ...), one (rank, chunk) cell per thread
+    //     and pass;
+    //   - in workgroup 0, the per-chunk error flags.
     int64_t idx_reg[kIdxPerThread];
-#pragma unroll
-    for (int u = 0; u < kIdxPerThread; ++u) // the guard is uniform over the workgroup
-        idx_reg[u] = u * kRankThreads < ne ? topk_idx[base + min(tid + u * kRankThreads, ne - 1)] : -1;
+    prefetch_idx(topk_idx, base, ne, idx_reg);
 
-    // (1) expert totals over all chunks, and the part of them in chunks before this one
+    const int groups = (E + 3) / 4; // <= 128
+    const int parts = kRankThreads / groups; // >= 8
+    const int g = tid % groups;
+    const int part = tid / groups;
+    const bool tab_thread = tid < parts * groups;
+    const int rb = min(kTabRows, (nchunks + parts - 1) / parts); // rows per thread and pass (uniform)
+    const int4 *tab4 = (const int4 *)cnt_tab;
+    int4 tab_reg[kTabRows];
+#pragma unroll
+    for (int u = 0; u < kTabRows; ++u) {
+        tab_reg[u] = int4{0, 0, 0, 0};
+        if (u < rb) // uniform
+            tab_reg[u] = tab4[(int64_t)min(part * rb + u, nchunks - 1) * groups + g];
+    }
+
+    const int my_ranks = nchunks > 0 && chunk < R ? (R - 1 - chunk) / nblocks + 1 : 0;
+    const int rank_cells = my_ranks * nchunks;
+    int rank_reg[kRankCellsPerThread];
+#pragma unroll
+    for (int u = 0; u < kRankCellsPerThread; ++u) {
+        rank_reg[u] = 0;
+        if (u * kRankThreads < rank_cells) { // uniform
+            const int cell = min(tid + u * kRankThreads, rank_cells - 1);
+            rank_reg[u] = rank_tab[(int64_t)(cell % nchunks) * R + chunk + (cell / nchunks) * nblocks];
+        }
+    }
+    int flag_reg = 0;
+    if (chunk == 0)
+        for (int c = tid; c < nchunks; c += kRankThreads)
+            flag_reg |= flag_tab[c];
+
+    // (1) expert totals over all chunks, and the part of them in chunks
+    // before this one; this chunk's ids into LDS; this workgroup's rank sums
     for (int e = tid; e < E; e += kRankThreads) {
         s_tot[e] = 0;
         s_cb[e] = 0;
     }
     for (int i = tid; i < kRankWaves * E; i += kRankThreads)
         s_w[i / E][i % E] = 0;
+    for (int i = tid; i < kRankSumSlots; i += kRankThreads)
+        s_rsum[i] = 0;
+    if (tid == 0)
+        s_flag = 0;
     __syncthreads();
-    column_sums(cnt_tab, E, nchunks, chunk, s_tot, s_cb);
+
+    if (tab_thread && nchunks > 0) {
+        int all[4] = {0, 0, 0, 0}, before[4] = {0, 0, 0, 0};
+        auto add_row = [&](int r, const int4 v) {
+            const int keep = r < nchunks ? 1 : 0;
+            const int early = r < chunk ? keep : 0;
+            all[0] += keep * v.x;
+            all[1] += keep * v.y;
+            all[2] += keep * v.z;
+            all[3] += keep * v.w;
+            before[0] += early * v.x;
+            before[1] += early * v.y;
+            before[2] += early * v.z;
+            before[3] += early * v.w;
+        };
+#pragma unroll
+        for (int u = 0; u < kTabRows; ++u)
+            if (u < rb)
+                add_row(part * rb + u, tab_reg[u]);
+        for (int r = parts * rb + part; r < nchunks; r += parts) // only for very many chunks
+            add_row(r, tab4[(int64_t)r * groups + g]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int e = 4 * g + c;
+            if (e < E) {
+                if (all[c])
+                    atomicAdd(&s_tot[e], all[c]);
+                if (before[c])
+                    atomicAdd(&s_cb[e], before[c]);
+            }
+        }
+    }
 #pragma unroll
     for (int u = 0; u < kIdxPerThread; ++u) {
         const int i = tid + u * kRankThreads;
@@ -186,6 +277,17 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
             s_e[i] = (v < 0 || v >= E) ? (int16_t)-1 : (int16_t)v;
         }
     }
+#pragma unroll
+    for (int u = 0; u < kRankCellsPerThread; ++u) {
+        const int cell = tid + u * kRankThreads;
+        if (cell < rank_cells && rank_reg[u])
+            atomicAdd(&s_rsum[cell / nchunks], rank_reg[u]);
+    }
+    for (int cell = tid + kRankCellsPerThread * kRankThreads; cell < rank_cells; cell += kRankThreads)
+        atomicAdd(&s_rsum[cell / nchunks],
+                  rank_tab[(int64_t)(cell % nchunks) * R + chunk + (cell / nchunks) * nblocks]);
+    if (flag_reg)
+        atomicOr(&s_flag, flag_reg);
     __syncthreads();
 
     // (2) aligned counts and their exclusive prefix sum ("/" is integer
@@ -206,13 +308,12 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     if (lane == kWave - 1)
         s_wsum[wave] = incl;
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int w = 0; w < kRankWaves; ++w) {
-            const int v = s_wsum[w];
-            s_wsum[w] = run;
-            run += v;
-        }
+    if (wave == 0) { // exclusive scan of the 16 wave sums by the first 16 lanes
+        int total;
+        const int v = lane < kRankWaves ? s_wsum[lane] : 0;
+        const int ex = exclusive_scan16(v, &total);
+        if (lane < kRankWaves)
+            s_wsum[lane] = ex;
     }
     __syncthreads();
     if (tid < E)
@@ -221,7 +322,8 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
         s_off[E] = s_wsum[wave] + incl;
     __syncthreads();
 
-    // (3) the small per-expert / per-rank outputs, once
+    // (3) the small outputs: per-expert ones and the error flag from workgroup
+    // 0, each rank's token count from the workgroup that summed it
     if (chunk == 0) {
         for (int e = tid; e < E; e += kRankThreads) {
             ntpe[e] = s_tot[e];
@@ -229,42 +331,32 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
         }
         for (int e = tid; e <= E; e += kRankThreads)
             off[e] = s_off[e];
-        for (int r = tid; r < R; r += kRankThreads)
-            s_rsum[r] = 0;
-        __syncthreads();
-        column_sums(rank_tab, R, nchunks, 0, s_rsum, nullptr);
-        __syncthreads();
-        for (int r = tid; r < R; r += kRankThreads)
-            ntpr[r] = s_rsum[r];
-        if (wave == 0) {
-            int f = 0;
-            for (int c = lane; c < nchunks; c += kWave)
-                f |= flag_tab[c];
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1)
-                f |= __shfl_xor(f, o, kWave);
-            if (lane == 0)
-                *error_flag = f;
-        }
+        if (tid == 0)
+            *error_flag = s_flag;
     }
+    for (int j = tid; j < my_ranks; j += kRankThreads)
+        ntpr[chunk + j * nblocks] = s_rsum[j];
+    if (nchunks == 0)
+        for (int r = tid; r < R; r += kRankThreads)
+            ntpr[r] = 0;
 
     // (4) rows holding no entry: alignment padding inside each expert, and
     // every row past the last expert up to the capacity
-    for (int e = chunk; e < E; e += gridDim.x) {
+    for (int e = chunk; e < E; e += nblocks) {
         const int lo = s_off[e] + s_tot[e];
         const int hi = s_off[e + 1];
         for (int row = lo + tid; row < hi; row += kRankThreads)
             recv_src[row] = -1;
     }
     for (int64_t row = (int64_t)s_off[E] + (int64_t)chunk * kRankThreads + tid; row < cap;
-         row += (int64_t)gridDim.x * kRankThreads)
+         row += (int64_t)nblocks * kRankThreads)
         recv_src[row] = -1;
 
     if (!has_chunk)
         return;
 
-    // (5) rank this chunk's entries (ids already in s_e)
-    // each wave owns a contiguous run of entries, in flat order
+    // (5) rank this chunk's entries (ids in s_e); each wave owns a contiguous
+    // run of entries, in flat order
     const int per_wave = ((ne + kRankWaves * kWave - 1) / (kRankWaves * kWave)) * kWave;
     const int w_lo = wave * per_wave;
     const int w_hi = min(ne, w_lo + per_wave);
@@ -278,8 +370,11 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
             s_w[wave][e] += __popcll(same); // one writer per (wave, expert)
     }
     __syncthreads();
+    // exclusive scan over the 16 waves of every expert's count, one thread per
+    // expert (consecutive experts: conflict-free LDS banks)
     for (int e = tid; e < E; e += kRankThreads) {
         int run = 0;
+#pragma unroll
         for (int w = 0; w < kRankWaves; ++w) {
             const int v = s_w[w][e];
             s_w[w][e] = run;
@@ -321,7 +416,7 @@ hipError_t launch_layout(const LayoutArgs &A, const LayoutPlan &P, hipStream_t s
     const int nbits = key_bits(A.E);
     const int nchunks = P.num_chunks;
     int32_t *cnt_tab = A.workspace;
-    int32_t *rank_tab = cnt_tab ? cnt_tab + (size_t)nchunks * A.E : nullptr;
+    int32_t *rank_tab = cnt_tab ? cnt_tab + (size_t)nchunks * ((A.E + 3) & ~3) : nullptr;
     int32_t *flag_tab = rank_tab ? rank_tab + (size_t)nchunks * A.R : nullptr;
     if (nchunks > 0) {
         const hipError_t err = launch_kernel(

@@ -82,7 +82,7 @@ int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_top
     const LayoutPlan plan = plan_layout(T, K, E, R);
     if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
         return MOE_ERR_WORKSPACE;
-    if (((uintptr_t)workspace & 3u) != 0)
+    if (((uintptr_t)workspace & 15u) != 0)
         return MOE_ERR_WORKSPACE;
 
     LayoutArgs args;

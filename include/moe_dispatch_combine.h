@@ -48,7 +48,7 @@ extern "C" {
 #define MOE_OK 0
 #define MOE_ERR_INVALID_ARG (-1) /* a size, range or pointer argument is invalid */
 #define MOE_ERR_CAPACITY (-2)    /* recv_capacity below moe_recv_capacity_bound()  */
-#define MOE_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required     */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace missing, misaligned or too small      */
 #define MOE_ERR_HIP (-4)         /* a HIP launch failed                            */
 
 /* Quantisation modes, numbered like quantMode in the CANN page's Formula. */
@@ -108,8 +108,9 @@ size_t moe_layout_workspace_bytes(int num_tokens, int num_topk, int num_experts,
  *   error_flag                 int32 [1]    MOE_FLAG_* bits; 0 if all ids were valid
  * Within an expert, rows follow ascending t*K + k.  An id outside [-1, E) sets
  * MOE_FLAG_BAD_EXPERT_ID and the entry is treated as -1.
- * Workspace: device, >= moe_layout_workspace_bytes(T, K, E, R) bytes (may be
- * NULL when that is 0).
+ * Workspace: device, 16-byte aligned, >= moe_layout_workspace_bytes(T, K, E, R)
+ * bytes (may be NULL when that is 0).  Must not be shared by calls that may
+ * run at the same time.
  * Errors: MOE_ERR_INVALID_ARG (ranges, NULL outputs), MOE_ERR_CAPACITY,
  * MOE_ERR_WORKSPACE, MOE_ERR_HIP.
  */
