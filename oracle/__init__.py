@@ -27,6 +27,11 @@ ERR_CAPACITY = -2
 QUANT_NONE = 0
 QUANT_INT8 = 2
 QUANT_MXFP8 = 4
+QUANT_FP8_E4M3_PT = 0x12
+QUANT_FP8_E5M2_PT = 0x22
+QUANT_MXFP8_E5M2 = 0x24
+PER_TOKEN_SCALE_MODES = (QUANT_INT8, QUANT_FP8_E4M3_PT, QUANT_FP8_E5M2_PT)
+MX_MODES = (QUANT_MXFP8, QUANT_MXFP8_E5M2)
 
 GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
              "-shared", "-fPIC", "-Wall", "-Wextra"]
@@ -74,6 +79,16 @@ def lib() -> ctypes.CDLL:
         L.oracle_quant_int8_rows.restype = None
         L.oracle_quant_mxfp8_rows.argtypes = [_P, i32, i32, _P, _P]
         L.oracle_quant_mxfp8_rows.restype = None
+        L.oracle_check_prequant_args.argtypes = [i32, i32, i32, i32, i64]
+        L.oracle_check_prequant_args.restype = i32
+        L.oracle_dispatch_prequantized.argtypes = [_P, i32, i32, _P, i32, i32, _P, _P, i64, _P, _P, _P]
+        L.oracle_dispatch_prequantized.restype = i32
+        L.oracle_cast_to_fp8_e5m2_array.argtypes = [_P, i64, _P]
+        L.oracle_cast_to_fp8_e5m2_array.restype = None
+        L.oracle_quant_mx_e5m2_rows.argtypes = [_P, i32, i32, _P, _P]
+        L.oracle_quant_mx_e5m2_rows.restype = None
+        L.oracle_quant_fp8_pertoken_rows.argtypes = [_P, i32, i32, i32, _P, _P]
+        L.oracle_quant_fp8_pertoken_rows.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = i32
         _lib = L
@@ -145,9 +160,9 @@ def dispatch(x_bits: np.ndarray, token_row: np.ndarray, recv_capacity: int,
         dt = np.uint16 if quant_mode == QUANT_NONE else (np.int8 if quant_mode == QUANT_INT8 else np.uint8)
         recv_x = np.zeros((cap, H), dt)
     if recv_scales is None:
-        if quant_mode == QUANT_INT8:
+        if quant_mode in PER_TOKEN_SCALE_MODES:
             recv_scales = np.zeros(cap, np.float32)
-        elif quant_mode == QUANT_MXFP8:
+        elif quant_mode in MX_MODES:
             recv_scales = np.zeros((cap, H // 32), np.uint8)
     recv_w = np.zeros(cap, np.float32) if with_weights else None
     rc = lib().oracle_dispatch(_ptr(x), T, H, K, _ptr(row), _ptr(w), cap, quant_mode,
@@ -155,6 +170,38 @@ def dispatch(x_bits: np.ndarray, token_row: np.ndarray, recv_capacity: int,
     if rc != OK:
         raise OracleError(rc)
     return recv_x, recv_scales, recv_w
+
+
+def check_prequant_args(T, row_bytes, scale_bytes, K, cap) -> int:
+    return int(lib().oracle_check_prequant_args(T, row_bytes, scale_bytes, K, cap))
+
+
+def dispatch_prequantized(data: np.ndarray, scales, token_row: np.ndarray, recv_capacity: int,
+                          topk_weights=None, recv_data=None, recv_scales=None, with_weights=False):
+    """Copy pre-quantised rows (data [T, row_bytes] and scales [T, scale_bytes],
+    any byte dtype) to their layout rows.  Returns (recv_data, recv_scales, recv_weights)."""
+    d = np.ascontiguousarray(data).view(np.uint8)
+    T, row_bytes = d.shape
+    if scales is None:
+        sc, scale_bytes = None, 0
+    else:
+        sc = np.ascontiguousarray(scales).view(np.uint8)
+        scale_bytes = sc.shape[1]
+    row = np.ascontiguousarray(token_row, dtype=np.int32)
+    K = row.shape[1]
+    cap = recv_capacity
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    if recv_data is None:
+        recv_data = np.zeros((cap, row_bytes), np.uint8)
+    if recv_scales is None and scale_bytes:
+        recv_scales = np.zeros((cap, scale_bytes), np.uint8)
+    recv_w = np.zeros(cap, np.float32) if with_weights else None
+    rc = lib().oracle_dispatch_prequantized(_ptr(d), T, row_bytes, _ptr(sc), scale_bytes, K,
+                                            _ptr(row), _ptr(w), cap, _ptr(recv_data),
+                                            _ptr(recv_scales), _ptr(recv_w))
+    if rc != OK:
+        raise OracleError(rc)
+    return recv_data, recv_scales, recv_w
 
 
 def combine(y_bits: np.ndarray, token_row: np.ndarray, topk_weights: np.ndarray | None = None) -> np.ndarray:
@@ -176,6 +223,31 @@ def cast_to_fp8_e4m3fn(v: np.ndarray) -> np.ndarray:
     out = np.zeros(v.shape, np.uint8)
     lib().oracle_cast_to_fp8_e4m3fn_array(_ptr(v), v.size, _ptr(out))
     return out
+
+
+def cast_to_fp8_e5m2(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.zeros(v.shape, np.uint8)
+    lib().oracle_cast_to_fp8_e5m2_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def quant_mx_e5m2_rows(x_bits: np.ndarray):
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    q = np.zeros((T, H), np.uint8)
+    s = np.zeros((T, H // 32), np.uint8)
+    lib().oracle_quant_mx_e5m2_rows(_ptr(x), T, H, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_fp8_pertoken_rows(x_bits: np.ndarray, fmt: str = "e4m3"):
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    q = np.zeros((T, H), np.uint8)
+    s = np.zeros(T, np.float32)
+    lib().oracle_quant_fp8_pertoken_rows(_ptr(x), T, H, {"e4m3": 1, "e5m2": 2}[fmt], _ptr(q), _ptr(s))
+    return q, s
 
 
 def quant_int8_rows(x_bits: np.ndarray):

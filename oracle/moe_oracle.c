@@ -46,8 +46,23 @@ enum {
     ORC_ERR_CAPACITY = -2,
 };
 
-/* Quantisation modes, numbered as the quantMode of [CANN] Formula. */
-enum { ORC_QUANT_NONE = 0, ORC_QUANT_INT8 = 2, ORC_QUANT_MXFP8 = 4 };
+/* Quantisation modes.  The low 4 bits are the quantMode of [CANN] Formula
+ * (0 none, 2 per-token dynamic, 4 MX); the next 4 bits select the
+ * destination type where the page allows more than one ([CANN] Constraint 8,
+ * Ascend 950: quantMode 2 may write INT8, FLOAT8_E4M3FN or FLOAT8_E5M2;
+ * quantMode 4 FLOAT8_E4M3FN or FLOAT8_E5M2): 0 = the default (int8 for mode
+ * 2, e4m3fn for mode 4), 1 = e4m3fn, 2 = e5m2. */
+enum {
+    ORC_QUANT_NONE = 0,
+    ORC_QUANT_INT8 = 2,
+    ORC_QUANT_MXFP8 = 4,
+    ORC_QUANT_FP8_E4M3_PT = 0x12,
+    ORC_QUANT_FP8_E5M2_PT = 0x22,
+    ORC_QUANT_MXFP8_E5M2 = 0x24,
+};
+
+/* 8-bit float element formats. */
+enum { FMT_E4M3FN = 1, FMT_E5M2 = 2 };
 
 /* ------------------------------------------------------------------------- */
 /* Argument rules (host-side validation the library must reproduce).          */
@@ -90,7 +105,20 @@ int oracle_check_rows_args(int T, int H, int K, int64_t cap, int quant_mode)
         cap > INT32_MAX)
         return ORC_ERR_INVALID_ARG;
     if (quant_mode != ORC_QUANT_NONE && quant_mode != ORC_QUANT_INT8 &&
-        quant_mode != ORC_QUANT_MXFP8)
+        quant_mode != ORC_QUANT_MXFP8 && quant_mode != ORC_QUANT_FP8_E4M3_PT &&
+        quant_mode != ORC_QUANT_FP8_E5M2_PT && quant_mode != ORC_QUANT_MXFP8_E5M2)
+        return ORC_ERR_INVALID_ARG;
+    return ORC_OK;
+}
+
+/* Pre-quantised rows ([NMA] dispatch Parameters x: a (data, scale) tuple for
+ * MXFP8 / MXFP4; Quantization Constraints: data [T, H] or [T, H/2], scales
+ * [T, H/32]): row_bytes a positive multiple of 16 up to 32768, scale_bytes
+ * 0..4096. */
+int oracle_check_prequant_args(int T, int row_bytes, int scale_bytes, int K, int64_t cap)
+{
+    if (T < 0 || K < 1 || K > 16 || row_bytes < 16 || row_bytes > 32768 || row_bytes % 16 != 0 ||
+        scale_bytes < 0 || scale_bytes > 4096 || cap < 0 || cap > INT32_MAX)
         return ORC_ERR_INVALID_ARG;
     return ORC_OK;
 }
@@ -248,6 +276,52 @@ void oracle_cast_to_fp8_e4m3fn_array(const float *v, int64_t n, uint8_t *out)
         out[i] = oracle_cast_to_fp8_e4m3fn((double)v[i]);
 }
 
+/* CastToFp8 for float8_e5m2 ([CANN] Constraint 8 lists FLOAT8_E5M2 as a
+ * destination of quantModes 2 and 4).  e5m2: 1 sign bit, 5 exponent bits with
+ * bias 15, 2 mantissa bits; largest finite value 1.75 * 2^15 = 57344,
+ * smallest normal 2^-14, subnormals are multiples of 2^-16.  Round to
+ * nearest, ties to even.  The format has infinities, but a quantiser that
+ * sends a finite input to infinity loses it, so magnitudes above 57344
+ * saturate to 57344, as for e4m3fn (reading).  Zero keeps its sign. */
+uint8_t oracle_cast_to_fp8_e5m2(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a > 57344.0)
+        a = 57344.0;
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: a = q * 2^-16 with q in 0..4 (q = 4 is 2^-14, the
+         * smallest normal, whose code is also 4) */
+        double q = nearbyint(a * 65536.0);
+        return (uint8_t)(sign | (uint8_t)q);
+    }
+    int e2;
+    double f = frexp(a, &e2);            /* a = f * 2^e2, f in [0.5, 1) */
+    int exponent = e2 - 1;               /* a = (1 + m/4) * 2^exponent   */
+    double m = nearbyint((2.0 * f - 1.0) * 4.0);
+    if (m == 4.0) {
+        m = 0.0;
+        exponent += 1;
+    }
+    return (uint8_t)(sign | (uint8_t)(((exponent + 15) << 2) | (int)m));
+}
+
+void oracle_cast_to_fp8_e5m2_array(const float *v, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_cast_to_fp8_e5m2((double)v[i]);
+}
+
+static uint8_t cast_to_fp8(int fmt, double v)
+{
+    return fmt == FMT_E5M2 ? oracle_cast_to_fp8_e5m2(v) : oracle_cast_to_fp8_e4m3fn(v);
+}
+
+/* Largest finite value and the exponent of the largest normal ("emax",
+ * [CANN] Formula Case 5) of each 8-bit float format. */
+static double fp8_max(int fmt) { return fmt == FMT_E5M2 ? 57344.0 : 448.0; }
+static int fp8_emax(int fmt) { return fmt == FMT_E5M2 ? 15 : 8; }
+
 /* [CANN] Formula Case 3 (quantMode 2, per-token dynamic quantisation), for
  * one token row, without smoothing scales:
  *   xFp32         = CastToFp32(X)
@@ -284,16 +358,17 @@ static void quant_int8_row(const uint16_t *x, int H, int8_t *quantOut, float *sc
 
 /* [CANN] Formula Case 5 (quantMode 4, MXFP8), for one token row, per block of
  * 32 consecutive elements (the block size of [NMA] Return Values):
- *   sharedExp     = Floor(log2(max(|x|))) - emax      emax = 8 for e4m3fn (448 = 1.75*2^8)
+ *   sharedExp     = Floor(log2(max(|x|))) - emax      emax = 8 for e4m3fn (448 = 1.75*2^8),
+ *                                                     15 for e5m2 (57344 = 1.75*2^15)
  *   dynamicScales = 2^sharedExp
  *   quantOut      = CastToFp8(X / dynamicScales)
  * Readings: the block maximum is taken of |x|; sharedExp is clamped below at
  * -127, the smallest exponent an e8m0 byte holds, and an all-zero block uses
  * -127; the stored float8_e8m0fnu scale is 2^sharedExp, i.e. the byte
  * sharedExp + 127, so that x ~= code * 2^sharedExp. */
-static void quant_mxfp8_row(const uint16_t *x, int H, uint8_t *quantOut, uint8_t *scales_out)
+static void quant_mx_row(const uint16_t *x, int H, int fmt, uint8_t *quantOut, uint8_t *scales_out)
 {
-    const int emax = 8;
+    const int emax = fp8_emax(fmt);
     for (int blk = 0; blk < H / 32; ++blk) {
         const uint16_t *xb = x + 32 * blk;
         double maxabs = 0.0;
@@ -310,10 +385,40 @@ static void quant_mxfp8_row(const uint16_t *x, int H, uint8_t *quantOut, uint8_t
         }
         double dynamicScales = ldexp(1.0, sharedExp);
         for (int j = 0; j < 32; ++j)
-            quantOut[32 * blk + j] =
-                oracle_cast_to_fp8_e4m3fn((double)bf16_to_f32(xb[j]) / dynamicScales);
+            quantOut[32 * blk + j] = cast_to_fp8(fmt, (double)bf16_to_f32(xb[j]) / dynamicScales);
         scales_out[blk] = (uint8_t)(sharedExp + 127);
     }
+}
+
+/* [CANN] Formula Case 3 with an 8-bit float destination ([CANN] Constraint 8,
+ * Ascend 950: quantMode 2 may write FLOAT8_E4M3FN or FLOAT8_E5M2; the
+ * "pertoken_fp8_e4m3" mode of [NMA] Quantization Selection Priority):
+ *   dynamicScales = dstTypeMax / Max(Abs(xFp32))     dstTypeMax = 448 or 57344
+ *   quantOut      = CastToFp8(xFp32 * dynamicScales) (the product in fp32)
+ *   scale out     = 1.0 / dynamicScales
+ * Degenerate rows as for int8: codes 0 and scale 0 when dynamicScales is not
+ * finite. */
+static void quant_fp8_pertoken_row(const uint16_t *x, int H, int fmt, uint8_t *quantOut,
+                                   float *scale_out)
+{
+    float maxabs = 0.0f;
+    for (int h = 0; h < H; ++h) {
+        float ab = fabsf(bf16_to_f32(x[h]));
+        if (ab > maxabs)
+            maxabs = ab;
+    }
+    const float dstTypeMax = (float)fp8_max(fmt);
+    float dynamicScales = dstTypeMax / maxabs;
+    if (!isfinite(dynamicScales)) {
+        for (int h = 0; h < H; ++h)
+            quantOut[h] = 0;
+    } else {
+        for (int h = 0; h < H; ++h) {
+            float prod = bf16_to_f32(x[h]) * dynamicScales; /* one fp32 multiply */
+            quantOut[h] = cast_to_fp8(fmt, (double)prod);
+        }
+    }
+    *scale_out = 1.0f / dynamicScales;
 }
 
 /* ------------------------------------------------------------------------- */
@@ -330,9 +435,9 @@ static void quant_mxfp8_row(const uint16_t *x, int H, uint8_t *quantOut, uint8_t
  * before the exchange).
  *
  * x: bf16 bits [T, H].  token_row: [T*K] from oracle_layout.  topk_weights:
- * [T*K] or NULL.  recv_x: [cap, H] of uint16 (bf16), int8 or uint8 (e4m3)
- * elements.  recv_scales: NULL (bf16), float [cap] (int8) or uint8
- * [cap * H/32] (MXFP8, row-major).  recv_weights: [cap] or NULL; receives the
+ * [T*K] or NULL.  recv_x: [cap, H] of uint16 (bf16), int8 or uint8 (fp8)
+ * elements.  recv_scales: NULL (bf16), float [cap] (per-token modes) or
+ * uint8 [cap * H/32] (MX modes, row-major).  recv_weights: [cap] or NULL; receives the
  * weight of the (t, k) entry a row holds.  Rows not named by token_row are
  * left untouched.
  */
@@ -348,39 +453,82 @@ int oracle_dispatch(const uint16_t *x, int T, int H, int K, const int32_t *token
     if (T > 0 && quant_mode != ORC_QUANT_NONE && !recv_scales)
         return ORC_ERR_INVALID_ARG;
 
+    const int per_token_scale = quant_mode == ORC_QUANT_INT8 || quant_mode == ORC_QUANT_FP8_E4M3_PT ||
+                                quant_mode == ORC_QUANT_FP8_E5M2_PT;
+    const int fmt = (quant_mode == ORC_QUANT_FP8_E5M2_PT || quant_mode == ORC_QUANT_MXFP8_E5M2)
+                        ? FMT_E5M2
+                        : FMT_E4M3FN;
 #pragma omp parallel
     {
-        int8_t *q8 = (int8_t *)malloc((size_t)H);
-        uint8_t *qf8 = (uint8_t *)malloc((size_t)H);
+        uint8_t *q = (uint8_t *)malloc((size_t)H);
         uint8_t *sc8 = (uint8_t *)malloc((size_t)H / 32);
 #pragma omp for schedule(static)
         for (int t = 0; t < T; ++t) {
             const uint16_t *xt = x + (int64_t)t * H;
-            float s_int8 = 0.0f;
+            float s_row = 0.0f;
             if (quant_mode == ORC_QUANT_INT8)
-                quant_int8_row(xt, H, q8, &s_int8);
-            else if (quant_mode == ORC_QUANT_MXFP8)
-                quant_mxfp8_row(xt, H, qf8, sc8);
+                quant_int8_row(xt, H, (int8_t *)q, &s_row);
+            else if (quant_mode == ORC_QUANT_FP8_E4M3_PT || quant_mode == ORC_QUANT_FP8_E5M2_PT)
+                quant_fp8_pertoken_row(xt, H, fmt, q, &s_row);
+            else if (quant_mode == ORC_QUANT_MXFP8 || quant_mode == ORC_QUANT_MXFP8_E5M2)
+                quant_mx_row(xt, H, fmt, q, sc8);
             for (int k = 0; k < K; ++k) {
                 int32_t row = token_row[(int64_t)t * K + k];
                 if (row < 0 || row >= cap)
                     continue;
                 if (quant_mode == ORC_QUANT_NONE) {
                     memcpy((uint16_t *)recv_x + (int64_t)row * H, xt, sizeof(uint16_t) * (size_t)H);
-                } else if (quant_mode == ORC_QUANT_INT8) {
-                    memcpy((int8_t *)recv_x + (int64_t)row * H, q8, (size_t)H);
-                    ((float *)recv_scales)[row] = s_int8;
                 } else {
-                    memcpy((uint8_t *)recv_x + (int64_t)row * H, qf8, (size_t)H);
-                    memcpy((uint8_t *)recv_scales + (int64_t)row * (H / 32), sc8, (size_t)H / 32);
+                    memcpy((uint8_t *)recv_x + (int64_t)row * H, q, (size_t)H);
+                    if (per_token_scale)
+                        ((float *)recv_scales)[row] = s_row;
+                    else
+                        memcpy((uint8_t *)recv_scales + (int64_t)row * (H / 32), sc8, (size_t)H / 32);
                 }
                 if (recv_weights)
                     recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;
             }
         }
-        free(q8);
-        free(qf8);
+        free(q);
         free(sc8);
+    }
+    return ORC_OK;
+}
+
+/*
+ * Dispatch of pre-quantised tokens ([NMA] dispatch Parameters x: for MXFP8 /
+ * MXFP4 per-block quantisation x is a tuple (data, scale); Return Values: the
+ * received rows keep that format).  Each token's data row (row_bytes) and
+ * scale row (scale_bytes) are copied unchanged to every row the layout gives
+ * it.  data: [T, row_bytes]; scales: [T, scale_bytes] or NULL when
+ * scale_bytes is 0; recv_data: [cap, row_bytes]; recv_scales:
+ * [cap, scale_bytes].
+ */
+int oracle_dispatch_prequantized(const uint8_t *data, int T, int row_bytes, const uint8_t *scales,
+                                 int scale_bytes, int K, const int32_t *token_row,
+                                 const float *topk_weights, int64_t cap, uint8_t *recv_data,
+                                 uint8_t *recv_scales, float *recv_weights)
+{
+    int rc = oracle_check_prequant_args(T, row_bytes, scale_bytes, K, cap);
+    if (rc != ORC_OK)
+        return rc;
+    if (T > 0 && (!data || !token_row || !recv_data))
+        return ORC_ERR_INVALID_ARG;
+    if (T > 0 && scale_bytes > 0 && (!scales || !recv_scales))
+        return ORC_ERR_INVALID_ARG;
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int32_t row = token_row[(int64_t)t * K + k];
+            if (row < 0 || row >= cap)
+                continue;
+            memcpy(recv_data + (int64_t)row * row_bytes, data + (int64_t)t * row_bytes,
+                   (size_t)row_bytes);
+            if (scale_bytes > 0)
+                memcpy(recv_scales + (int64_t)row * scale_bytes, scales + (int64_t)t * scale_bytes,
+                       (size_t)scale_bytes);
+            if (recv_weights)
+                recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;
+        }
     }
     return ORC_OK;
 }
@@ -395,7 +543,23 @@ void oracle_quant_int8_rows(const uint16_t *x, int T, int H, int8_t *q, float *s
 void oracle_quant_mxfp8_rows(const uint16_t *x, int T, int H, uint8_t *q, uint8_t *scales)
 {
     for (int t = 0; t < T; ++t)
-        quant_mxfp8_row(x + (int64_t)t * H, H, q + (int64_t)t * H, scales + (int64_t)t * (H / 32));
+        quant_mx_row(x + (int64_t)t * H, H, FMT_E4M3FN, q + (int64_t)t * H,
+                     scales + (int64_t)t * (H / 32));
+}
+
+void oracle_quant_mx_e5m2_rows(const uint16_t *x, int T, int H, uint8_t *q, uint8_t *scales)
+{
+    for (int t = 0; t < T; ++t)
+        quant_mx_row(x + (int64_t)t * H, H, FMT_E5M2, q + (int64_t)t * H,
+                     scales + (int64_t)t * (H / 32));
+}
+
+/* fmt: 1 = e4m3fn, 2 = e5m2 */
+void oracle_quant_fp8_pertoken_rows(const uint16_t *x, int T, int H, int fmt, uint8_t *q,
+                                    float *scales)
+{
+    for (int t = 0; t < T; ++t)
+        quant_fp8_pertoken_row(x + (int64_t)t * H, H, fmt, q + (int64_t)t * H, scales + t);
 }
 
 /* ------------------------------------------------------------------------- */
