@@ -58,12 +58,20 @@ def parse():
     return p.parse_args()
 
 
-def stage_bytes(T, H, K, R, E, V, cap, quant):
-    """Algorithmic bytes of each stage (see module docstring)."""
-    s_q = 2 if quant == 0 else 1
-    sigma = 0 if quant == 0 else (4 if quant == 2 else H // 32)
+PER_TOKEN_MODES = (0x02, 0x12, 0x22)
+
+
+def stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows=None):
+    """Algorithmic bytes of each stage (see module docstring).  prequant_rows =
+    (data bytes, scale bytes) per token for the pre-quantised pass-through."""
     layout = 8 * T * K + 4 * T * R + 4 * R + 8 * E + 4 * (E + 1) + 4 * T * K + 4 * cap + 4
-    dispatch = 2 * T * H + 4 * T * K + V * (H * s_q + sigma)
+    if prequant_rows is not None:
+        rb, sb = prequant_rows
+        dispatch = T * (rb + sb) + 4 * T * K + V * (rb + sb)
+    else:
+        s_q = 2 if quant == 0 else 1
+        sigma = 0 if quant == 0 else (4 if quant in PER_TOKEN_MODES else H // 32)
+        dispatch = 2 * T * H + 4 * T * K + V * (H * s_q + sigma)
     combine = 2 * V * H + 8 * T * K + 2 * T * H
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
 
@@ -149,7 +157,7 @@ class StageEvents:
         return f.value * 1e3
 
 
-def cpu_baseline(inp, w, quant, budget_s, bytes_fn):
+def cpu_baseline(inp, w, quant, budget_s, bytes_fn, prequant=None):
     """The oracle, as it is, on the same workload, repeated until the time
     budget is used (at least once)."""
     import numpy as np
@@ -159,11 +167,12 @@ def cpu_baseline(inp, w, quant, budget_s, bytes_fn):
     t0 = time.perf_counter()
     while True:
         ol = oracle.layout(inp.topk_idx, E, R, a)
-        rx, rs, _ = oracle.dispatch(inp.x_bits, ol.token_row, ol.recv_capacity, None, quant)
-        if quant == 0:
-            y = rx
+        if prequant is not None:
+            oracle.dispatch_prequantized(prequant[0], prequant[1], ol.token_row, ol.recv_capacity)
+            y = prequant[2]
         else:
-            y = np.zeros((ol.recv_capacity, w.hidden), np.uint16)   # expert output stand-in
+            rx, rs, _ = oracle.dispatch(inp.x_bits, ol.token_row, ol.recv_capacity, None, quant)
+            y = rx if quant == 0 else np.zeros((ol.recv_capacity, w.hidden), np.uint16)
         oracle.combine(y, ol.token_row, inp.topk_weights)
         reps += 1
         V = int((inp.topk_idx >= 0).sum())
@@ -197,27 +206,51 @@ def main():
     T, H, K, E, R, a, quant = (w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
                                w.expert_alignment, w.quant_mode)
     dev = torch.device("cuda", 0)
-    inp = W.generate(w)
+    prequant_rows = W.prequant_row_bytes(w) if w.prequant else None
+    if w.prequant:
+        data_h, scales_h, idx_h, wt_h = W.generate_prequant(w)
+        inp = W.Inputs(w, None, idx_h, wt_h)
+    else:
+        inp = W.generate(w)
     V = int((inp.topk_idx >= 0).sum())
 
     idx = torch.from_numpy(inp.topk_idx).to(dev)
-    x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     wt = torch.from_numpy(inp.topk_weights).to(dev)
     lay = moe.allocate_layout(T, K, E, R, a, device=dev)
     cap = lay.recv_capacity
-    rx, rs, _ = moe.allocate_recv(lay, H, quant)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-
-    # identity expert output (made once, outside the timed region)
     moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)
-    moe.moe_dispatch(x, lay, None, quant, recv_x=rx, recv_scales=rs)
-    if quant == 0:
-        y = rx
-    elif quant == 2:
-        y = (rx.float() * rs[:, None]).to(torch.bfloat16)
+    cpu_y = None
+    if w.prequant:
+        data = torch.from_numpy(data_h).to(dev)
+        scales = torch.from_numpy(scales_h).to(dev)
+        rd = torch.empty((cap, data.shape[1]), dtype=torch.uint8, device=dev)
+        rsc = torch.empty((cap, scales.shape[1]), dtype=torch.uint8, device=dev)
+        # expert output stand-in: seeded bf16 rows (combine does not depend on values)
+        y_bits = W.random_bf16_rows(cap, H, 5)
+        y = torch.from_numpy(y_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        cpu_y = (data_h, scales_h, y_bits)
+
+        def run_dispatch():
+            moe.moe_dispatch_prequantized(data, scales, lay, None, rd, rsc)
     else:
-        y = (rx.float().view(cap, H // 32, 32) * torch.exp2(rs.float() - 127.0)[:, :, None]).view(cap, H)
-        y = torch.nan_to_num(y).to(torch.bfloat16)
+        x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        rx, rs, _ = moe.allocate_recv(lay, H, quant)
+
+        def run_dispatch():
+            moe.moe_dispatch(x, lay, None, quant, recv_x=rx, recv_scales=rs)
+
+        # identity expert output (made once, outside the timed region)
+        run_dispatch()
+        if quant == 0:
+            y = rx
+        else:
+            codes = rx.float()
+            if quant in PER_TOKEN_MODES:
+                y = codes * rs[:, None]
+            else:
+                y = (codes.view(cap, H // 32, 32) * torch.exp2(rs.float() - 127.0)[:, :, None]).view(cap, H)
+            y = torch.nan_to_num(y, nan=0.0, posinf=0.0, neginf=0.0).to(torch.bfloat16)
     torch.cuda.synchronize()
 
     timer = StageEvents(torch)
@@ -228,7 +261,7 @@ def main():
         moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)
         if ev is not None:
             timer.record(ev[1])
-        moe.moe_dispatch(x, lay, None, quant, recv_x=rx, recv_scales=rs)
+        run_dispatch()
         if ev is not None:
             timer.record(ev[2])
         moe.moe_combine(y, lay, wt, out=out)
@@ -258,7 +291,7 @@ def main():
     avg_us = {k: float(np.mean(v)) for k, v in st.items()}
     med_us = {k: float(np.median(v)) for k, v in st.items()}
 
-    sb = stage_bytes(T, H, K, R, E, V, cap, quant)
+    sb = stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows)
     step_bytes = sum(sb.values())
     ms_per_step = elapsed / args.steps * 1e3
     gbs = step_bytes * args.steps / elapsed / 1e9
@@ -271,7 +304,9 @@ def main():
         # cheap sanity check after timing: every dispatched row is its token
         src = lay.recv_src.long()
         u = src >= 0
-        if quant == 0:
+        if w.prequant:
+            assert torch.equal(rd[u], data[src[u] // K])
+        elif quant == 0:
             assert torch.equal(rx.view(torch.int16)[u], x.view(torch.int16)[src[u] // K])
         assert int(lay.error_flag.item()) == 0
 
@@ -286,9 +321,13 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(inp, w, quant, args.cpu_seconds,
-                           lambda v, c: stage_bytes(T, H, K, R, E, v, c, quant))
+                           lambda v, c: stage_bytes(T, H, K, R, E, v, c, quant, prequant_rows),
+                           prequant=cpu_y)
 
-    qname = {0: "bf16", 2: "int8", 4: "mxfp8_e4m3"}[quant]
+    qname = {0: "bf16", 2: "int8", 4: "mxfp8_e4m3", 0x12: "fp8_e4m3_per_token",
+             0x22: "fp8_e5m2_per_token", 0x24: "mxfp8_e5m2"}[quant]
+    if w.prequant:
+        qname = f"{w.prequant}_prequantized"
     rec = {
         "metric": "dispatch+combine effective HBM GB/s and tokens/s (% of peak) at 4096x7168 top-8",
         "value": round(gbs, 2),
@@ -300,7 +339,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if quant == 0 else f"bf16->{qname}",
+        "dtype": ("bf16" if quant == 0 else f"bf16->{qname}") if not w.prequant else qname,
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.describe(), "num_tokens": T, "hidden": H,
                    "num_experts": E, "num_virtual_ranks": R, "top_k": K, "expert_alignment": a,

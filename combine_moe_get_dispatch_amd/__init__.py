@@ -34,14 +34,21 @@ MOE_ERR_HIP = -4
 QUANT_NONE = 0
 QUANT_INT8_PER_TOKEN = 2
 QUANT_MXFP8_E4M3 = 4
+QUANT_FP8_E4M3_PER_TOKEN = 0x12
+QUANT_FP8_E5M2_PER_TOKEN = 0x22
+QUANT_MXFP8_E5M2 = 0x24
+PER_TOKEN_SCALE_MODES = (QUANT_INT8_PER_TOKEN, QUANT_FP8_E4M3_PER_TOKEN, QUANT_FP8_E5M2_PER_TOKEN)
+MX_MODES = (QUANT_MXFP8_E4M3, QUANT_MXFP8_E5M2)
 
 FLAG_BAD_EXPERT_ID = 1
 
 __all__ = [
-    "moe_get_dispatch_layout", "moe_dispatch", "moe_combine", "moe_recv_capacity_bound",
+    "moe_get_dispatch_layout", "moe_dispatch", "moe_dispatch_prequantized", "moe_combine",
+    "moe_recv_capacity_bound",
     "moe_layout_workspace_bytes", "DispatchLayout", "allocate_layout", "allocate_recv",
     "num_recv_tokens_per_expert_list", "MoeError", "lib",
-    "QUANT_NONE", "QUANT_INT8_PER_TOKEN", "QUANT_MXFP8_E4M3",
+    "QUANT_NONE", "QUANT_INT8_PER_TOKEN", "QUANT_MXFP8_E4M3", "QUANT_FP8_E4M3_PER_TOKEN",
+    "QUANT_FP8_E5M2_PER_TOKEN", "QUANT_MXFP8_E5M2",
 ]
 
 
@@ -73,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.moe_get_dispatch_layout.restype = i32
         L.moe_dispatch.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
         L.moe_dispatch.restype = i32
+        L.moe_dispatch_prequantized.argtypes = [P, i32, i32, P, i32, i32, P, P, i64, P, P, P, P]
+        L.moe_dispatch_prequantized.restype = i32
         L.moe_combine.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
         L.moe_combine.restype = i32
         L.moe_status_string.argtypes = [i32]
@@ -184,26 +193,29 @@ def num_recv_tokens_per_expert_list(layout: DispatchLayout) -> list:
     return layout.num_recv_tokens_per_expert.cpu().tolist()
 
 
+_RECV_DTYPE = {QUANT_NONE: torch.bfloat16, QUANT_INT8_PER_TOKEN: torch.int8,
+               QUANT_MXFP8_E4M3: torch.float8_e4m3fn, QUANT_FP8_E4M3_PER_TOKEN: torch.float8_e4m3fn,
+               QUANT_FP8_E5M2_PER_TOKEN: torch.float8_e5m2, QUANT_MXFP8_E5M2: torch.float8_e5m2}
+
+
 def allocate_recv(layout: DispatchLayout, hidden: int, quant_mode: int = QUANT_NONE,
                   with_weights: bool = False):
+    """Receive buffers for ``quant_mode``: rows [cap, H] of the mode's element
+    type, scales fp32 [cap] (per-token modes) or uint8 e8m0 [cap, H/32] (MX
+    modes) or None (bf16), optional fp32 row weights [cap]."""
     dev = layout.token_row.device
     cap = layout.recv_capacity
-    if quant_mode == QUANT_NONE:
-        rx, rs = torch.empty((cap, hidden), dtype=torch.bfloat16, device=dev), None
-    elif quant_mode == QUANT_INT8_PER_TOKEN:
-        rx = torch.empty((cap, hidden), dtype=torch.int8, device=dev)
+    if quant_mode not in _RECV_DTYPE:
+        raise ValueError(f"unsupported quant_mode {quant_mode}")
+    rx = torch.empty((cap, hidden), dtype=_RECV_DTYPE[quant_mode], device=dev)
+    if quant_mode in PER_TOKEN_SCALE_MODES:
         rs = torch.empty(cap, dtype=torch.float32, device=dev)
-    elif quant_mode == QUANT_MXFP8_E4M3:
-        rx = torch.empty((cap, hidden), dtype=torch.float8_e4m3fn, device=dev)
+    elif quant_mode in MX_MODES:
         rs = torch.empty((cap, hidden // 32), dtype=torch.uint8, device=dev)
     else:
-        raise ValueError(f"unsupported quant_mode {quant_mode}")
+        rs = None
     rw = torch.empty(cap, dtype=torch.float32, device=dev) if with_weights else None
     return rx, rs, rw
-
-
-_RECV_DTYPE = {QUANT_NONE: torch.bfloat16, QUANT_INT8_PER_TOKEN: torch.int8,
-               QUANT_MXFP8_E4M3: torch.float8_e4m3fn}
 
 
 def moe_dispatch(x: torch.Tensor, layout: DispatchLayout, topk_weights: Optional[torch.Tensor] = None,
@@ -227,9 +239,9 @@ def moe_dispatch(x: torch.Tensor, layout: DispatchLayout, topk_weights: Optional
         recv_scales = rs if recv_scales is None else recv_scales
         recv_weights = rw if recv_weights is None else recv_weights
     _check(recv_x, "recv_x", _RECV_DTYPE[quant_mode], (cap, H), dev)
-    if quant_mode == QUANT_INT8_PER_TOKEN:
+    if quant_mode in PER_TOKEN_SCALE_MODES:
         _check(recv_scales, "recv_scales", torch.float32, (cap,), dev)
-    elif quant_mode == QUANT_MXFP8_E4M3:
+    elif quant_mode in MX_MODES:
         _check(recv_scales, "recv_scales", torch.uint8, (cap, H // 32), dev)
     if recv_weights is not None:
         _check(recv_weights, "recv_weights", torch.float32, (cap,), dev)
@@ -239,6 +251,53 @@ def moe_dispatch(x: torch.Tensor, layout: DispatchLayout, topk_weights: Optional
     if rc != MOE_OK:
         raise MoeError("moe_dispatch", rc)
     return recv_x, recv_scales, recv_weights
+
+
+def _bytes2d(t: torch.Tensor, name: str, rows: int, dev) -> torch.Tensor:
+    if t.device != dev or t.dim() != 2 or t.shape[0] != rows or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [{rows}, n] tensor on {dev}")
+    return t.view(torch.uint8)
+
+
+def moe_dispatch_prequantized(data: torch.Tensor, scales: Optional[torch.Tensor],
+                              layout: DispatchLayout, topk_weights: Optional[torch.Tensor] = None,
+                              recv_data: Optional[torch.Tensor] = None,
+                              recv_scales: Optional[torch.Tensor] = None,
+                              recv_weights: Optional[torch.Tensor] = None,
+                              with_weights: bool = False):
+    """Copy pre-quantised tokens -- the (data, scale) tuple input of MXFP8 /
+    MXFP4 dispatch: data [T, H] float8 or [T, H/2] packed float4, scales
+    [T, H/32] e8m0 bytes -- unchanged into their experts' rows.  Any element
+    dtype is accepted; rows are moved as bytes.  Returns (recv_data,
+    recv_scales, recv_weights) with the input dtypes."""
+    T, K, cap = layout.num_tokens, layout.num_topk, layout.recv_capacity
+    dev = data.device
+    if dev.type != "cuda":
+        raise ValueError("data must be on a HIP device")
+    d8 = _bytes2d(data, "data", T, dev)
+    row_bytes = d8.shape[1]
+    s8 = None if scales is None else _bytes2d(scales, "scales", T, dev)
+    scale_bytes = 0 if s8 is None else s8.shape[1]
+    if topk_weights is not None:
+        _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    if recv_data is None:
+        recv_data = torch.empty((cap,) + tuple(data.shape[1:]), dtype=data.dtype, device=dev)
+    if recv_scales is None and scales is not None:
+        recv_scales = torch.empty((cap,) + tuple(scales.shape[1:]), dtype=scales.dtype, device=dev)
+    if recv_weights is None and with_weights:
+        recv_weights = torch.empty(cap, dtype=torch.float32, device=dev)
+    rd8 = _bytes2d(recv_data, "recv_data", cap, dev)
+    rs8 = None if recv_scales is None else _bytes2d(recv_scales, "recv_scales", cap, dev)
+    if rd8.shape[1] != row_bytes or (rs8 is not None and rs8.shape[1] != scale_bytes):
+        raise ValueError("receive buffers do not match the row sizes of the input")
+    if recv_weights is not None:
+        _check(recv_weights, "recv_weights", torch.float32, (cap,), dev)
+    rc = lib().moe_dispatch_prequantized(_ptr(d8), T, row_bytes, _ptr(s8), scale_bytes, K,
+                                         _ptr(layout.token_row), _ptr(topk_weights), cap,
+                                         _ptr(rd8), _ptr(rs8), _ptr(recv_weights), _stream(dev))
+    if rc != MOE_OK:
+        raise MoeError("moe_dispatch_prequantized", rc)
+    return recv_data, recv_scales, recv_weights
 
 
 def moe_combine(expert_out: torch.Tensor, layout: DispatchLayout,

@@ -2,30 +2,113 @@
 // optionally quantised once per token.
 //
 // What is computed (Normal Mode API page, dispatch and Return Values recv_x;
-// CANN aclnnMoeDistributeDispatchV2 page, Formula Cases 1, 3 and 5):
-//   bf16 : recv[row(t,k)] = x[t]
-//   int8 : dynamicScales = 127 / max|x[t]| (fp32), q = rint(x * dynamicScales),
-//          scale = 1 / dynamicScales; codes 0 and scale 0 when dynamicScales
-//          is not finite
-//   MXFP8: per 32 elements sharedExp = max(floor(log2 max|x|) - 8, -127),
-//          q = e4m3fn(x / 2^sharedExp) (ties to even, saturated to 448),
-//          e8m0 byte = sharedExp + 127
+// CANN aclnnMoeDistributeDispatchV2 page, Formula Cases 1, 3 and 5 and
+// Constraint 8 for the destination types):
+//   bf16      : recv[row(t,k)] = x[t]
+//   per-token : dynamicScales = dstTypeMax / max|x[t]| (fp32),
+//               q = cast(x * dynamicScales) with the product in fp32,
+//               scale = 1 / dynamicScales; codes 0 and scale 0 when
+//               dynamicScales is not finite.  dstTypeMax / cast:
+//               int8 127 / round half to even; e4m3fn 448 and e5m2 57344 /
+//               round half to even, saturated to dstTypeMax
+//   MX        : per 32 elements sharedExp = max(floor(log2 max|x|) - emax, -127)
+//               (emax 8 for e4m3fn, 15 for e5m2), q = cast(x / 2^sharedExp),
+//               e8m0 byte = sharedExp + 127
+//   pre-quantised rows (the Normal Mode API page's (data, scale) tuple input):
+//               data row and scale row copied unchanged
 //
 // Design (gfx950): one workgroup per token, one 16-byte vector per lane
 // (896 lanes for H = 7168; two vectors per lane above H = 8192).  The token
 // row is read from HBM exactly once and held in VGPRs; it is quantised there
-// once; then each of the
-// K copies is written with 16-byte (bf16) or 8-byte (int8 / e4m3) stores, one
-// contiguous row per wave instruction group.  The stores are nontemporal:
-// every expanded row is written once and only read again by the next stage,
-// so it should not evict the routing tables from L2.  Row offsets are 64-bit
-// (the largest receive buffers exceed 4 GiB).
+// once; then each of the K copies is written with 16-byte (bf16) or 8-byte
+// (1-byte codes) stores, one contiguous row per wave instruction group.  The
+// stores are nontemporal: every expanded row is written once and only read
+// again by the next stage, so it should not evict the routing tables from
+// L2.  Row offsets are 64-bit (the largest receive buffers exceed 4 GiB).
 #include "device_common.h"
 #include "launch.h"
 
 #include "../../include/moe_dispatch_combine.h"
 
 namespace moe {
+
+// --------------------------------------------------------------------------- element codecs
+
+enum class Dst { Int8, E4M3, E5M2 };
+
+// e4m3fn code of an fp32 value: magnitude saturated to 448; below 2^-6 the
+// code is the number of 2^-9 steps, rounded half to even (a * 2^9 is exact);
+// otherwise exponent field (e + 7) and the top 3 mantissa bits, rounded half
+// to even on the 20 bits below them (a carry out of the mantissa moves into
+// the exponent field through the plain integer add).  `sign` (0 or 0x80)
+// comes from the source element so that -0 and negative values that round
+// to zero keep their sign.
+__device__ __forceinline__ uint32_t e4m3fn_code(float v, uint32_t sign)
+{
+    const float a = fminf(fabsf(v), 448.0f);
+    uint32_t code;
+    if (a < 0x1p-6f) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        const uint32_t b = __float_as_uint(a);
+        const uint32_t base = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+        const uint32_t rem = b & 0xFFFFFu;
+        code = base + ((rem > 0x80000u) || (rem == 0x80000u && (base & 1u)) ? 1u : 0u);
+    }
+    return code | sign;
+}
+
+// e5m2 code of an fp32 value: magnitude saturated to 57344; below 2^-14 the
+// number of 2^-16 steps; otherwise exponent field (e + 15) and the top 2
+// mantissa bits, rounded half to even on the 21 bits below them.
+__device__ __forceinline__ uint32_t e5m2_code(float v, uint32_t sign)
+{
+    const float a = fminf(fabsf(v), 57344.0f);
+    uint32_t code;
+    if (a < 0x1p-14f) {
+        code = (uint32_t)__builtin_rintf(a * 65536.0f);
+    } else {
+        const uint32_t b = __float_as_uint(a);
+        const uint32_t base = (((b >> 23) - 112u) << 2) | ((b >> 21) & 3u);
+        const uint32_t rem = b & 0x1FFFFFu;
+        code = base + ((rem > 0x100000u) || (rem == 0x100000u && (base & 1u)) ? 1u : 0u);
+    }
+    return code | sign;
+}
+
+template <Dst D> struct DstTraits;
+template <> struct DstTraits<Dst::Int8> {
+    static constexpr float kMax = 127.0f;
+    // the product is within +-127 (plus one rounding): the integer fits int8
+    __device__ static uint32_t code(float p, uint32_t) { return (uint32_t)((int)__builtin_rintf(p)) & 0xFFu; }
+};
+template <> struct DstTraits<Dst::E4M3> {
+    static constexpr float kMax = 448.0f;
+    static constexpr int kEmax = 8;
+    __device__ static uint32_t code(float p, uint32_t sign) { return e4m3fn_code(p, sign); }
+};
+template <> struct DstTraits<Dst::E5M2> {
+    static constexpr float kMax = 57344.0f;
+    static constexpr int kEmax = 15;
+    __device__ static uint32_t code(float p, uint32_t sign) { return e5m2_code(p, sign); }
+};
+
+// sign bits (0 or 0x80) of the two bf16 elements of a 32-bit word
+__device__ __forceinline__ uint32_t sign_lo(uint32_t w) { return (w >> 8) & 0x80u; }
+__device__ __forceinline__ uint32_t sign_hi(uint32_t w) { return (w >> 24) & 0x80u; }
+
+__device__ __forceinline__ void write_row_weight(const int32_t *__restrict__ token_row,
+                                                 const float *__restrict__ topk_weights,
+                                                 float *__restrict__ recv_weights, int t, int K,
+                                                 int64_t cap)
+{
+    const int tid = threadIdx.x;
+    if (recv_weights && tid < K) {
+        const int row = token_row[(int64_t)t * K + tid];
+        if (row >= 0 && row < cap)
+            recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + tid] : 1.0f;
+    }
+}
 
 // --------------------------------------------------------------------------- bf16
 
@@ -56,24 +139,13 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_bf16_kernel(
                 __builtin_nontemporal_store(v[j], dst + i);
         }
     }
-    if (recv_weights && tid < K) {
-        const int row = token_row[(int64_t)t * K + tid];
-        if (row >= 0 && row < cap)
-            recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + tid] : 1.0f;
-    }
+    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
 }
 
-// --------------------------------------------------------------------------- int8
+// --------------------------------------------------------------------------- per-token dynamic
 
-__device__ __forceinline__ uint32_t q8(float f, float ds)
-{
-    // one fp32 multiply, then round half to even; |f * ds| <= 127 (plus one
-    // rounding), so the integer always fits int8
-    return (uint32_t)((int)__builtin_rintf(f * ds)) & 0xFFu;
-}
-
-template <int VPT>
-__global__ __launch_bounds__(kRowMaxThreads) void dispatch_int8_kernel(
+template <int VPT, Dst D>
+__global__ __launch_bounds__(kRowMaxThreads) void dispatch_pertoken_kernel(
     const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
     const float *__restrict__ topk_weights, int64_t cap, u32x2 *__restrict__ recv,
     float *__restrict__ recv_scales, float *__restrict__ recv_weights)
@@ -104,7 +176,7 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_int8_kernel(
     for (int w = 1; w < nthr / kWave; ++w)
         m = fmaxf(m, s_wmax[w]);
 
-    const float ds = 127.0f / m; // IEEE division (built with correctly rounded fp32 divide)
+    const float ds = DstTraits<D>::kMax / m; // IEEE division (built with correctly rounded fp32 divide)
     const bool degenerate = !(ds <= 3.402823466e38f);
     const float scale = 1.0f / ds;
 
@@ -115,8 +187,8 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_int8_kernel(
         if (!degenerate) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint32_t lo = q8(bf16_lo(v[j][c]), ds);
-                const uint32_t hi = q8(bf16_hi(v[j][c]), ds);
+                const uint32_t lo = DstTraits<D>::code(bf16_lo(v[j][c]) * ds, sign_lo(v[j][c]));
+                const uint32_t hi = DstTraits<D>::code(bf16_hi(v[j][c]) * ds, sign_hi(v[j][c]));
                 w[c >> 1] |= (lo | (hi << 8)) << (16 * (c & 1));
             }
         }
@@ -137,39 +209,13 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_int8_kernel(
         if (tid == 0)
             recv_scales[row] = scale;
     }
-    if (recv_weights && tid < K) {
-        const int row = token_row[(int64_t)t * K + tid];
-        if (row >= 0 && row < cap)
-            recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + tid] : 1.0f;
-    }
+    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
 }
 
-// --------------------------------------------------------------------------- MXFP8 e4m3
+// --------------------------------------------------------------------------- MX (32-element blocks)
 
-// e4m3fn code of v (an exact multiple of a power of two, from a bf16 times
-// 2^-sharedExp).  Magnitude saturated to 448; below 2^-6 the code is the
-// number of 2^-9 steps, rounded half to even; otherwise exponent field
-// (e + 7) and the top 3 mantissa bits, rounded half to even on the 20 bits
-// below them (a carry out of the mantissa moves into the exponent field by
-// the plain integer add).  `sign` is taken from the source element so that
-// -0 and negative values that round to zero keep their sign.
-__device__ __forceinline__ uint32_t e4m3fn_code(float v, uint32_t sign)
-{
-    const float a = fminf(fabsf(v), 448.0f);
-    uint32_t code;
-    if (a < 0x1p-6f) {
-        code = (uint32_t)__builtin_rintf(a * 512.0f);
-    } else {
-        const uint32_t b = __float_as_uint(a);
-        const uint32_t base = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
-        const uint32_t rem = b & 0xFFFFFu;
-        code = base + ((rem > 0x80000u) || (rem == 0x80000u && (base & 1u)) ? 1u : 0u);
-    }
-    return code | sign;
-}
-
-template <int VPT>
-__global__ __launch_bounds__(kRowMaxThreads) void dispatch_mxfp8_kernel(
+template <int VPT, Dst D>
+__global__ __launch_bounds__(kRowMaxThreads) void dispatch_mx_kernel(
     const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
     const float *__restrict__ topk_weights, int64_t cap, u32x2 *__restrict__ recv,
     uint8_t *__restrict__ recv_scales, float *__restrict__ recv_weights)
@@ -198,15 +244,19 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_mxfp8_kernel(
         }
         m = fmaxf(m, __shfl_xor(m, 1, kWave));
         m = fmaxf(m, __shfl_xor(m, 2, kWave));
+        // floor(log2 m) is the fp32 exponent field - 127 (any m below 2^-119,
+        // subnormals and 0 included, ends up at the -127 clamp)
         const int ebits = (int)((__float_as_uint(m) >> 23) & 0xFFu);
-        const int se = max(ebits - 127 - 8, -127); // floor(log2 m) - emax, emax(e4m3fn) = 8
+        const int se = max(ebits - 127 - DstTraits<D>::kEmax, -127);
         const float inv = __uint_as_float((uint32_t)(127 - se) << 23); // 2^-se, normal for se in [-127, 119]
         sbyte[j] = (uint32_t)(se + 127);
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint32_t lo = e4m3fn_code(bf16_lo(xv[c]) * inv, (xv[c] >> 8) & 0x80u);
-            const uint32_t hi = e4m3fn_code(bf16_hi(xv[c]) * inv, (xv[c] >> 24) & 0x80u);
+            // x * 2^-se is exact: a bf16 scaled by a power of two (results
+            // that would be fp32-subnormal are far below the fp8 rounding step)
+            const uint32_t lo = DstTraits<D>::code(bf16_lo(xv[c]) * inv, sign_lo(xv[c]));
+            const uint32_t hi = DstTraits<D>::code(bf16_hi(xv[c]) * inv, sign_hi(xv[c]));
             w[c >> 1] |= (lo | (hi << 8)) << (16 * (c & 1));
         }
         q[j] = u32x2{w[0], w[1]};
@@ -228,14 +278,80 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_mxfp8_kernel(
             }
         }
     }
-    if (recv_weights && tid < K) {
-        const int row = token_row[(int64_t)t * K + tid];
-        if (row >= 0 && row < cap)
-            recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + tid] : 1.0f;
+    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
+}
+
+// --------------------------------------------------------------------------- pre-quantised rows
+
+template <int VPT>
+__global__ __launch_bounds__(kRowMaxThreads) void dispatch_rows_kernel(
+    const u32x4 *__restrict__ data, int nvec, const uint8_t *__restrict__ scales, int scale_bytes,
+    int K, const int32_t *__restrict__ token_row, const float *__restrict__ topk_weights,
+    int64_t cap, u32x4 *__restrict__ recv_data, uint8_t *__restrict__ recv_scales,
+    float *__restrict__ recv_weights)
+{
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const u32x4 *dt = data + (int64_t)t * nvec;
+    u32x4 v[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+        v[j] = dt[min(tid + j * nthr, nvec - 1)]; // clamped: always in bounds
+    for (int k = 0; k < K; ++k) {
+        const int row = token_row[(int64_t)t * K + k];
+        if (row < 0 || row >= cap)
+            continue;
+        u32x4 *dst = recv_data + (int64_t)row * nvec;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int i = tid + j * nthr;
+            if (i < nvec)
+                __builtin_nontemporal_store(v[j], dst + i);
+        }
+        // the scale row (H/32 bytes for MX data) is small: re-read from cache per copy
+        for (int i = tid; i < scale_bytes; i += nthr)
+            recv_scales[(int64_t)row * scale_bytes + i] = scales[(int64_t)t * scale_bytes + i];
     }
+    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
 }
 
 // --------------------------------------------------------------------------- launch
+
+template <int V>
+static hipError_t launch_dispatch_v(dim3 grid, dim3 block, hipStream_t stream, const u32x4 *xv,
+                                    int nvec, int K, const int32_t *token_row,
+                                    const float *topk_weights, int64_t cap, int quant_mode,
+                                    void *recv_x, void *recv_scales, float *recv_weights)
+{
+    switch (quant_mode) {
+    case MOE_QUANT_NONE:
+        return launch_kernel(dispatch_bf16_kernel<V>, grid, block, 0, stream, xv, nvec, K,
+                             token_row, topk_weights, cap, (u32x4 *)recv_x, recv_weights);
+    case MOE_QUANT_INT8_PER_TOKEN:
+        return launch_kernel(dispatch_pertoken_kernel<V, Dst::Int8>, grid, block, 0, stream, xv,
+                             nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x,
+                             (float *)recv_scales, recv_weights);
+    case MOE_QUANT_FP8_E4M3_PER_TOKEN:
+        return launch_kernel(dispatch_pertoken_kernel<V, Dst::E4M3>, grid, block, 0, stream, xv,
+                             nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x,
+                             (float *)recv_scales, recv_weights);
+    case MOE_QUANT_FP8_E5M2_PER_TOKEN:
+        return launch_kernel(dispatch_pertoken_kernel<V, Dst::E5M2>, grid, block, 0, stream, xv,
+                             nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x,
+                             (float *)recv_scales, recv_weights);
+    case MOE_QUANT_MXFP8_E4M3:
+        return launch_kernel(dispatch_mx_kernel<V, Dst::E4M3>, grid, block, 0, stream, xv, nvec,
+                             K, token_row, topk_weights, cap, (u32x2 *)recv_x,
+                             (uint8_t *)recv_scales, recv_weights);
+    case MOE_QUANT_MXFP8_E5M2:
+        return launch_kernel(dispatch_mx_kernel<V, Dst::E5M2>, grid, block, 0, stream, xv, nvec,
+                             K, token_row, topk_weights, cap, (u32x2 *)recv_x,
+                             (uint8_t *)recv_scales, recv_weights);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_dispatch(const void *x, int T, int H, int K, const int32_t *token_row,
                            const float *topk_weights, int64_t cap, int quant_mode, void *recv_x,
@@ -248,26 +364,32 @@ hipError_t launch_dispatch(const void *x, int T, int H, int K, const int32_t *to
     const int vpt = (nvec + threads - 1) / threads; // 1 or 2 (H <= 16384)
     const dim3 grid(T), block(threads);
     const u32x4 *xv = (const u32x4 *)x;
+    if (vpt == 1)
+        return launch_dispatch_v<1>(grid, block, stream, xv, nvec, K, token_row, topk_weights, cap,
+                                    quant_mode, recv_x, recv_scales, recv_weights);
+    return launch_dispatch_v<2>(grid, block, stream, xv, nvec, K, token_row, topk_weights, cap,
+                                quant_mode, recv_x, recv_scales, recv_weights);
+}
 
-#define MOE_DISPATCH_CASE(V)                                                                       \
-    case V:                                                                                        \
-        if (quant_mode == MOE_QUANT_NONE)                                                          \
-            return launch_kernel(dispatch_bf16_kernel<V>, grid, block, 0, stream, xv, nvec, K,    \
-                                 token_row, topk_weights, cap, (u32x4 *)recv_x, recv_weights);     \
-        if (quant_mode == MOE_QUANT_INT8_PER_TOKEN)                                                \
-            return launch_kernel(dispatch_int8_kernel<V>, grid, block, 0, stream, xv, nvec, K,    \
-                                 token_row, topk_weights, cap, (u32x2 *)recv_x,                   \
-                                 (float *)recv_scales, recv_weights);                              \
-        return launch_kernel(dispatch_mxfp8_kernel<V>, grid, block, 0, stream, xv, nvec, K,       \
-                             token_row, topk_weights, cap, (u32x2 *)recv_x,                       \
-                             (uint8_t *)recv_scales, recv_weights);
-
-    switch (vpt) {
-        MOE_DISPATCH_CASE(1)
-        MOE_DISPATCH_CASE(2)
-    }
-#undef MOE_DISPATCH_CASE
-    return hipErrorInvalidValue;
+hipError_t launch_dispatch_rows(const void *data, int T, int row_bytes, const void *scales,
+                                int scale_bytes, int K, const int32_t *token_row,
+                                const float *topk_weights, int64_t cap, void *recv_data,
+                                void *recv_scales, float *recv_weights, hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    const int nvec = row_bytes / 16;
+    const int threads = row_block_threads(nvec);
+    const int vpt = (nvec + threads - 1) / threads; // 1 or 2 (row_bytes <= 32768)
+    const dim3 grid(T), block(threads);
+    if (vpt == 1)
+        return launch_kernel(dispatch_rows_kernel<1>, grid, block, 0, stream, (const u32x4 *)data,
+                             nvec, (const uint8_t *)scales, scale_bytes, K, token_row,
+                             topk_weights, cap, (u32x4 *)recv_data, (uint8_t *)recv_scales,
+                             recv_weights);
+    return launch_kernel(dispatch_rows_kernel<2>, grid, block, 0, stream, (const u32x4 *)data, nvec,
+                         (const uint8_t *)scales, scale_bytes, K, token_row, topk_weights, cap,
+                         (u32x4 *)recv_data, (uint8_t *)recv_scales, recv_weights);
 }
 
 } // namespace moe

@@ -35,7 +35,22 @@ int check_rows_sizes(int T, int H, int K, int64_t cap, int quant_mode)
         H % MOE_HIDDEN_MULTIPLE != 0 || cap < 0 || cap > INT32_MAX)
         return MOE_ERR_INVALID_ARG;
     if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_INT8_PER_TOKEN &&
-        quant_mode != MOE_QUANT_MXFP8_E4M3)
+        quant_mode != MOE_QUANT_MXFP8_E4M3 && quant_mode != MOE_QUANT_FP8_E4M3_PER_TOKEN &&
+        quant_mode != MOE_QUANT_FP8_E5M2_PER_TOKEN && quant_mode != MOE_QUANT_MXFP8_E5M2)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+bool per_token_scale(int quant_mode)
+{
+    return quant_mode == MOE_QUANT_INT8_PER_TOKEN || quant_mode == MOE_QUANT_FP8_E4M3_PER_TOKEN ||
+           quant_mode == MOE_QUANT_FP8_E5M2_PER_TOKEN;
+}
+
+int check_prequant_sizes(int T, int row_bytes, int scale_bytes, int K, int64_t cap)
+{
+    if (T < 0 || K < 1 || K > MOE_MAX_TOPK || row_bytes < 16 || row_bytes > 32768 ||
+        row_bytes % 16 != 0 || scale_bytes < 0 || scale_bytes > 4096 || cap < 0 || cap > INT32_MAX)
         return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
@@ -120,12 +135,36 @@ int moe_dispatch(const void *x, int num_tokens, int hidden, int num_topk,
         return MOE_ERR_INVALID_ARG;
     if (quant_mode != MOE_QUANT_NONE && !recv_scales)
         return MOE_ERR_INVALID_ARG;
-    if (quant_mode == MOE_QUANT_INT8_PER_TOKEN && ((uintptr_t)recv_scales & 3u) != 0)
+    if (per_token_scale(quant_mode) && ((uintptr_t)recv_scales & 3u) != 0)
         return MOE_ERR_INVALID_ARG;
     if (recv_weights && ((uintptr_t)recv_weights & 3u) != 0)
         return MOE_ERR_INVALID_ARG;
     return launch_dispatch(x, T, H, K, token_row, topk_weights, recv_capacity, quant_mode, recv_x,
                            recv_scales, recv_weights, stream) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
+int moe_dispatch_prequantized(const void *data, int num_tokens, int row_bytes, const void *scales,
+                              int scale_bytes, int num_topk, const int32_t *token_row,
+                              const float *topk_weights, int64_t recv_capacity, void *recv_data,
+                              void *recv_scales, float *recv_weights, hipStream_t stream)
+{
+    const int T = num_tokens, K = num_topk;
+    int rc = check_prequant_sizes(T, row_bytes, scale_bytes, K, recv_capacity);
+    if (rc != MOE_OK)
+        return rc;
+    if (T == 0)
+        return MOE_OK;
+    if (!data || !token_row || !recv_data || !aligned16(data) || !aligned16(recv_data))
+        return MOE_ERR_INVALID_ARG;
+    if (scale_bytes > 0 && (!scales || !recv_scales))
+        return MOE_ERR_INVALID_ARG;
+    if (recv_weights && ((uintptr_t)recv_weights & 3u) != 0)
+        return MOE_ERR_INVALID_ARG;
+    return launch_dispatch_rows(data, T, row_bytes, scales, scale_bytes, K, token_row, topk_weights,
+                                recv_capacity, recv_data, recv_scales, recv_weights,
+                                stream) == hipSuccess
                ? MOE_OK
                : MOE_ERR_HIP;
 }

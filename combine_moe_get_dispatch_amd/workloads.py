@@ -39,6 +39,12 @@ BASE_SEED = 20261202
 QUANT_NONE = 0
 QUANT_INT8_PER_TOKEN = 2
 QUANT_MXFP8_E4M3 = 4
+QUANT_FP8_E4M3_PER_TOKEN = 0x12
+QUANT_FP8_E5M2_PER_TOKEN = 0x22
+QUANT_MXFP8_E5M2 = 0x24
+QUANT_NAMES = {QUANT_NONE: "bf16", QUANT_INT8_PER_TOKEN: "int8 per-token",
+               QUANT_MXFP8_E4M3: "MXFP8 e4m3", QUANT_FP8_E4M3_PER_TOKEN: "FP8 e4m3 per-token",
+               QUANT_FP8_E5M2_PER_TOKEN: "FP8 e5m2 per-token", QUANT_MXFP8_E5M2: "MXFP8 e5m2"}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -58,9 +64,12 @@ class Workload:
     outlier_prob: float = 0.0
     outlier_scale: float = 1.0
     seed_index: int = 0
+    prequant: str = ""              # "" | "mxfp8" | "mxfp4": pre-quantised (data, scale) input
 
     def describe(self) -> str:
-        q = {0: "bf16", 2: "int8 per-token", 4: "MXFP8 e4m3"}[self.quant_mode]
+        q = QUANT_NAMES[self.quant_mode]
+        if self.prequant:
+            q = f"pre-quantised {self.prequant.upper()} pass-through"
         return (f"{self.num_tokens} tokens x hidden {self.hidden}, "
                 f"{self.num_experts} experts / {self.num_ranks} virtual ranks, "
                 f"top-{self.num_topk} {self.routing}, alignment {self.expert_alignment}, {q}")
@@ -78,7 +87,26 @@ WORKLOADS = [
     Workload("bf16_32768x7168_e512_top16", 32768, 7168, 512, 64, 16, 128, QUANT_NONE,
              seed_index=4),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# Further rows: the other 8-bit destinations the pages allow and the
+# pre-quantised tuple input, on the shapes of the measured workloads.
+NEXT_WORKLOADS = [
+    Workload("fp8e4m3_pertoken_8192x7168_e256_top8_zipf", 8192, 7168, 256, 16, 8, 128,
+             QUANT_FP8_E4M3_PER_TOKEN, routing="zipf", zipf_s=1.1, x_sigma=2.0, seed_index=2),
+    Workload("fp8e5m2_pertoken_8192x7168_e256_top8_zipf", 8192, 7168, 256, 16, 8, 128,
+             QUANT_FP8_E5M2_PER_TOKEN, routing="zipf", zipf_s=1.1, x_sigma=2.0, seed_index=2),
+    Workload("mxfp8e5m2_8192x4096_e128_top8_drop", 8192, 4096, 128, 8, 8, 32, QUANT_MXFP8_E5M2,
+             drop_prob=0.1, outlier_prob=0.01, outlier_scale=50.0, seed_index=3),
+    Workload("mxfp8_prequant_8192x7168_e256_top8", 8192, 7168, 256, 8, 8, 1, QUANT_NONE,
+             seed_index=5, prequant="mxfp8"),
+    Workload("mxfp4_prequant_8192x7168_e256_top8", 8192, 7168, 256, 8, 8, 1, QUANT_NONE,
+             seed_index=6, prequant="mxfp4"),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + NEXT_WORKLOADS}
+
+
+def prequant_row_bytes(w: Workload):
+    """(data bytes, scale bytes) per token of a pre-quantised workload."""
+    return (w.hidden if w.prequant == "mxfp8" else w.hidden // 2), w.hidden // 32
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -170,6 +198,20 @@ def generate(w: Workload, num_tokens: Optional[int] = None, seed_offset: int = 0
     x = make_x(_rng(w, 0, seed_offset), T, w.hidden, w.x_sigma, w.outlier_prob, w.outlier_scale)
     idx, wt = generate_routing(w, T, seed_offset)
     return Inputs(w, x, idx, wt)
+
+
+def generate_prequant(w: Workload, num_tokens: Optional[int] = None):
+    """(data uint8 [T, row_bytes], scales uint8 [T, H/32], topk_idx,
+    topk_weights) of a pre-quantised workload.  The data bytes are uniform
+    (dispatch moves them without reading their values); scale bytes are
+    e8m0 exponents 2^-27..2^12 (bytes 100..139)."""
+    T = w.num_tokens if num_tokens is None else num_tokens
+    rb, sb = prequant_row_bytes(w)
+    rng = _rng(w, 0, 0)
+    data = rng.integers(0, 256, size=(T, rb), dtype=np.uint8)
+    scales = rng.integers(100, 140, size=(T, sb), dtype=np.uint8)
+    idx, wt = generate_routing(w, T)
+    return data, scales, idx, wt
 
 
 def random_bf16_rows(rows: int, hidden: int, seed: int, sigma: float = 1.0) -> np.ndarray:

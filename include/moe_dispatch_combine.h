@@ -51,10 +51,16 @@ extern "C" {
 #define MOE_ERR_WORKSPACE (-3)   /* workspace missing, misaligned or too small      */
 #define MOE_ERR_HIP (-4)         /* a HIP launch failed                            */
 
-/* Quantisation modes, numbered like quantMode in the CANN page's Formula. */
-#define MOE_QUANT_NONE 0           /* bf16 rows (Formula Case 1)                          */
-#define MOE_QUANT_INT8_PER_TOKEN 2 /* int8 rows + fp32 scale per row (Formula Case 3)      */
-#define MOE_QUANT_MXFP8_E4M3 4     /* e4m3fn rows + e8m0 byte per 32 elements (Case 5)     */
+/* Quantisation modes.  The low 4 bits are quantMode of the CANN page's Formula
+ * (0 none, 2 per-token dynamic, 4 MX); bits 4-7 select the destination type
+ * where the page allows several (CANN page, Constraint 8, Ascend 950):
+ * 0 = default (int8 for 2, e4m3fn for 4), 1 = float8_e4m3fn, 2 = float8_e5m2. */
+#define MOE_QUANT_NONE 0                  /* bf16 rows (Formula Case 1)                         */
+#define MOE_QUANT_INT8_PER_TOKEN 2        /* int8 rows + fp32 scale per row (Case 3)             */
+#define MOE_QUANT_MXFP8_E4M3 4            /* e4m3fn rows + e8m0 byte per 32 elements (Case 5)    */
+#define MOE_QUANT_FP8_E4M3_PER_TOKEN 0x12 /* e4m3fn rows + fp32 scale per row (Case 3, max 448)  */
+#define MOE_QUANT_FP8_E5M2_PER_TOKEN 0x22 /* e5m2 rows + fp32 scale per row (Case 3, max 57344)  */
+#define MOE_QUANT_MXFP8_E5M2 0x24         /* e5m2 rows + e8m0 byte per 32 elements (Case 5)      */
 
 /* Bits of the device error flag written by moe_get_dispatch_layout. */
 #define MOE_FLAG_BAD_EXPERT_ID 1 /* some topk_idx entry was outside [-1, num_experts) */
@@ -133,10 +139,15 @@ int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_top
  *                             recv_scales[row] = 1.0f / dynamicScales  (fp32)
  *                             (a row whose dynamicScales is not finite gets codes 0
  *                             and scale 0)
- *   MOE_QUANT_MXFP8_E4M3:     per 32-element block j: sharedExp =
- *                             max(floor(log2 max|x|) - 8, -127) (-127 for a zero block),
- *                             recv_x[row, h] = e4m3fn(x[t, h] / 2^sharedExp), rounded
- *                             half to even and saturated to +-448,
+ *   MOE_QUANT_FP8_E4M3_PER_TOKEN / MOE_QUANT_FP8_E5M2_PER_TOKEN: as the int8
+ *                             mode with dstTypeMax 448 / 57344 and the product
+ *                             cast to e4m3fn / e5m2 (half to even, saturated to
+ *                             dstTypeMax); recv_scales[row] = 1.0f / dynamicScales
+ *   MOE_QUANT_MXFP8_E4M3 / MOE_QUANT_MXFP8_E5M2: per 32-element block j:
+ *                             sharedExp = max(floor(log2 max|x|) - emax, -127)
+ *                             (emax 8 / 15; -127 for a zero block),
+ *                             recv_x[row, h] = fp8(x[t, h] / 2^sharedExp), rounded
+ *                             half to even and saturated to +-448 / +-57344,
  *                             recv_scales[row * H/32 + j] = sharedExp + 127 (e8m0)
  *   recv_weights[row] = topk_weights[t, k] (1.0f if topk_weights is NULL), when
  *   recv_weights is not NULL.
@@ -144,8 +155,9 @@ int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_top
  * Rows no entry names (padding, unused) are not written.
  * Inputs (device): x bf16 [T, H]; token_row int32 [T, K] from
  *   moe_get_dispatch_layout; topk_weights fp32 [T, K] or NULL.
- * Outputs (device): recv_x [recv_capacity, H] of bf16 / int8 / e4m3fn;
- *   recv_scales NULL (bf16) / fp32 [recv_capacity] / uint8 [recv_capacity, H/32];
+ * Outputs (device): recv_x [recv_capacity, H] of bf16 / int8 / fp8;
+ *   recv_scales NULL (bf16) / fp32 [recv_capacity] (per-token modes) /
+ *   uint8 [recv_capacity, H/32] (MX modes);
  *   recv_weights fp32 [recv_capacity] or NULL.
  * Sizes: T >= 0, 32 <= H <= 16384 with H % 32 == 0, 1 <= K <= 16,
  *   0 <= recv_capacity < 2^31.
@@ -156,6 +168,29 @@ int moe_dispatch(const void *x, int num_tokens, int hidden, int num_topk,
                  const int32_t *token_row, const float *topk_weights, int64_t recv_capacity,
                  int quant_mode, void *recv_x, void *recv_scales, float *recv_weights,
                  hipStream_t stream);
+
+/*
+ * Dispatch of pre-quantised tokens (Normal Mode API page, dispatch Parameters
+ * x and Quantization Constraints: for MXFP8 / MXFP4 per-block quantisation x
+ * is a (data, scale) tuple, data [T, H] float8 or [T, H/2] float4_e2m1fn_x2,
+ * scales [T, H/32] float8_e8m0fnu; the received rows keep that format).
+ *
+ * For every entry (t, k) with row = token_row[t, k] in [0, recv_capacity):
+ *   recv_data[row, :] = data[t, :] and recv_scales[row, :] = scales[t, :]
+ * byte for byte; recv_weights[row] as for moe_dispatch.
+ * Inputs (device): data [T, row_bytes]; scales [T, scale_bytes] (NULL when
+ *   scale_bytes is 0); token_row int32 [T, K]; topk_weights fp32 [T, K] or NULL.
+ * Outputs (device): recv_data [recv_capacity, row_bytes]; recv_scales
+ *   [recv_capacity, scale_bytes]; recv_weights fp32 [recv_capacity] or NULL.
+ * Sizes: T >= 0, 16 <= row_bytes <= 32768 with row_bytes % 16 == 0,
+ *   0 <= scale_bytes <= 4096, 1 <= K <= 16, 0 <= recv_capacity < 2^31.
+ * data and recv_data must be 16-byte aligned.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP.
+ */
+int moe_dispatch_prequantized(const void *data, int num_tokens, int row_bytes, const void *scales,
+                              int scale_bytes, int num_topk, const int32_t *token_row,
+                              const float *topk_weights, int64_t recv_capacity, void *recv_data,
+                              void *recv_scales, float *recv_weights, hipStream_t stream);
 
 /*
  * Combine (Normal Mode API page, combine: "multiply by weights and sum";

@@ -16,8 +16,17 @@ if not os.path.exists(moe.LIB_PATH):      # build only when nothing is built
 
 DEV = torch.device("cuda", 0)
 
-SENTINEL = {0: 0xFFFF, 2: 0x55, 4: 0x7F}        # bf16 NaN / int8 85 / e4m3 NaN
-SCALE_SENTINEL = {2: -7.0, 4: 0xFF}
+PER_TOKEN = (2, 0x12, 0x22)
+MX = (4, 0x24)
+E5M2 = (0x22, 0x24)
+
+
+def sentinel(quant):
+    return 0xFFFF if quant == 0 else (0x55 if quant == 2 else 0x7F)   # bf16 NaN / int8 85 / fp8 NaN
+
+
+def scale_sentinel(quant):
+    return -7.0 if quant in PER_TOKEN else 0xFF
 
 
 def bf16_dev(bits: np.ndarray) -> torch.Tensor:
@@ -58,27 +67,23 @@ def poisoned_recv(lay, H, quant):
     writes show."""
     rx, rs, rw = moe.allocate_recv(lay, H, quant, with_weights=True)
     if quant == 0:
-        rx.view(torch.int16).fill_(np.int16(np.uint16(SENTINEL[0]).view(np.int16)))
+        rx.view(torch.int16).fill_(np.int16(np.uint16(sentinel(0)).view(np.int16)))
     else:
-        rx.view(torch.uint8).fill_(SENTINEL[quant])
-    if quant == 2:
-        rs.fill_(SCALE_SENTINEL[2])
-    elif quant == 4:
-        rs.fill_(SCALE_SENTINEL[4])
+        rx.view(torch.uint8).fill_(sentinel(quant))
+    if rs is not None:
+        rs.fill_(scale_sentinel(quant))
     rw.fill_(-3.0)
     return rx, rs, rw
 
 
 def oracle_poisoned(cap, H, quant):
     if quant == 0:
-        rx = np.full((cap, H), SENTINEL[0], np.uint16)
-        rs = None
-    elif quant == 2:
-        rx = np.full((cap, H), SENTINEL[2], np.int8)
-        rs = np.full(cap, SCALE_SENTINEL[2], np.float32)
+        return np.full((cap, H), sentinel(0), np.uint16), None
+    rx = np.full((cap, H), sentinel(quant), np.int8 if quant == 2 else np.uint8)
+    if quant in PER_TOKEN:
+        rs = np.full(cap, scale_sentinel(quant), np.float32)
     else:
-        rx = np.full((cap, H), SENTINEL[4], np.uint8)
-        rs = np.full((cap, H // 32), SCALE_SENTINEL[4], np.uint8)
+        rs = np.full((cap, H // 32), scale_sentinel(quant), np.uint8)
     return rx, rs
 
 
@@ -91,18 +96,22 @@ def recv_to_host(rx, quant):
 
 
 def dequant_identity_expert(rx_host: np.ndarray, rs_host, quant: int) -> np.ndarray:
-    """The identity expert for quantised rows: bf16(decode(codes)), computed on
-    the CPU with torch (test harness, not part of the path)."""
+    """The identity expert for quantised rows: bf16(decode(codes) * scale),
+    computed on the CPU with torch (test harness, not part of the path)."""
     if quant == 0:
         return rx_host
     if quant == 2:
-        y = torch.from_numpy(rx_host.astype(np.float32)) * torch.from_numpy(rs_host)[:, None]
+        codes = torch.from_numpy(rx_host.astype(np.float32))
     else:
-        codes = torch.from_numpy(rx_host).view(torch.float8_e4m3fn).float()
+        fp8 = torch.float8_e5m2 if quant in E5M2 else torch.float8_e4m3fn
+        codes = torch.from_numpy(rx_host).view(fp8).float()
+    if quant in PER_TOKEN:
+        y = codes * torch.from_numpy(rs_host)[:, None]
+    else:
         cap, H = rx_host.shape
         sc = torch.from_numpy(rs_host.astype(np.float32) - 127.0)
         y = (codes.view(cap, H // 32, 32) * torch.exp2(sc)[:, :, None]).view(cap, H)
-    y = torch.nan_to_num(y, nan=0.0)        # padding rows hold sentinels; never read by combine
+    y = torch.nan_to_num(y, nan=0.0, posinf=0.0, neginf=0.0)   # padding rows hold sentinels
     return y.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 

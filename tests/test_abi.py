@@ -123,3 +123,30 @@ def test_dispatch_pointer_rules(L):
     assert L.moe_dispatch(None, 0, 64, 2, None, None, 100, 0, None, None, None, None) == 0
     assert L.moe_combine(BAD, 100, 4, 64, 2, BAD, None, ctypes.c_void_p(0x1004), None) == -1
     assert L.moe_combine(None, 100, 0, 64, 2, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("q", [0x14, 0x32, 0x42, 0x23, 6])
+def test_unknown_quant_modes_rejected(L, orc, q):
+    assert orc.check_rows_args(16, 1024, 4, 1000, q) == -1
+    assert L.moe_dispatch(BAD, 16, 1024, 4, BAD, BAD, 1000, q, BAD, BAD, BAD, None) == -1
+
+
+PREQUANT_CASES = [(4, 8, 1, 2, 10), (4, 24, 1, 2, 10), (4, 32784, 0, 2, 10), (4, 32, 4097, 2, 10),
+                  (4, 32, -1, 2, 10), (4, 32, 1, 0, 10), (4, 32, 1, 17, 10), (-1, 32, 1, 2, 10),
+                  (4, 32, 1, 2, -1)]
+
+
+@pytest.mark.parametrize("T,rb,sb,K,cap", PREQUANT_CASES)
+def test_prequantized_rejects_like_the_oracle(L, orc, T, rb, sb, K, cap):
+    expect = orc.check_prequant_args(T, rb, sb, K, cap)
+    assert expect != 0
+    assert L.moe_dispatch_prequantized(BAD, T, rb, BAD, sb, K, BAD, None, cap, BAD, BAD, None, None) == expect
+
+
+def test_prequantized_pointer_rules(L):
+    f = L.moe_dispatch_prequantized
+    assert f(None, 4, 64, BAD, 2, 2, BAD, None, 100, BAD, BAD, None, None) == -1
+    assert f(ctypes.c_void_p(0x1008), 4, 64, BAD, 2, 2, BAD, None, 100, BAD, BAD, None, None) == -1
+    assert f(BAD, 4, 64, None, 2, 2, BAD, None, 100, BAD, BAD, None, None) == -1
+    assert f(BAD, 4, 64, BAD, 2, 2, BAD, None, 100, BAD, None, None, None) == -1
+    assert f(None, 0, 64, None, 2, 2, None, None, 100, None, None, None, None) == 0

@@ -42,9 +42,9 @@ def run_full_case(x_bits, idx, wts, E, R, a, quant, north_star=True):
     moe.moe_dispatch(x_dev, lay, w_dev, quant, recv_x=rx, recv_scales=rs, recv_weights=rw)
     grx = recv_to_host(rx, quant)
     np.testing.assert_array_equal(grx, orx)
-    if quant == 2:
+    if rs is not None and rs.dtype == torch.float32:
         np.testing.assert_array_equal(rs.cpu().numpy().view(np.uint32), ors.view(np.uint32))
-    elif quant == 4:
+    elif rs is not None:
         np.testing.assert_array_equal(rs.cpu().numpy(), ors)
     used = ol.recv_src >= 0
     np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
@@ -132,6 +132,11 @@ EDGE = [
     ("duplicates", 333, 64, 4, 2, 8, 3, 0, True, 0.0),
     ("all_dropped", 64, 64, 8, 2, 4, 4, 0, False, 1.0),
     ("one_token", 1, 7168, 256, 8, 8, 128, 2, False, 0.0),
+    ("fp8_e4m3_per_token", 700, 7168, 64, 8, 8, 16, 0x12, False, 0.05),
+    ("fp8_e5m2_per_token", 700, 4096, 64, 8, 8, 16, 0x22, True, 0.05),
+    ("mxfp8_e5m2", 700, 4096, 128, 8, 8, 32, 0x24, False, 0.1),
+    ("mxfp8_e5m2_max_hidden", 40, 16384, 128, 8, 8, 32, 0x24, False, 0.0),
+    ("fp8_e4m3_per_token_h96", 257, 96, 8, 2, 3, 1, 0x12, False, 0.1),
 ]
 
 
@@ -195,7 +200,7 @@ def test_quant_special_rows():
     T = x.shape[0]
     idx = np.stack([np.arange(T) % E, (np.arange(T) + 1) % E], axis=1).astype(np.int64)
     wts = np.full((T, K), 0.5, np.float32)
-    for quant in (2, 4):
+    for quant in (2, 4, 0x12, 0x22, 0x24):
         run_full_case(x, idx, wts, E, 2, 1, quant, north_star=False)
 
 
@@ -305,3 +310,35 @@ def test_graph_capture_replays_match_eager(quant):
         for a_, b_ in zip(ref, got):
             if a_ is not None:
                 assert torch.equal(a_, b_)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "no_scales"])
+def test_dispatch_prequantized_parity(fmt):
+    """Pre-quantised (data, scale) rows are copied byte for byte: whole
+    receive buffers equal the oracle's, sentinels included."""
+    rng = np.random.default_rng(zlib.crc32(fmt.encode()))
+    T, H, K, E, R, a = 900, 7168, 8, 64, 8, 32
+    idx, wts = _routing(rng, T, K, E, drop=0.05)
+    row_bytes = H if fmt == "mxfp8" else H // 2
+    scale_bytes = 0 if fmt == "no_scales" else H // 32
+    data = rng.integers(0, 256, size=(T, row_bytes), dtype=np.uint8)
+    sc = rng.integers(100, 140, size=(T, scale_bytes), dtype=np.uint8) if scale_bytes else None
+    ol = oracle.layout(idx, E, R, a)
+    lay = gpu_layout(idx, E, R, a)
+    cap = ol.recv_capacity
+    ord0 = np.full((cap, row_bytes), 0xA5, np.uint8)
+    ors0 = np.full((cap, scale_bytes), 0x5A, np.uint8) if scale_bytes else None
+    ord_, ors, orw = oracle.dispatch_prequantized(data, sc, ol.token_row, cap, wts, ord0,
+                                                  ors0, with_weights=True)
+    dtype = torch.float8_e4m3fn if fmt == "mxfp8" else torch.uint8
+    d_dev = torch.from_numpy(data).to(DEV).view(dtype)
+    s_dev = None if sc is None else torch.from_numpy(sc).to(DEV)
+    rd = torch.full((cap, row_bytes), 0xA5, dtype=torch.uint8, device=DEV).view(dtype)
+    rs = None if sc is None else torch.full((cap, scale_bytes), 0x5A, dtype=torch.uint8, device=DEV)
+    rw = torch.full((cap,), -3.0, device=DEV)
+    moe.moe_dispatch_prequantized(d_dev, s_dev, lay, torch.from_numpy(wts).to(DEV), rd, rs, rw)
+    np.testing.assert_array_equal(rd.view(torch.uint8).cpu().numpy(), ord_)
+    if sc is not None:
+        np.testing.assert_array_equal(rs.cpu().numpy(), ors)
+    used = ol.recv_src >= 0
+    np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
