@@ -30,6 +30,10 @@ QUANT_MXFP8 = 4
 QUANT_FP8_E4M3_PT = 0x12
 QUANT_FP8_E5M2_PT = 0x22
 QUANT_MXFP8_E5M2 = 0x24
+QUANT_FP8_E4M3_PG = 0x13
+QUANT_FP8_E5M2_PG = 0x23
+GROUP = 128
+PER_GROUP_MODES = (QUANT_FP8_E4M3_PG, QUANT_FP8_E5M2_PG)
 PER_TOKEN_SCALE_MODES = (QUANT_INT8, QUANT_FP8_E4M3_PT, QUANT_FP8_E5M2_PT)
 MX_MODES = (QUANT_MXFP8, QUANT_MXFP8_E5M2)
 
@@ -89,6 +93,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_quant_mx_e5m2_rows.restype = None
         L.oracle_quant_fp8_pertoken_rows.argtypes = [_P, i32, i32, i32, _P, _P]
         L.oracle_quant_fp8_pertoken_rows.restype = None
+        L.oracle_check_static_args.argtypes = [i32, i32, i32, i64, i32]
+        L.oracle_check_static_args.restype = i32
+        L.oracle_dispatch_static.argtypes = [_P, i32, i32, i32, _P, _P, i64, _P, i32, _P, _P]
+        L.oracle_dispatch_static.restype = i32
+        L.oracle_quant_fp8_pergroup_rows.argtypes = [_P, i32, i32, i32, _P, _P]
+        L.oracle_quant_fp8_pergroup_rows.restype = None
+        L.oracle_quant_static_int8_rows.argtypes = [_P, i32, i32, _P, i32, _P]
+        L.oracle_quant_static_int8_rows.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = i32
         _lib = L
@@ -164,12 +176,55 @@ def dispatch(x_bits: np.ndarray, token_row: np.ndarray, recv_capacity: int,
             recv_scales = np.zeros(cap, np.float32)
         elif quant_mode in MX_MODES:
             recv_scales = np.zeros((cap, H // 32), np.uint8)
+        elif quant_mode in PER_GROUP_MODES:
+            recv_scales = np.zeros((cap, (H + GROUP - 1) // GROUP), np.float32)
     recv_w = np.zeros(cap, np.float32) if with_weights else None
     rc = lib().oracle_dispatch(_ptr(x), T, H, K, _ptr(row), _ptr(w), cap, quant_mode,
                                _ptr(recv_x), _ptr(recv_scales), _ptr(recv_w))
     if rc != OK:
         raise OracleError(rc)
     return recv_x, recv_scales, recv_w
+
+
+def check_static_args(T, H, K, cap, num_scales) -> int:
+    return int(lib().oracle_check_static_args(T, H, K, cap, num_scales))
+
+
+def dispatch_static(x_bits, token_row, recv_capacity, scales, topk_weights=None, recv_x=None,
+                    with_weights=False):
+    """Static int8 quantisation (scales: 1 or H fp32 values).  Returns (recv_x, recv_weights)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    row = np.ascontiguousarray(token_row, dtype=np.int32)
+    K = row.shape[1]
+    sc = np.ascontiguousarray(scales, dtype=np.float32).reshape(-1)
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    if recv_x is None:
+        recv_x = np.zeros((recv_capacity, H), np.int8)
+    recv_w = np.zeros(recv_capacity, np.float32) if with_weights else None
+    rc = lib().oracle_dispatch_static(_ptr(x), T, H, K, _ptr(row), _ptr(w), recv_capacity,
+                                      _ptr(sc), sc.size, _ptr(recv_x), _ptr(recv_w))
+    if rc != OK:
+        raise OracleError(rc)
+    return recv_x, recv_w
+
+
+def quant_fp8_pergroup_rows(x_bits: np.ndarray, fmt: str = "e4m3"):
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    q = np.zeros((T, H), np.uint8)
+    s = np.zeros((T, (H + GROUP - 1) // GROUP), np.float32)
+    lib().oracle_quant_fp8_pergroup_rows(_ptr(x), T, H, {"e4m3": 1, "e5m2": 2}[fmt], _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_static_int8_rows(x_bits: np.ndarray, scales):
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    sc = np.ascontiguousarray(scales, dtype=np.float32).reshape(-1)
+    q = np.zeros((T, H), np.int8)
+    lib().oracle_quant_static_int8_rows(_ptr(x), T, H, _ptr(sc), sc.size, _ptr(q))
+    return q
 
 
 def check_prequant_args(T, row_bytes, scale_bytes, K, cap) -> int:

@@ -59,7 +59,14 @@ enum {
     ORC_QUANT_FP8_E4M3_PT = 0x12,
     ORC_QUANT_FP8_E5M2_PT = 0x22,
     ORC_QUANT_MXFP8_E5M2 = 0x24,
+    ORC_QUANT_FP8_E4M3_PG = 0x13,
+    ORC_QUANT_FP8_E5M2_PG = 0x23,
 };
+
+/* Group size of the per-group dynamic quantisation (quantMode 3).  The page
+ * gives none; its buffer sizing for this mode aligns H to 128 ([CANN]
+ * Constraint 9, Ascend 950: alignedH = Align128(H)), read as the group. */
+enum { ORC_GROUP = 128 };
 
 /* 8-bit float element formats. */
 enum { FMT_E4M3FN = 1, FMT_E5M2 = 2 };
@@ -106,7 +113,19 @@ int oracle_check_rows_args(int T, int H, int K, int64_t cap, int quant_mode)
         return ORC_ERR_INVALID_ARG;
     if (quant_mode != ORC_QUANT_NONE && quant_mode != ORC_QUANT_INT8 &&
         quant_mode != ORC_QUANT_MXFP8 && quant_mode != ORC_QUANT_FP8_E4M3_PT &&
-        quant_mode != ORC_QUANT_FP8_E5M2_PT && quant_mode != ORC_QUANT_MXFP8_E5M2)
+        quant_mode != ORC_QUANT_FP8_E5M2_PT && quant_mode != ORC_QUANT_MXFP8_E5M2 &&
+        quant_mode != ORC_QUANT_FP8_E4M3_PG && quant_mode != ORC_QUANT_FP8_E5M2_PG)
+        return ORC_ERR_INVALID_ARG;
+    return ORC_OK;
+}
+
+/* Static quantisation arguments: the dispatch sizes plus 1 or H scales. */
+int oracle_check_static_args(int T, int H, int K, int64_t cap, int num_scales)
+{
+    int rc = oracle_check_rows_args(T, H, K, cap, ORC_QUANT_NONE);
+    if (rc != ORC_OK)
+        return rc;
+    if (num_scales != 1 && num_scales != H)
         return ORC_ERR_INVALID_ARG;
     return ORC_OK;
 }
@@ -421,6 +440,58 @@ static void quant_fp8_pertoken_row(const uint16_t *x, int H, int fmt, uint8_t *q
     *scale_out = 1.0f / dynamicScales;
 }
 
+/* [CANN] Formula Case 4 (quantMode 3, per-group dynamic quantisation; the
+ * page prints the Case 3 formula for it, and Constraint 8 (Ascend 950) gives
+ * FLOAT8_E4M3FN or FLOAT8_E5M2 as the destination): Case 3 applied to each
+ * group of ORC_GROUP consecutive elements of the row (the last group holds
+ * the H % 128 remaining elements when H is not a multiple of 128):
+ *   dynamicScales_g = dstTypeMax / Max(Abs(xFp32 over g))
+ *   quantOut        = CastToFp8(xFp32 * dynamicScales_g)   (product in fp32)
+ *   scale out g     = 1.0 / dynamicScales_g                (fp32, ceil(H/128) per row)
+ * A group whose dynamicScales is not finite gets codes 0 and scale 0. */
+static void quant_fp8_pergroup_row(const uint16_t *x, int H, int fmt, uint8_t *quantOut,
+                                   float *scales_out)
+{
+    const float dstTypeMax = (float)fp8_max(fmt);
+    for (int g0 = 0, g = 0; g0 < H; g0 += ORC_GROUP, ++g) {
+        const int n = H - g0 < ORC_GROUP ? H - g0 : ORC_GROUP;
+        float maxabs = 0.0f;
+        for (int h = g0; h < g0 + n; ++h) {
+            float ab = fabsf(bf16_to_f32(x[h]));
+            if (ab > maxabs)
+                maxabs = ab;
+        }
+        float dynamicScales = dstTypeMax / maxabs;
+        for (int h = g0; h < g0 + n; ++h)
+            quantOut[h] = isfinite(dynamicScales)
+                              ? cast_to_fp8(fmt, (double)(bf16_to_f32(x[h]) * dynamicScales))
+                              : 0;
+        scales_out[g] = 1.0f / dynamicScales;
+    }
+}
+
+/* [CANN] Formula Case 2 (quantMode 1, static quantisation) with an INT8
+ * destination ([CANN] Constraint 8, Ascend 950: the input scales are one
+ * quantisation coefficient, shape (1,), or a smoothing vector shared by all
+ * experts, shape (H,)):
+ *   xFp32    = CastToFp32(X) * scales     (fp32 multiply)
+ *   quantOut = Cast(xFp32, INT8)
+ * Reading: the cast rounds half to even and saturates to [-128, 127] (a
+ * static scale does not bound the product as the dynamic modes do). */
+static void quant_static_int8_row(const uint16_t *x, int H, const float *scales, int num_scales,
+                                  int8_t *quantOut)
+{
+    for (int h = 0; h < H; ++h) {
+        float xFp32 = bf16_to_f32(x[h]) * scales[num_scales == 1 ? 0 : h];
+        float r = rintf(xFp32);
+        if (r > 127.0f)
+            r = 127.0f;
+        if (r < -128.0f)
+            r = -128.0f;
+        quantOut[h] = (int8_t)r;
+    }
+}
+
 /* ------------------------------------------------------------------------- */
 /* Dispatch                                                                   */
 /* ------------------------------------------------------------------------- */
@@ -436,8 +507,9 @@ static void quant_fp8_pertoken_row(const uint16_t *x, int H, int fmt, uint8_t *q
  *
  * x: bf16 bits [T, H].  token_row: [T*K] from oracle_layout.  topk_weights:
  * [T*K] or NULL.  recv_x: [cap, H] of uint16 (bf16), int8 or uint8 (fp8)
- * elements.  recv_scales: NULL (bf16), float [cap] (per-token modes) or
- * uint8 [cap * H/32] (MX modes, row-major).  recv_weights: [cap] or NULL; receives the
+ * elements.  recv_scales: NULL (bf16), float [cap] (per-token modes), float
+ * [cap * ceil(H/128)] (per-group modes) or uint8 [cap * H/32] (MX modes),
+ * row-major.  recv_weights: [cap] or NULL; receives the
  * weight of the (t, k) entry a row holds.  Rows not named by token_row are
  * left untouched.
  */
@@ -455,13 +527,14 @@ int oracle_dispatch(const uint16_t *x, int T, int H, int K, const int32_t *token
 
     const int per_token_scale = quant_mode == ORC_QUANT_INT8 || quant_mode == ORC_QUANT_FP8_E4M3_PT ||
                                 quant_mode == ORC_QUANT_FP8_E5M2_PT;
-    const int fmt = (quant_mode == ORC_QUANT_FP8_E5M2_PT || quant_mode == ORC_QUANT_MXFP8_E5M2)
-                        ? FMT_E5M2
-                        : FMT_E4M3FN;
+    const int per_group = quant_mode == ORC_QUANT_FP8_E4M3_PG || quant_mode == ORC_QUANT_FP8_E5M2_PG;
+    const int G = (H + ORC_GROUP - 1) / ORC_GROUP;
+    const int fmt = (quant_mode >> 4) == 2 ? FMT_E5M2 : FMT_E4M3FN;
 #pragma omp parallel
     {
         uint8_t *q = (uint8_t *)malloc((size_t)H);
         uint8_t *sc8 = (uint8_t *)malloc((size_t)H / 32);
+        float *scg = (float *)malloc(sizeof(float) * (size_t)G);
 #pragma omp for schedule(static)
         for (int t = 0; t < T; ++t) {
             const uint16_t *xt = x + (int64_t)t * H;
@@ -472,6 +545,8 @@ int oracle_dispatch(const uint16_t *x, int T, int H, int K, const int32_t *token
                 quant_fp8_pertoken_row(xt, H, fmt, q, &s_row);
             else if (quant_mode == ORC_QUANT_MXFP8 || quant_mode == ORC_QUANT_MXFP8_E5M2)
                 quant_mx_row(xt, H, fmt, q, sc8);
+            else if (per_group)
+                quant_fp8_pergroup_row(xt, H, fmt, q, scg);
             for (int k = 0; k < K; ++k) {
                 int32_t row = token_row[(int64_t)t * K + k];
                 if (row < 0 || row >= cap)
@@ -482,6 +557,8 @@ int oracle_dispatch(const uint16_t *x, int T, int H, int K, const int32_t *token
                     memcpy((uint8_t *)recv_x + (int64_t)row * H, q, (size_t)H);
                     if (per_token_scale)
                         ((float *)recv_scales)[row] = s_row;
+                    else if (per_group)
+                        memcpy((float *)recv_scales + (int64_t)row * G, scg, sizeof(float) * (size_t)G);
                     else
                         memcpy((uint8_t *)recv_scales + (int64_t)row * (H / 32), sc8, (size_t)H / 32);
                 }
@@ -491,6 +568,42 @@ int oracle_dispatch(const uint16_t *x, int T, int H, int K, const int32_t *token
         }
         free(q);
         free(sc8);
+        free(scg);
+    }
+    return ORC_OK;
+}
+
+/*
+ * Dispatch with static int8 quantisation ([CANN] Formula Case 2, quantMode
+ * 1): every token is quantised once with the caller's scales (1 value, or H
+ * values applied per channel) and copied to its rows; no scales are output
+ * (they are the caller's).  recv_x: int8 [cap, H].
+ */
+int oracle_dispatch_static(const uint16_t *x, int T, int H, int K, const int32_t *token_row,
+                           const float *topk_weights, int64_t cap, const float *scales,
+                           int num_scales, int8_t *recv_x, float *recv_weights)
+{
+    int rc = oracle_check_static_args(T, H, K, cap, num_scales);
+    if (rc != ORC_OK)
+        return rc;
+    if (T > 0 && (!x || !token_row || !recv_x || !scales))
+        return ORC_ERR_INVALID_ARG;
+#pragma omp parallel
+    {
+        int8_t *q = (int8_t *)malloc((size_t)H);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            quant_static_int8_row(x + (int64_t)t * H, H, scales, num_scales, q);
+            for (int k = 0; k < K; ++k) {
+                int32_t row = token_row[(int64_t)t * K + k];
+                if (row < 0 || row >= cap)
+                    continue;
+                memcpy(recv_x + (int64_t)row * H, q, (size_t)H);
+                if (recv_weights)
+                    recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;
+            }
+        }
+        free(q);
     }
     return ORC_OK;
 }
@@ -552,6 +665,23 @@ void oracle_quant_mx_e5m2_rows(const uint16_t *x, int T, int H, uint8_t *q, uint
     for (int t = 0; t < T; ++t)
         quant_mx_row(x + (int64_t)t * H, H, FMT_E5M2, q + (int64_t)t * H,
                      scales + (int64_t)t * (H / 32));
+}
+
+/* fmt: 1 = e4m3fn, 2 = e5m2; scales [T, ceil(H/128)] */
+void oracle_quant_fp8_pergroup_rows(const uint16_t *x, int T, int H, int fmt, uint8_t *q,
+                                    float *scales)
+{
+    const int G = (H + ORC_GROUP - 1) / ORC_GROUP;
+    for (int t = 0; t < T; ++t)
+        quant_fp8_pergroup_row(x + (int64_t)t * H, H, fmt, q + (int64_t)t * H,
+                               scales + (int64_t)t * G);
+}
+
+void oracle_quant_static_int8_rows(const uint16_t *x, int T, int H, const float *scales,
+                                   int num_scales, int8_t *q)
+{
+    for (int t = 0; t < T; ++t)
+        quant_static_int8_row(x + (int64_t)t * H, H, scales, num_scales, q + (int64_t)t * H);
 }
 
 /* fmt: 1 = e4m3fn, 2 = e5m2 */
