@@ -59,18 +59,28 @@ def parse():
 
 
 PER_TOKEN_MODES = (0x02, 0x12, 0x22)
+PER_GROUP_MODES = (0x13, 0x23)
 
 
-def stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows=None):
+def stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows=None, static=False):
     """Algorithmic bytes of each stage (see module docstring).  prequant_rows =
     (data bytes, scale bytes) per token for the pre-quantised pass-through."""
     layout = 8 * T * K + 4 * T * R + 4 * R + 8 * E + 4 * (E + 1) + 4 * T * K + 4 * cap + 4
     if prequant_rows is not None:
         rb, sb = prequant_rows
         dispatch = T * (rb + sb) + 4 * T * K + V * (rb + sb)
+    elif static:
+        dispatch = 2 * T * H + 4 * T * K + V * H
     else:
         s_q = 2 if quant == 0 else 1
-        sigma = 0 if quant == 0 else (4 if quant in PER_TOKEN_MODES else H // 32)
+        if quant == 0:
+            sigma = 0
+        elif quant in PER_TOKEN_MODES:
+            sigma = 4
+        elif quant in PER_GROUP_MODES:
+            sigma = 4 * ((H + 127) // 128)
+        else:
+            sigma = H // 32
         dispatch = 2 * T * H + 4 * T * K + V * (H * s_q + sigma)
     combine = 2 * V * H + 8 * T * K + 2 * T * H
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
@@ -170,6 +180,10 @@ def cpu_baseline(inp, w, quant, budget_s, bytes_fn, prequant=None):
         if prequant is not None:
             oracle.dispatch_prequantized(prequant[0], prequant[1], ol.token_row, ol.recv_capacity)
             y = prequant[2]
+        elif w.static_scale > 0:
+            oracle.dispatch_static(inp.x_bits, ol.token_row, ol.recv_capacity,
+                                   np.array([w.static_scale], np.float32))
+            y = np.zeros((ol.recv_capacity, w.hidden), np.uint16)
         else:
             rx, rs, _ = oracle.dispatch(inp.x_bits, ol.token_row, ol.recv_capacity, None, quant)
             y = rx if quant == 0 else np.zeros((ol.recv_capacity, w.hidden), np.uint16)
@@ -233,6 +247,16 @@ def main():
 
         def run_dispatch():
             moe.moe_dispatch_prequantized(data, scales, lay, None, rd, rsc)
+    elif w.static_scale > 0:
+        x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        rx = torch.empty((cap, H), dtype=torch.int8, device=dev)
+        sscale = torch.tensor([w.static_scale], dtype=torch.float32, device=dev)
+
+        def run_dispatch():
+            moe.moe_dispatch_static(x, lay, sscale, None, recv_x=rx)
+
+        run_dispatch()
+        y = (rx.float() / w.static_scale).to(torch.bfloat16)   # identity expert
     else:
         x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
         rx, rs, _ = moe.allocate_recv(lay, H, quant)
@@ -248,6 +272,8 @@ def main():
             codes = rx.float()
             if quant in PER_TOKEN_MODES:
                 y = codes * rs[:, None]
+            elif quant in PER_GROUP_MODES:
+                y = codes * rs.repeat_interleave(128, dim=1)[:, :H]
             else:
                 y = (codes.view(cap, H // 32, 32) * torch.exp2(rs.float() - 127.0)[:, :, None]).view(cap, H)
             y = torch.nan_to_num(y, nan=0.0, posinf=0.0, neginf=0.0).to(torch.bfloat16)
@@ -291,7 +317,7 @@ def main():
     avg_us = {k: float(np.mean(v)) for k, v in st.items()}
     med_us = {k: float(np.median(v)) for k, v in st.items()}
 
-    sb = stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows)
+    sb = stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows, w.static_scale > 0)
     step_bytes = sum(sb.values())
     ms_per_step = elapsed / args.steps * 1e3
     gbs = step_bytes * args.steps / elapsed / 1e9
@@ -306,7 +332,7 @@ def main():
         u = src >= 0
         if w.prequant:
             assert torch.equal(rd[u], data[src[u] // K])
-        elif quant == 0:
+        elif quant == 0 and not w.static_scale > 0:
             assert torch.equal(rx.view(torch.int16)[u], x.view(torch.int16)[src[u] // K])
         assert int(lay.error_flag.item()) == 0
 
@@ -321,11 +347,15 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(inp, w, quant, args.cpu_seconds,
-                           lambda v, c: stage_bytes(T, H, K, R, E, v, c, quant, prequant_rows),
+                           lambda v, c: stage_bytes(T, H, K, R, E, v, c, quant, prequant_rows,
+                                                    w.static_scale > 0),
                            prequant=cpu_y)
 
     qname = {0: "bf16", 2: "int8", 4: "mxfp8_e4m3", 0x12: "fp8_e4m3_per_token",
-             0x22: "fp8_e5m2_per_token", 0x24: "mxfp8_e5m2"}[quant]
+             0x22: "fp8_e5m2_per_token", 0x24: "mxfp8_e5m2", 0x13: "fp8_e4m3_per_group",
+             0x23: "fp8_e5m2_per_group"}[quant]
+    if w.static_scale > 0:
+        qname = "int8_static"
     if w.prequant:
         qname = f"{w.prequant}_prequantized"
     rec = {
@@ -339,7 +369,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16" if quant == 0 else f"bf16->{qname}") if not w.prequant else qname,
+        "dtype": ("bf16" if qname == "bf16" else f"bf16->{qname}") if not w.prequant else qname,
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.describe(), "num_tokens": T, "hidden": H,
                    "num_experts": E, "num_virtual_ranks": R, "top_k": K, "expert_alignment": a,

@@ -37,18 +37,24 @@ QUANT_MXFP8_E4M3 = 4
 QUANT_FP8_E4M3_PER_TOKEN = 0x12
 QUANT_FP8_E5M2_PER_TOKEN = 0x22
 QUANT_MXFP8_E5M2 = 0x24
+QUANT_FP8_E4M3_PER_GROUP = 0x13
+QUANT_FP8_E5M2_PER_GROUP = 0x23
+QUANT_GROUP = 128
+PER_GROUP_MODES = (QUANT_FP8_E4M3_PER_GROUP, QUANT_FP8_E5M2_PER_GROUP)
 PER_TOKEN_SCALE_MODES = (QUANT_INT8_PER_TOKEN, QUANT_FP8_E4M3_PER_TOKEN, QUANT_FP8_E5M2_PER_TOKEN)
 MX_MODES = (QUANT_MXFP8_E4M3, QUANT_MXFP8_E5M2)
 
 FLAG_BAD_EXPERT_ID = 1
 
 __all__ = [
-    "moe_get_dispatch_layout", "moe_dispatch", "moe_dispatch_prequantized", "moe_combine",
+    "moe_get_dispatch_layout", "moe_dispatch", "moe_dispatch_static", "moe_dispatch_prequantized",
+    "moe_combine",
     "moe_recv_capacity_bound",
     "moe_layout_workspace_bytes", "DispatchLayout", "allocate_layout", "allocate_recv",
     "num_recv_tokens_per_expert_list", "MoeError", "lib",
     "QUANT_NONE", "QUANT_INT8_PER_TOKEN", "QUANT_MXFP8_E4M3", "QUANT_FP8_E4M3_PER_TOKEN",
-    "QUANT_FP8_E5M2_PER_TOKEN", "QUANT_MXFP8_E5M2",
+    "QUANT_FP8_E5M2_PER_TOKEN", "QUANT_MXFP8_E5M2", "QUANT_FP8_E4M3_PER_GROUP",
+    "QUANT_FP8_E5M2_PER_GROUP",
 ]
 
 
@@ -80,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.moe_get_dispatch_layout.restype = i32
         L.moe_dispatch.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
         L.moe_dispatch.restype = i32
+        L.moe_dispatch_static.argtypes = [P, i32, i32, i32, P, P, i64, P, i32, P, P, P]
+        L.moe_dispatch_static.restype = i32
         L.moe_dispatch_prequantized.argtypes = [P, i32, i32, P, i32, i32, P, P, i64, P, P, P, P]
         L.moe_dispatch_prequantized.restype = i32
         L.moe_combine.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
@@ -195,14 +203,16 @@ def num_recv_tokens_per_expert_list(layout: DispatchLayout) -> list:
 
 _RECV_DTYPE = {QUANT_NONE: torch.bfloat16, QUANT_INT8_PER_TOKEN: torch.int8,
                QUANT_MXFP8_E4M3: torch.float8_e4m3fn, QUANT_FP8_E4M3_PER_TOKEN: torch.float8_e4m3fn,
-               QUANT_FP8_E5M2_PER_TOKEN: torch.float8_e5m2, QUANT_MXFP8_E5M2: torch.float8_e5m2}
+               QUANT_FP8_E5M2_PER_TOKEN: torch.float8_e5m2, QUANT_MXFP8_E5M2: torch.float8_e5m2,
+               QUANT_FP8_E4M3_PER_GROUP: torch.float8_e4m3fn, QUANT_FP8_E5M2_PER_GROUP: torch.float8_e5m2}
 
 
 def allocate_recv(layout: DispatchLayout, hidden: int, quant_mode: int = QUANT_NONE,
                   with_weights: bool = False):
     """Receive buffers for ``quant_mode``: rows [cap, H] of the mode's element
-    type, scales fp32 [cap] (per-token modes) or uint8 e8m0 [cap, H/32] (MX
-    modes) or None (bf16), optional fp32 row weights [cap]."""
+    type, scales fp32 [cap] (per-token modes), fp32 [cap, ceil(H/128)]
+    (per-group modes), uint8 e8m0 [cap, H/32] (MX modes) or None (bf16),
+    optional fp32 row weights [cap]."""
     dev = layout.token_row.device
     cap = layout.recv_capacity
     if quant_mode not in _RECV_DTYPE:
@@ -212,6 +222,9 @@ def allocate_recv(layout: DispatchLayout, hidden: int, quant_mode: int = QUANT_N
         rs = torch.empty(cap, dtype=torch.float32, device=dev)
     elif quant_mode in MX_MODES:
         rs = torch.empty((cap, hidden // 32), dtype=torch.uint8, device=dev)
+    elif quant_mode in PER_GROUP_MODES:
+        rs = torch.empty((cap, (hidden + QUANT_GROUP - 1) // QUANT_GROUP), dtype=torch.float32,
+                         device=dev)
     else:
         rs = None
     rw = torch.empty(cap, dtype=torch.float32, device=dev) if with_weights else None
@@ -243,6 +256,9 @@ def moe_dispatch(x: torch.Tensor, layout: DispatchLayout, topk_weights: Optional
         _check(recv_scales, "recv_scales", torch.float32, (cap,), dev)
     elif quant_mode in MX_MODES:
         _check(recv_scales, "recv_scales", torch.uint8, (cap, H // 32), dev)
+    elif quant_mode in PER_GROUP_MODES:
+        _check(recv_scales, "recv_scales", torch.float32,
+               (cap, (H + QUANT_GROUP - 1) // QUANT_GROUP), dev)
     if recv_weights is not None:
         _check(recv_weights, "recv_weights", torch.float32, (cap,), dev)
     rc = lib().moe_dispatch(_ptr(x), T, H, K, _ptr(layout.token_row), _ptr(topk_weights), cap,
@@ -251,6 +267,38 @@ def moe_dispatch(x: torch.Tensor, layout: DispatchLayout, topk_weights: Optional
     if rc != MOE_OK:
         raise MoeError("moe_dispatch", rc)
     return recv_x, recv_scales, recv_weights
+
+
+def moe_dispatch_static(x: torch.Tensor, layout: DispatchLayout, scales: torch.Tensor,
+                        topk_weights: Optional[torch.Tensor] = None,
+                        recv_x: Optional[torch.Tensor] = None,
+                        recv_weights: Optional[torch.Tensor] = None, with_weights: bool = False):
+    """Static int8 quantisation with the caller's fp32 scales (1 value, or H
+    per-channel values) and dispatch.  Returns (recv_x int8 [cap, H], recv_weights)."""
+    T, K, cap = layout.num_tokens, layout.num_topk, layout.recv_capacity
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError(f"x must be [{T}, hidden]")
+    H = x.shape[1]
+    dev = x.device
+    _check(x, "x", torch.bfloat16, device=dev)
+    _check(scales, "scales", torch.float32, device=dev)
+    if scales.numel() not in (1, H):
+        raise ValueError("scales must hold 1 or hidden values")
+    if topk_weights is not None:
+        _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    if recv_x is None:
+        recv_x = torch.empty((cap, H), dtype=torch.int8, device=dev)
+    if recv_weights is None and with_weights:
+        recv_weights = torch.empty(cap, dtype=torch.float32, device=dev)
+    _check(recv_x, "recv_x", torch.int8, (cap, H), dev)
+    if recv_weights is not None:
+        _check(recv_weights, "recv_weights", torch.float32, (cap,), dev)
+    rc = lib().moe_dispatch_static(_ptr(x), T, H, K, _ptr(layout.token_row), _ptr(topk_weights),
+                                   cap, _ptr(scales), scales.numel(), _ptr(recv_x),
+                                   _ptr(recv_weights), _stream(dev))
+    if rc != MOE_OK:
+        raise MoeError("moe_dispatch_static", rc)
+    return recv_x, recv_weights
 
 
 def _bytes2d(t: torch.Tensor, name: str, rows: int, dev) -> torch.Tensor:

@@ -14,6 +14,10 @@
 //   MX        : per 32 elements sharedExp = max(floor(log2 max|x|) - emax, -127)
 //               (emax 8 for e4m3fn, 15 for e5m2), q = cast(x / 2^sharedExp),
 //               e8m0 byte = sharedExp + 127
+//   per-group : the per-token formula applied to each group of 128 elements
+//               (Formula Case 4; FP8 destinations), one fp32 scale per group
+//   static    : q = int8_sat(rint(x * scale)) with the caller's scale(s)
+//               (Formula Case 2: one coefficient or one per channel)
 //   pre-quantised rows (the Normal Mode API page's (data, scale) tuple input):
 //               data row and scale row copied unchanged
 //
@@ -281,6 +285,133 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_mx_kernel(
     write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
 }
 
+// --------------------------------------------------------------------------- per-group dynamic
+
+// A group of 128 elements is 16 lanes x 8 elements; 16-lane groups are
+// aligned inside the wave.  Lanes past the row end hold copies of the row's
+// last vector, which belongs to the row's last (possibly partial) group, so
+// they cannot change any group's maximum.
+template <int VPT, Dst D>
+__global__ __launch_bounds__(kRowMaxThreads) void dispatch_pergroup_kernel(
+    const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
+    const float *__restrict__ topk_weights, int64_t cap, u32x2 *__restrict__ recv,
+    float *__restrict__ recv_scales, float *__restrict__ recv_weights)
+{
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int ngroups = (nvec + 15) / 16;
+    const u32x4 *xt = x + (int64_t)t * nvec;
+    u32x4 xin[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+        xin[j] = xt[min(tid + j * nthr, nvec - 1)]; // clamped: always in bounds
+    u32x2 q[VPT];
+    float gscale[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const u32x4 xv = xin[j];
+        float m = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            m = fmaxf(m, fabsf(bf16_lo(xv[c])));
+            m = fmaxf(m, fabsf(bf16_hi(xv[c])));
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1)
+            m = fmaxf(m, __shfl_xor(m, o, kWave));
+        const float ds = DstTraits<D>::kMax / m; // IEEE division
+        const bool degenerate = !(ds <= 3.402823466e38f);
+        gscale[j] = 1.0f / ds;
+        uint32_t w[2] = {0u, 0u};
+        if (!degenerate) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t lo = DstTraits<D>::code(bf16_lo(xv[c]) * ds, sign_lo(xv[c]));
+                const uint32_t hi = DstTraits<D>::code(bf16_hi(xv[c]) * ds, sign_hi(xv[c]));
+                w[c >> 1] |= (lo | (hi << 8)) << (16 * (c & 1));
+            }
+        }
+        q[j] = u32x2{w[0], w[1]};
+    }
+
+    for (int k = 0; k < K; ++k) {
+        const int row = token_row[(int64_t)t * K + k];
+        if (row < 0 || row >= cap)
+            continue;
+        u32x2 *dst = recv + (int64_t)row * nvec;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int i = tid + j * nthr;
+            if (i < nvec) {
+                __builtin_nontemporal_store(q[j], dst + i);
+                if ((i & 15) == 0)
+                    recv_scales[(int64_t)row * ngroups + (i >> 4)] = gscale[j];
+            }
+        }
+    }
+    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
+}
+
+// --------------------------------------------------------------------------- static int8
+
+template <int VPT>
+__global__ __launch_bounds__(kRowMaxThreads) void dispatch_static_kernel(
+    const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
+    const float *__restrict__ topk_weights, int64_t cap, const float *__restrict__ scales,
+    int per_channel, u32x2 *__restrict__ recv, float *__restrict__ recv_weights)
+{
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const u32x4 *xt = x + (int64_t)t * nvec;
+    const float4 *sc4 = (const float4 *)scales;
+    u32x4 xin[VPT];
+    float4 s_lo[VPT], s_hi[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int i = min(tid + j * nthr, nvec - 1); // clamped: always in bounds
+        xin[j] = xt[i];
+        if (per_channel) { // uniform: the 8 channel scales of this vector
+            s_lo[j] = sc4[2 * i];
+            s_hi[j] = sc4[2 * i + 1];
+        } else {
+            const float s0 = scales[0];
+            s_lo[j] = float4{s0, s0, s0, s0};
+            s_hi[j] = s_lo[j];
+        }
+    }
+    u32x2 q[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const float sv[8] = {s_lo[j].x, s_lo[j].y, s_lo[j].z, s_lo[j].w,
+                             s_hi[j].x, s_hi[j].y, s_hi[j].z, s_hi[j].w};
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // one fp32 multiply, round half to even, saturate to [-128, 127]
+            const float lo = fminf(fmaxf(__builtin_rintf(bf16_lo(xin[j][c]) * sv[2 * c]), -128.0f), 127.0f);
+            const float hi = fminf(fmaxf(__builtin_rintf(bf16_hi(xin[j][c]) * sv[2 * c + 1]), -128.0f), 127.0f);
+            const uint32_t b = ((uint32_t)(int)lo & 0xFFu) | (((uint32_t)(int)hi & 0xFFu) << 8);
+            w[c >> 1] |= b << (16 * (c & 1));
+        }
+        q[j] = u32x2{w[0], w[1]};
+    }
+    for (int k = 0; k < K; ++k) {
+        const int row = token_row[(int64_t)t * K + k];
+        if (row < 0 || row >= cap)
+            continue;
+        u32x2 *dst = recv + (int64_t)row * nvec;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int i = tid + j * nthr;
+            if (i < nvec)
+                __builtin_nontemporal_store(q[j], dst + i);
+        }
+    }
+    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
+}
+
 // --------------------------------------------------------------------------- pre-quantised rows
 
 template <int VPT>
@@ -348,6 +479,14 @@ static hipError_t launch_dispatch_v(dim3 grid, dim3 block, hipStream_t stream, c
         return launch_kernel(dispatch_mx_kernel<V, Dst::E5M2>, grid, block, 0, stream, xv, nvec,
                              K, token_row, topk_weights, cap, (u32x2 *)recv_x,
                              (uint8_t *)recv_scales, recv_weights);
+    case MOE_QUANT_FP8_E4M3_PER_GROUP:
+        return launch_kernel(dispatch_pergroup_kernel<V, Dst::E4M3>, grid, block, 0, stream, xv,
+                             nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x,
+                             (float *)recv_scales, recv_weights);
+    case MOE_QUANT_FP8_E5M2_PER_GROUP:
+        return launch_kernel(dispatch_pergroup_kernel<V, Dst::E5M2>, grid, block, 0, stream, xv,
+                             nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x,
+                             (float *)recv_scales, recv_weights);
     default:
         return hipErrorInvalidValue;
     }
@@ -369,6 +508,27 @@ hipError_t launch_dispatch(const void *x, int T, int H, int K, const int32_t *to
                                     quant_mode, recv_x, recv_scales, recv_weights);
     return launch_dispatch_v<2>(grid, block, stream, xv, nvec, K, token_row, topk_weights, cap,
                                 quant_mode, recv_x, recv_scales, recv_weights);
+}
+
+hipError_t launch_dispatch_static(const void *x, int T, int H, int K, const int32_t *token_row,
+                                  const float *topk_weights, int64_t cap, const float *scales,
+                                  int num_scales, void *recv_x, float *recv_weights,
+                                  hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    const int nvec = H / 8;
+    const int threads = row_block_threads(nvec);
+    const int vpt = (nvec + threads - 1) / threads;
+    const dim3 grid(T), block(threads);
+    const int per_channel = num_scales == H ? 1 : 0;
+    if (vpt == 1)
+        return launch_kernel(dispatch_static_kernel<1>, grid, block, 0, stream, (const u32x4 *)x,
+                             nvec, K, token_row, topk_weights, cap, scales, per_channel,
+                             (u32x2 *)recv_x, recv_weights);
+    return launch_kernel(dispatch_static_kernel<2>, grid, block, 0, stream, (const u32x4 *)x, nvec,
+                         K, token_row, topk_weights, cap, scales, per_channel, (u32x2 *)recv_x,
+                         recv_weights);
 }
 
 hipError_t launch_dispatch_rows(const void *data, int T, int row_bytes, const void *scales,

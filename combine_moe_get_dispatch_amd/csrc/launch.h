@@ -90,6 +90,11 @@ hipError_t launch_dispatch(const void *x, int T, int H, int K, const int32_t *to
                            const float *topk_weights, int64_t cap, int quant_mode, void *recv_x,
                            void *recv_scales, float *recv_weights, hipStream_t stream);
 
+hipError_t launch_dispatch_static(const void *x, int T, int H, int K, const int32_t *token_row,
+                                  const float *topk_weights, int64_t cap, const float *scales,
+                                  int num_scales, void *recv_x, float *recv_weights,
+                                  hipStream_t stream);
+
 hipError_t launch_dispatch_rows(const void *data, int T, int row_bytes, const void *scales,
                                 int scale_bytes, int K, const int32_t *token_row,
                                 const float *topk_weights, int64_t cap, void *recv_data,

@@ -36,15 +36,17 @@ int check_rows_sizes(int T, int H, int K, int64_t cap, int quant_mode)
         return MOE_ERR_INVALID_ARG;
     if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_INT8_PER_TOKEN &&
         quant_mode != MOE_QUANT_MXFP8_E4M3 && quant_mode != MOE_QUANT_FP8_E4M3_PER_TOKEN &&
-        quant_mode != MOE_QUANT_FP8_E5M2_PER_TOKEN && quant_mode != MOE_QUANT_MXFP8_E5M2)
+        quant_mode != MOE_QUANT_FP8_E5M2_PER_TOKEN && quant_mode != MOE_QUANT_MXFP8_E5M2 &&
+        quant_mode != MOE_QUANT_FP8_E4M3_PER_GROUP && quant_mode != MOE_QUANT_FP8_E5M2_PER_GROUP)
         return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
-bool per_token_scale(int quant_mode)
+bool fp32_scales(int quant_mode)
 {
     return quant_mode == MOE_QUANT_INT8_PER_TOKEN || quant_mode == MOE_QUANT_FP8_E4M3_PER_TOKEN ||
-           quant_mode == MOE_QUANT_FP8_E5M2_PER_TOKEN;
+           quant_mode == MOE_QUANT_FP8_E5M2_PER_TOKEN || quant_mode == MOE_QUANT_FP8_E4M3_PER_GROUP ||
+           quant_mode == MOE_QUANT_FP8_E5M2_PER_GROUP;
 }
 
 int check_prequant_sizes(int T, int row_bytes, int scale_bytes, int K, int64_t cap)
@@ -135,12 +137,37 @@ int moe_dispatch(const void *x, int num_tokens, int hidden, int num_topk,
         return MOE_ERR_INVALID_ARG;
     if (quant_mode != MOE_QUANT_NONE && !recv_scales)
         return MOE_ERR_INVALID_ARG;
-    if (per_token_scale(quant_mode) && ((uintptr_t)recv_scales & 3u) != 0)
+    if (fp32_scales(quant_mode) && ((uintptr_t)recv_scales & 3u) != 0)
         return MOE_ERR_INVALID_ARG;
     if (recv_weights && ((uintptr_t)recv_weights & 3u) != 0)
         return MOE_ERR_INVALID_ARG;
     return launch_dispatch(x, T, H, K, token_row, topk_weights, recv_capacity, quant_mode, recv_x,
                            recv_scales, recv_weights, stream) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
+int moe_dispatch_static(const void *x, int num_tokens, int hidden, int num_topk,
+                        const int32_t *token_row, const float *topk_weights,
+                        int64_t recv_capacity, const float *scales, int num_scales, void *recv_x,
+                        float *recv_weights, hipStream_t stream)
+{
+    const int T = num_tokens, H = hidden, K = num_topk;
+    int rc = check_rows_sizes(T, H, K, recv_capacity, MOE_QUANT_NONE);
+    if (rc != MOE_OK)
+        return rc;
+    if (num_scales != 1 && num_scales != H)
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !token_row || !recv_x || !scales || !aligned16(x) || !aligned16(recv_x))
+        return MOE_ERR_INVALID_ARG;
+    if (((uintptr_t)scales & (num_scales == H ? 15u : 3u)) != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (recv_weights && ((uintptr_t)recv_weights & 3u) != 0)
+        return MOE_ERR_INVALID_ARG;
+    return launch_dispatch_static(x, T, H, K, token_row, topk_weights, recv_capacity, scales,
+                                  num_scales, recv_x, recv_weights, stream) == hipSuccess
                ? MOE_OK
                : MOE_ERR_HIP;
 }

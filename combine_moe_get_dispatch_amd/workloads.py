@@ -42,7 +42,10 @@ QUANT_MXFP8_E4M3 = 4
 QUANT_FP8_E4M3_PER_TOKEN = 0x12
 QUANT_FP8_E5M2_PER_TOKEN = 0x22
 QUANT_MXFP8_E5M2 = 0x24
-QUANT_NAMES = {QUANT_NONE: "bf16", QUANT_INT8_PER_TOKEN: "int8 per-token",
+QUANT_FP8_E4M3_PER_GROUP = 0x13
+QUANT_FP8_E5M2_PER_GROUP = 0x23
+QUANT_NAMES = {QUANT_FP8_E4M3_PER_GROUP: "FP8 e4m3 per-group(128)",
+               QUANT_FP8_E5M2_PER_GROUP: "FP8 e5m2 per-group(128)",QUANT_NONE: "bf16", QUANT_INT8_PER_TOKEN: "int8 per-token",
                QUANT_MXFP8_E4M3: "MXFP8 e4m3", QUANT_FP8_E4M3_PER_TOKEN: "FP8 e4m3 per-token",
                QUANT_FP8_E5M2_PER_TOKEN: "FP8 e5m2 per-token", QUANT_MXFP8_E5M2: "MXFP8 e5m2"}
 
@@ -65,11 +68,14 @@ class Workload:
     outlier_scale: float = 1.0
     seed_index: int = 0
     prequant: str = ""              # "" | "mxfp8" | "mxfp4": pre-quantised (data, scale) input
+    static_scale: float = 0.0       # > 0: static int8 quantisation with this one coefficient
 
     def describe(self) -> str:
         q = QUANT_NAMES[self.quant_mode]
         if self.prequant:
             q = f"pre-quantised {self.prequant.upper()} pass-through"
+        if self.static_scale > 0:
+            q = f"static int8 (scale {self.static_scale:g})"
         return (f"{self.num_tokens} tokens x hidden {self.hidden}, "
                 f"{self.num_experts} experts / {self.num_ranks} virtual ranks, "
                 f"top-{self.num_topk} {self.routing}, alignment {self.expert_alignment}, {q}")
@@ -96,6 +102,10 @@ NEXT_WORKLOADS = [
              QUANT_FP8_E5M2_PER_TOKEN, routing="zipf", zipf_s=1.1, x_sigma=2.0, seed_index=2),
     Workload("mxfp8e5m2_8192x4096_e128_top8_drop", 8192, 4096, 128, 8, 8, 32, QUANT_MXFP8_E5M2,
              drop_prob=0.1, outlier_prob=0.01, outlier_scale=50.0, seed_index=3),
+    Workload("fp8e4m3_pergroup_8192x7168_e256_top8_zipf", 8192, 7168, 256, 16, 8, 128,
+             QUANT_FP8_E4M3_PER_GROUP, routing="zipf", zipf_s=1.1, x_sigma=2.0, seed_index=2),
+    Workload("int8_static_8192x7168_e256_top8_zipf", 8192, 7168, 256, 16, 8, 128, QUANT_NONE,
+             routing="zipf", zipf_s=1.1, x_sigma=2.0, seed_index=2, static_scale=127.0 / 12.0),
     Workload("mxfp8_prequant_8192x7168_e256_top8", 8192, 7168, 256, 8, 8, 1, QUANT_NONE,
              seed_index=5, prequant="mxfp8"),
     Workload("mxfp4_prequant_8192x7168_e256_top8", 8192, 7168, 256, 8, 8, 1, QUANT_NONE,

@@ -61,6 +61,12 @@ extern "C" {
 #define MOE_QUANT_FP8_E4M3_PER_TOKEN 0x12 /* e4m3fn rows + fp32 scale per row (Case 3, max 448)  */
 #define MOE_QUANT_FP8_E5M2_PER_TOKEN 0x22 /* e5m2 rows + fp32 scale per row (Case 3, max 57344)  */
 #define MOE_QUANT_MXFP8_E5M2 0x24         /* e5m2 rows + e8m0 byte per 32 elements (Case 5)      */
+#define MOE_QUANT_FP8_E4M3_PER_GROUP 0x13 /* e4m3fn rows + fp32 scale per 128 elements (Case 4) */
+#define MOE_QUANT_FP8_E5M2_PER_GROUP 0x23 /* e5m2 rows + fp32 scale per 128 elements (Case 4)   */
+
+/* Group size of the per-group modes.  The CANN page gives none; its buffer
+ * sizing for per-group quantisation aligns H to 128 (Constraint 9). */
+#define MOE_QUANT_GROUP 128
 
 /* Bits of the device error flag written by moe_get_dispatch_layout. */
 #define MOE_FLAG_BAD_EXPERT_ID 1 /* some topk_idx entry was outside [-1, num_experts) */
@@ -143,6 +149,11 @@ int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_top
  *                             mode with dstTypeMax 448 / 57344 and the product
  *                             cast to e4m3fn / e5m2 (half to even, saturated to
  *                             dstTypeMax); recv_scales[row] = 1.0f / dynamicScales
+ *   MOE_QUANT_FP8_E4M3_PER_GROUP / MOE_QUANT_FP8_E5M2_PER_GROUP: the per-token
+ *                             FP8 formula applied to each group g of 128 elements
+ *                             (the last group holds H % 128 elements when H is not
+ *                             a multiple of 128); recv_scales[row * G + g] =
+ *                             1.0f / dynamicScales_g, G = ceil(H / 128)
  *   MOE_QUANT_MXFP8_E4M3 / MOE_QUANT_MXFP8_E5M2: per 32-element block j:
  *                             sharedExp = max(floor(log2 max|x|) - emax, -127)
  *                             (emax 8 / 15; -127 for a zero block),
@@ -157,6 +168,7 @@ int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_top
  *   moe_get_dispatch_layout; topk_weights fp32 [T, K] or NULL.
  * Outputs (device): recv_x [recv_capacity, H] of bf16 / int8 / fp8;
  *   recv_scales NULL (bf16) / fp32 [recv_capacity] (per-token modes) /
+ *   fp32 [recv_capacity, ceil(H/128)] (per-group modes) /
  *   uint8 [recv_capacity, H/32] (MX modes);
  *   recv_weights fp32 [recv_capacity] or NULL.
  * Sizes: T >= 0, 32 <= H <= 16384 with H % 32 == 0, 1 <= K <= 16,
@@ -168,6 +180,27 @@ int moe_dispatch(const void *x, int num_tokens, int hidden, int num_topk,
                  const int32_t *token_row, const float *topk_weights, int64_t recv_capacity,
                  int quant_mode, void *recv_x, void *recv_scales, float *recv_weights,
                  hipStream_t stream);
+
+/*
+ * Dispatch with static int8 quantisation (CANN page, Formula Case 2, quantMode
+ * 1; Constraint 8: the scales are one quantisation coefficient, shape (1,),
+ * or one smoothing value per channel, shape (H,)).
+ *
+ * For every entry (t, k) with row = token_row[t, k] in [0, recv_capacity):
+ *   recv_x[row, h] = saturate_int8(round_half_even(x[t, h] * scales[h or 0]))
+ * with the product in fp32 and saturation to [-128, 127]; no scales are
+ * written (they are the caller's).  recv_weights as for moe_dispatch.
+ * Inputs (device): x bf16 [T, H]; token_row int32 [T, K]; topk_weights fp32
+ *   [T, K] or NULL; scales fp32 [num_scales], num_scales 1 or H (16-byte
+ *   aligned when H).
+ * Output (device): recv_x int8 [recv_capacity, H].
+ * Sizes and alignment as for moe_dispatch.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP.
+ */
+int moe_dispatch_static(const void *x, int num_tokens, int hidden, int num_topk,
+                        const int32_t *token_row, const float *topk_weights,
+                        int64_t recv_capacity, const float *scales, int num_scales, void *recv_x,
+                        float *recv_weights, hipStream_t stream);
 
 /*
  * Dispatch of pre-quantised tokens (Normal Mode API page, dispatch Parameters

@@ -17,8 +17,9 @@ if not os.path.exists(moe.LIB_PATH):      # build only when nothing is built
 DEV = torch.device("cuda", 0)
 
 PER_TOKEN = (2, 0x12, 0x22)
+PER_GROUP = (0x13, 0x23)
 MX = (4, 0x24)
-E5M2 = (0x22, 0x24)
+E5M2 = (0x22, 0x24, 0x23)
 
 
 def sentinel(quant):
@@ -26,7 +27,7 @@ def sentinel(quant):
 
 
 def scale_sentinel(quant):
-    return -7.0 if quant in PER_TOKEN else 0xFF
+    return -7.0 if quant in PER_TOKEN + PER_GROUP else 0xFF
 
 
 def bf16_dev(bits: np.ndarray) -> torch.Tensor:
@@ -82,6 +83,8 @@ def oracle_poisoned(cap, H, quant):
     rx = np.full((cap, H), sentinel(quant), np.int8 if quant == 2 else np.uint8)
     if quant in PER_TOKEN:
         rs = np.full(cap, scale_sentinel(quant), np.float32)
+    elif quant in PER_GROUP:
+        rs = np.full((cap, (H + 127) // 128), scale_sentinel(quant), np.float32)
     else:
         rs = np.full((cap, H // 32), scale_sentinel(quant), np.uint8)
     return rx, rs
@@ -107,6 +110,10 @@ def dequant_identity_expert(rx_host: np.ndarray, rs_host, quant: int) -> np.ndar
         codes = torch.from_numpy(rx_host).view(fp8).float()
     if quant in PER_TOKEN:
         y = codes * torch.from_numpy(rs_host)[:, None]
+    elif quant in PER_GROUP:
+        cap, H = rx_host.shape
+        per_elem = torch.from_numpy(rs_host).repeat_interleave(128, dim=1)[:, :H]
+        y = codes * per_elem
     else:
         cap, H = rx_host.shape
         sc = torch.from_numpy(rs_host.astype(np.float32) - 127.0)

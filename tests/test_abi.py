@@ -125,7 +125,7 @@ def test_dispatch_pointer_rules(L):
     assert L.moe_combine(None, 100, 0, 64, 2, None, None, None, None) == 0
 
 
-@pytest.mark.parametrize("q", [0x14, 0x32, 0x42, 0x23, 6])
+@pytest.mark.parametrize("q", [0x14, 0x32, 0x42, 0x33, 6])
 def test_unknown_quant_modes_rejected(L, orc, q):
     assert orc.check_rows_args(16, 1024, 4, 1000, q) == -1
     assert L.moe_dispatch(BAD, 16, 1024, 4, BAD, BAD, 1000, q, BAD, BAD, BAD, None) == -1
@@ -150,3 +150,18 @@ def test_prequantized_pointer_rules(L):
     assert f(BAD, 4, 64, None, 2, 2, BAD, None, 100, BAD, BAD, None, None) == -1
     assert f(BAD, 4, 64, BAD, 2, 2, BAD, None, 100, BAD, None, None, None) == -1
     assert f(None, 0, 64, None, 2, 2, None, None, 100, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("n", [0, 2, 1023, 1025])
+def test_static_rejects_like_the_oracle(L, orc, n):
+    expect = orc.check_static_args(16, 1024, 4, 1000, n)
+    assert expect == -1
+    assert L.moe_dispatch_static(BAD, 16, 1024, 4, BAD, None, 1000, BAD, n, BAD, None, None) == -1
+
+
+def test_static_pointer_rules(L):
+    f = L.moe_dispatch_static
+    assert f(BAD, 16, 1024, 4, BAD, None, 1000, None, 1, BAD, None, None) == -1
+    assert f(BAD, 16, 1024, 4, BAD, None, 1000, ctypes.c_void_p(0x1004), 1024, BAD, None, None) == -1
+    assert f(BAD, 16, 48, 4, BAD, None, 1000, BAD, 1, BAD, None, None) == -1
+    assert f(None, 0, 1024, 4, None, None, 1000, None, 1, None, None, None) == 0

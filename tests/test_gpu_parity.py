@@ -137,6 +137,10 @@ EDGE = [
     ("mxfp8_e5m2", 700, 4096, 128, 8, 8, 32, 0x24, False, 0.1),
     ("mxfp8_e5m2_max_hidden", 40, 16384, 128, 8, 8, 32, 0x24, False, 0.0),
     ("fp8_e4m3_per_token_h96", 257, 96, 8, 2, 3, 1, 0x12, False, 0.1),
+    ("fp8_e4m3_per_group", 700, 7168, 64, 8, 8, 16, 0x13, False, 0.05),
+    ("fp8_e5m2_per_group", 700, 4096, 64, 8, 8, 16, 0x23, True, 0.05),
+    ("fp8_e4m3_per_group_partial", 300, 160, 16, 4, 4, 8, 0x13, False, 0.1),
+    ("fp8_e5m2_per_group_max_hidden", 40, 16384, 128, 8, 8, 32, 0x23, False, 0.0),
 ]
 
 
@@ -200,7 +204,7 @@ def test_quant_special_rows():
     T = x.shape[0]
     idx = np.stack([np.arange(T) % E, (np.arange(T) + 1) % E], axis=1).astype(np.int64)
     wts = np.full((T, K), 0.5, np.float32)
-    for quant in (2, 4, 0x12, 0x22, 0x24):
+    for quant in (2, 4, 0x12, 0x22, 0x24, 0x13, 0x23):
         run_full_case(x, idx, wts, E, 2, 1, quant, north_star=False)
 
 
@@ -340,5 +344,32 @@ def test_dispatch_prequantized_parity(fmt):
     np.testing.assert_array_equal(rd.view(torch.uint8).cpu().numpy(), ord_)
     if sc is not None:
         np.testing.assert_array_equal(rs.cpu().numpy(), ors)
+    used = ol.recv_src >= 0
+    np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_dispatch_static_parity(per_channel):
+    """Static int8 (caller scales, saturating): whole receive buffers equal
+    the oracle's, sentinels included."""
+    rng = np.random.default_rng(77 + per_channel)
+    T, H, K, E, R, a = 600, 7168, 8, 64, 8, 4
+    idx, wts = _routing(rng, T, K, E, drop=0.05)
+    x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    if per_channel:
+        scales = rng.uniform(10.0, 80.0, H).astype(np.float32)
+    else:
+        scales = np.array([45.0], np.float32)
+    ol = oracle.layout(idx, E, R, a)
+    cap = ol.recv_capacity
+    orx, orw = oracle.dispatch_static(x_bits, ol.token_row, cap, scales, wts,
+                                      recv_x=np.full((cap, H), 0x55, np.int8), with_weights=True)
+    assert (orx == 127).any() and (orx == -128).any()        # saturation exercised
+    lay = gpu_layout(idx, E, R, a)
+    rx = torch.full((cap, H), 0x55, dtype=torch.int8, device=DEV)
+    rw = torch.full((cap,), -3.0, device=DEV)
+    moe.moe_dispatch_static(bf16_dev(x_bits), lay, torch.from_numpy(scales).to(DEV),
+                            torch.from_numpy(wts).to(DEV), recv_x=rx, recv_weights=rw)
+    np.testing.assert_array_equal(rx.cpu().numpy(), orx)
     used = ol.recv_src >= 0
     np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
