@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_quant_fp8_pergroup_rows.restype = None
         L.oracle_quant_static_int8_rows.argtypes = [_P, i32, i32, _P, i32, _P]
         L.oracle_quant_static_int8_rows.restype = None
+        L.oracle_combine_fused.argtypes = [_P, i64, i32, i32, i32, _P, _P, _P, _P, _P,
+                                           ctypes.c_double, _P, _P]
+        L.oracle_combine_fused.restype = i32
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = i32
         _lib = L
@@ -271,6 +274,26 @@ def combine(y_bits: np.ndarray, token_row: np.ndarray, topk_weights: np.ndarray 
     if rc != OK:
         raise OracleError(rc)
     return out
+
+
+def combine_fused(y_bits, token_row, topk_weights=None, shared=None, residual=None, gamma=None,
+                  eps: float = 1e-6, with_norm: bool = False):
+    """fp64 (out, norm): out = weighted sum + shared + residual; norm = RMSNorm(out) * gamma."""
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    cap, H = y.shape
+    row = np.ascontiguousarray(token_row, dtype=np.int32)
+    T, K = row.shape
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    sh = None if shared is None else np.ascontiguousarray(shared, dtype=np.uint16)
+    rs = None if residual is None else np.ascontiguousarray(residual, dtype=np.uint16)
+    g = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.uint16)
+    out = np.zeros((T, H), np.float64)
+    norm = np.zeros((T, H), np.float64) if with_norm else None
+    rc = lib().oracle_combine_fused(_ptr(y), cap, T, H, K, _ptr(row), _ptr(w), _ptr(sh), _ptr(rs),
+                                    _ptr(g), float(eps), _ptr(out), _ptr(norm))
+    if rc != OK:
+        raise OracleError(rc)
+    return out, norm
 
 
 def cast_to_fp8_e4m3fn(v: np.ndarray) -> np.ndarray:

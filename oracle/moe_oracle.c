@@ -732,6 +732,49 @@ int oracle_combine(const uint16_t *y, int64_t cap, int T, int H, int K, const in
     return ORC_OK;
 }
 
+/*
+ * Combine with the epilogues the pages name ([EPBM] ep_combine(): in fused
+ * shared-expert mode the shared expert's outputs are added to the reduced
+ * routed outputs; [CANN] Description names aclnnMoeDistributeCombineAddRmsNorm,
+ * a combine followed by a residual add and an RMS normalisation).  Reading:
+ *   s[t, h]    = sum_k w[t,k] * y[row(t,k), h]  +  shared[t, h]  +  residual[t, h]
+ *   out[t, h]  = s[t, h]
+ *   norm[t, h] = s[t, h] / sqrt(mean_h(s[t, :]^2) + eps) * gamma[h]
+ * with shared, residual and gamma optional (NULL: absent / no
+ * normalisation).  shared, residual: bf16 bits [T, H]; gamma: bf16 bits [H];
+ * out, norm: double [T, H] (norm may be NULL).  All in fp64.
+ */
+int oracle_combine_fused(const uint16_t *y, int64_t cap, int T, int H, int K,
+                         const int32_t *token_row, const float *topk_weights,
+                         const uint16_t *shared, const uint16_t *residual, const uint16_t *gamma,
+                         double eps, double *out, double *norm)
+{
+    int rc = oracle_combine(y, cap, T, H, K, token_row, topk_weights, out);
+    if (rc != ORC_OK)
+        return rc;
+    if (norm && (!gamma || !(eps >= 0.0)))
+        return ORC_ERR_INVALID_ARG;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        double *o = out + (int64_t)t * H;
+        for (int h = 0; h < H; ++h) {
+            if (shared)
+                o[h] += (double)bf16_to_f32(shared[(int64_t)t * H + h]);
+            if (residual)
+                o[h] += (double)bf16_to_f32(residual[(int64_t)t * H + h]);
+        }
+        if (norm) {
+            double ss = 0.0;
+            for (int h = 0; h < H; ++h)
+                ss += o[h] * o[h];
+            const double rms = sqrt(ss / H + eps);
+            for (int h = 0; h < H; ++h)
+                norm[(int64_t)t * H + h] = o[h] / rms * (double)bf16_to_f32(gamma[h]);
+        }
+    }
+    return ORC_OK;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
