@@ -62,7 +62,7 @@ PER_TOKEN_MODES = (0x02, 0x12, 0x22)
 PER_GROUP_MODES = (0x13, 0x23)
 
 
-def stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows=None, static=False):
+def stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows=None, static=False, epilogue=False):
     """Algorithmic bytes of each stage (see module docstring).  prequant_rows =
     (data bytes, scale bytes) per token for the pre-quantised pass-through."""
     layout = 8 * T * K + 4 * T * R + 4 * R + 8 * E + 4 * (E + 1) + 4 * T * K + 4 * cap + 4
@@ -83,6 +83,8 @@ def stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows=None, static=False):
             sigma = H // 32
         dispatch = 2 * T * H + 4 * T * K + V * (H * s_q + sigma)
     combine = 2 * V * H + 8 * T * K + 2 * T * H
+    if epilogue:   # shared row + residual row read, normalised row written, gamma read
+        combine += 3 * 2 * T * H + 2 * H
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
 
 
@@ -173,6 +175,10 @@ def cpu_baseline(inp, w, quant, budget_s, bytes_fn, prequant=None):
     import numpy as np
     import oracle
     E, R, a = w.num_experts, w.num_ranks, w.expert_alignment
+    if w.epilogue:
+        from combine_moe_get_dispatch_amd import workloads as W
+        epi = (W.random_bf16_rows(w.num_tokens, w.hidden, 21), W.random_bf16_rows(w.num_tokens, w.hidden, 22),
+               np.full(w.hidden, 0x3F80, np.uint16))
     reps, total_bytes = 0, 0
     t0 = time.perf_counter()
     while True:
@@ -187,7 +193,11 @@ def cpu_baseline(inp, w, quant, budget_s, bytes_fn, prequant=None):
         else:
             rx, rs, _ = oracle.dispatch(inp.x_bits, ol.token_row, ol.recv_capacity, None, quant)
             y = rx if quant == 0 else np.zeros((ol.recv_capacity, w.hidden), np.uint16)
-        oracle.combine(y, ol.token_row, inp.topk_weights)
+        if w.epilogue:
+            oracle.combine_fused(y, ol.token_row, inp.topk_weights, epi[0], epi[1], epi[2], 1e-6,
+                                 with_norm=True)
+        else:
+            oracle.combine(y, ol.token_row, inp.topk_weights)
         reps += 1
         V = int((inp.topk_idx >= 0).sum())
         total_bytes += sum(bytes_fn(V, ol.recv_capacity).values())
@@ -279,6 +289,18 @@ def main():
             y = torch.nan_to_num(y, nan=0.0, posinf=0.0, neginf=0.0).to(torch.bfloat16)
     torch.cuda.synchronize()
 
+    if w.epilogue:
+        shared = torch.from_numpy(W.random_bf16_rows(T, H, 21).view(np.int16)).to(dev).view(torch.bfloat16)
+        residual = torch.from_numpy(W.random_bf16_rows(T, H, 22).view(np.int16)).to(dev).view(torch.bfloat16)
+        gamma = torch.ones(H, dtype=torch.bfloat16, device=dev)
+        out_norm = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+        def run_combine():
+            moe.moe_combine_fused(y, lay, wt, shared, residual, gamma, 1e-6, out=out, out_norm=out_norm)
+    else:
+        def run_combine():
+            moe.moe_combine(y, lay, wt, out=out)
+
     timer = StageEvents(torch)
 
     def step(ev=None):
@@ -290,7 +312,7 @@ def main():
         run_dispatch()
         if ev is not None:
             timer.record(ev[2])
-        moe.moe_combine(y, lay, wt, out=out)
+        run_combine()
         if ev is not None:
             timer.record(ev[3])
 
@@ -317,7 +339,8 @@ def main():
     avg_us = {k: float(np.mean(v)) for k, v in st.items()}
     med_us = {k: float(np.median(v)) for k, v in st.items()}
 
-    sb = stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows, w.static_scale > 0)
+    sb = stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows, w.static_scale > 0,
+                     bool(w.epilogue))
     step_bytes = sum(sb.values())
     ms_per_step = elapsed / args.steps * 1e3
     gbs = step_bytes * args.steps / elapsed / 1e9
@@ -348,7 +371,7 @@ def main():
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(inp, w, quant, args.cpu_seconds,
                            lambda v, c: stage_bytes(T, H, K, R, E, v, c, quant, prequant_rows,
-                                                    w.static_scale > 0),
+                                                    w.static_scale > 0, bool(w.epilogue)),
                            prequant=cpu_y)
 
     qname = {0: "bf16", 2: "int8", 4: "mxfp8_e4m3", 0x12: "fp8_e4m3_per_token",

@@ -48,7 +48,7 @@ FLAG_BAD_EXPERT_ID = 1
 
 __all__ = [
     "moe_get_dispatch_layout", "moe_dispatch", "moe_dispatch_static", "moe_dispatch_prequantized",
-    "moe_combine",
+    "moe_combine", "moe_combine_fused",
     "moe_recv_capacity_bound",
     "moe_layout_workspace_bytes", "DispatchLayout", "allocate_layout", "allocate_recv",
     "num_recv_tokens_per_expert_list", "MoeError", "lib",
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch_prequantized.restype = i32
         L.moe_combine.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
         L.moe_combine.restype = i32
+        L.moe_combine_fused.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, P, P, P]
+        L.moe_combine_fused.restype = i32
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -368,3 +370,44 @@ def moe_combine(expert_out: torch.Tensor, layout: DispatchLayout,
     if rc != MOE_OK:
         raise MoeError("moe_combine", rc)
     return out
+
+
+def moe_combine_fused(expert_out: torch.Tensor, layout: DispatchLayout,
+                      topk_weights: Optional[torch.Tensor] = None,
+                      shared_out: Optional[torch.Tensor] = None,
+                      residual: Optional[torch.Tensor] = None,
+                      rms_weight: Optional[torch.Tensor] = None, rms_eps: float = 1e-6,
+                      out: Optional[torch.Tensor] = None, out_norm: Optional[torch.Tensor] = None,
+                      with_norm: bool = False):
+    """Combine plus epilogues: out = sum_k w y (+ shared_out) (+ residual);
+    out_norm = RMSNorm(out) * rms_weight when rms_weight is given.
+    Returns (out, out_norm)."""
+    T, K, cap = layout.num_tokens, layout.num_topk, layout.recv_capacity
+    if expert_out.dim() != 2 or expert_out.shape[0] != cap:
+        raise ValueError(f"expert_out must be [{cap}, hidden]")
+    H = expert_out.shape[1]
+    dev = expert_out.device
+    _check(expert_out, "expert_out", torch.bfloat16, device=dev)
+    if topk_weights is not None:
+        _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    for name, t_ in (("shared_out", shared_out), ("residual", residual)):
+        if t_ is not None:
+            _check(t_, name, torch.bfloat16, (T, H), dev)
+    want_norm = with_norm or out_norm is not None
+    if want_norm:
+        if rms_weight is None:
+            raise ValueError("rms_weight is required for the normalised output")
+        _check(rms_weight, "rms_weight", torch.bfloat16, (H,), dev)
+        if out_norm is None:
+            out_norm = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        _check(out_norm, "out_norm", torch.bfloat16, (T, H), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, H), dev)
+    rc = lib().moe_combine_fused(_ptr(expert_out), cap, T, H, K, _ptr(layout.token_row),
+                                 _ptr(topk_weights), _ptr(shared_out), _ptr(residual),
+                                 _ptr(rms_weight if want_norm else None), float(rms_eps), _ptr(out),
+                                 _ptr(out_norm if want_norm else None), _stream(dev))
+    if rc != MOE_OK:
+        raise MoeError("moe_combine_fused", rc)
+    return out, out_norm

@@ -16,6 +16,16 @@
 // over the receive buffer, but each load instruction of a wave reads 1 KiB
 // contiguous bytes of one row.  Row indices and weights are uniform per
 // workgroup and live in scalar registers.
+//
+// combine_fused_kernel adds the epilogues named by the pages (EPBatchManager
+// page, ep_combine(): shared expert outputs added to the reduced routed
+// outputs; CANN page: the CombineAddRmsNorm companion): the shared-expert row
+// and the residual row of the token are loaded with the expert rows and
+// added to the fp32 sum, which is stored, and optionally normalised,
+//   norm = s / sqrt(mean(s^2) + eps) * gamma,
+// from the fp32 values (sum of squares: per lane, then wave shuffles, then
+// the waves in order through LDS -- a fixed order, so results are
+// deterministic).  This saves a full [T, H] read and write per epilogue.
 #include "device_common.h"
 #include "launch.h"
 
@@ -74,6 +84,110 @@ __global__ __launch_bounds__(kRowMaxThreads) void combine_kernel(
     }
 }
 
+template <int VPT, int KMAX>
+__global__ __launch_bounds__(kRowMaxThreads) void combine_fused_kernel(
+    const u32x4 *__restrict__ y, int nvec, int K, const int32_t *__restrict__ token_row,
+    const float *__restrict__ topk_weights, int64_t cap, const u32x4 *__restrict__ shared,
+    const u32x4 *__restrict__ residual, const u32x4 *__restrict__ gamma, float eps,
+    u32x4 *__restrict__ out, u32x4 *__restrict__ out_norm)
+{
+    __shared__ float s_ss[kRowMaxThreads / kWave];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    int rows[KMAX];
+    float wts[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        rows[k] = -1;
+        wts[k] = 0.0f;
+        if (k < K) {
+            const int r = token_row[(int64_t)t * K + k];
+            rows[k] = (r >= 0 && r < cap) ? r : -1;
+            wts[k] = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;
+        }
+    }
+    float acc[VPT][8];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int i = min(tid + j * nthr, nvec - 1); // clamped: always in bounds
+        u32x4 yv[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (rows[k] >= 0)
+                yv[k] = __builtin_nontemporal_load(y + (int64_t)rows[k] * nvec + i);
+        u32x4 sv = u32x4{0u, 0u, 0u, 0u}, rv = u32x4{0u, 0u, 0u, 0u};
+        if (shared)
+            sv = shared[(int64_t)t * nvec + i];
+        if (residual)
+            rv = residual[(int64_t)t * nvec + i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[j][e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (rows[k] < 0)
+                continue;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc[j][2 * c] = __builtin_fmaf(wts[k], bf16_lo(yv[k][c]), acc[j][2 * c]);
+                acc[j][2 * c + 1] = __builtin_fmaf(wts[k], bf16_hi(yv[k][c]), acc[j][2 * c + 1]);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (shared) {
+                acc[j][2 * c] += bf16_lo(sv[c]);
+                acc[j][2 * c + 1] += bf16_hi(sv[c]);
+            }
+            if (residual) {
+                acc[j][2 * c] += bf16_lo(rv[c]);
+                acc[j][2 * c + 1] += bf16_hi(rv[c]);
+            }
+        }
+        if (tid + j * nthr < nvec) {
+            u32x4 o;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                o[c] = pack_bf16x2(acc[j][2 * c], acc[j][2 * c + 1]);
+            out[(int64_t)t * nvec + tid + j * nthr] = o;
+        }
+    }
+    if (!out_norm)
+        return;
+
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+        if (tid + j * nthr < nvec)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ss = __builtin_fmaf(acc[j][e], acc[j][e], ss);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        ss += __shfl_xor(ss, o, kWave);
+    if ((tid & (kWave - 1)) == 0)
+        s_ss[tid / kWave] = ss;
+    __syncthreads();
+    float total = 0.0f;
+    for (int w = 0; w < nthr / kWave; ++w)
+        total += s_ss[w];
+    const float inv = 1.0f / sqrtf(total / (float)(nvec * 8) + eps);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int i = tid + j * nthr;
+        if (i < nvec) {
+            const u32x4 g = gamma[i];
+            u32x4 o;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                o[c] = pack_bf16x2(acc[j][2 * c] * inv * bf16_lo(g[c]),
+                                   acc[j][2 * c + 1] * inv * bf16_hi(g[c]));
+            out_norm[(int64_t)t * nvec + i] = o;
+        }
+    }
+}
+
 template <int VPT>
 static hipError_t launch_combine_k(int kmax, dim3 grid, dim3 block, hipStream_t stream,
                                    const u32x4 *y, int nvec, int K, const int32_t *token_row,
@@ -109,6 +223,47 @@ hipError_t launch_combine(const void *y, int64_t cap, int T, int H, int K,
     if (vpt == 1)
         return launch_combine_k<1>(kmax, grid, block, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
     return launch_combine_k<2>(kmax, grid, block, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
+}
+
+template <int VPT>
+static hipError_t launch_fused_k(int kmax, dim3 grid, dim3 block, hipStream_t stream,
+                                 const u32x4 *y, int nvec, int K, const int32_t *token_row,
+                                 const float *w, int64_t cap, const u32x4 *sh, const u32x4 *res,
+                                 const u32x4 *g, float eps, u32x4 *out, u32x4 *norm)
+{
+    switch (kmax) {
+    case 1:
+        return launch_kernel(combine_fused_kernel<VPT, 1>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, sh, res, g, eps, out, norm);
+    case 2:
+        return launch_kernel(combine_fused_kernel<VPT, 2>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, sh, res, g, eps, out, norm);
+    case 4:
+        return launch_kernel(combine_fused_kernel<VPT, 4>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, sh, res, g, eps, out, norm);
+    case 8:
+        return launch_kernel(combine_fused_kernel<VPT, 8>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, sh, res, g, eps, out, norm);
+    default:
+        return launch_kernel(combine_fused_kernel<VPT, 16>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, sh, res, g, eps, out, norm);
+    }
+}
+
+hipError_t launch_combine_fused(const void *y, int64_t cap, int T, int H, int K,
+                                const int32_t *token_row, const float *topk_weights,
+                                const void *shared, const void *residual, const void *gamma,
+                                float eps, void *out, void *out_norm, hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    const int nvec = H / 8;
+    const int threads = row_block_threads(nvec);
+    const int vpt = (nvec + threads - 1) / threads;
+    const int kmax = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : 16;
+    const dim3 grid(T), block(threads);
+    if (vpt == 1)
+        return launch_fused_k<1>(kmax, grid, block, stream, (const u32x4 *)y, nvec, K, token_row,
+                                 topk_weights, cap, (const u32x4 *)shared, (const u32x4 *)residual,
+                                 (const u32x4 *)gamma, eps, (u32x4 *)out, (u32x4 *)out_norm);
+    return launch_fused_k<2>(kmax, grid, block, stream, (const u32x4 *)y, nvec, K, token_row,
+                             topk_weights, cap, (const u32x4 *)shared, (const u32x4 *)residual,
+                             (const u32x4 *)gamma, eps, (u32x4 *)out, (u32x4 *)out_norm);
 }
 
 } // namespace moe

@@ -104,4 +104,9 @@ hipError_t launch_combine(const void *y, int64_t cap, int T, int H, int K,
                           const int32_t *token_row, const float *topk_weights, void *out,
                           hipStream_t stream);
 
+hipError_t launch_combine_fused(const void *y, int64_t cap, int T, int H, int K,
+                                const int32_t *token_row, const float *topk_weights,
+                                const void *shared, const void *residual, const void *gamma,
+                                float eps, void *out, void *out_norm, hipStream_t stream);
+
 } // namespace moe

@@ -9,6 +9,7 @@
 #include "../../include/moe_dispatch_combine.h"
 
 #include <climits>
+#include <cmath>
 
 using namespace moe;
 
@@ -212,6 +213,32 @@ int moe_combine(const void *expert_out, int64_t recv_capacity, int num_tokens, i
         return MOE_ERR_INVALID_ARG;
     return launch_combine(expert_out, recv_capacity, T, H, K, token_row, topk_weights, out,
                           stream) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
+int moe_combine_fused(const void *expert_out, int64_t recv_capacity, int num_tokens, int hidden,
+                      int num_topk, const int32_t *token_row, const float *topk_weights,
+                      const void *shared_out, const void *residual, const void *rms_weight,
+                      float rms_eps, void *out, void *out_norm, hipStream_t stream)
+{
+    const int T = num_tokens, H = hidden, K = num_topk;
+    int rc = check_rows_sizes(T, H, K, recv_capacity, MOE_QUANT_NONE);
+    if (rc != MOE_OK)
+        return rc;
+    if (out_norm && (!rms_weight || !std::isfinite(rms_eps) || rms_eps < 0.0f))
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!token_row || !out || !aligned16(out) || !aligned16(expert_out) ||
+        !aligned16(shared_out) || !aligned16(residual) || !aligned16(rms_weight) ||
+        !aligned16(out_norm))
+        return MOE_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && !expert_out)
+        return MOE_ERR_INVALID_ARG;
+    return launch_combine_fused(expert_out, recv_capacity, T, H, K, token_row, topk_weights,
+                                shared_out, residual, rms_weight, rms_eps, out, out_norm,
+                                stream) == hipSuccess
                ? MOE_OK
                : MOE_ERR_HIP;
 }

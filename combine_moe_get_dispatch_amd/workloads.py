@@ -69,6 +69,7 @@ class Workload:
     seed_index: int = 0
     prequant: str = ""              # "" | "mxfp8" | "mxfp4": pre-quantised (data, scale) input
     static_scale: float = 0.0       # > 0: static int8 quantisation with this one coefficient
+    epilogue: str = ""              # "" | "shared_residual_rmsnorm": combine epilogues
 
     def describe(self) -> str:
         q = QUANT_NAMES[self.quant_mode]
@@ -76,6 +77,8 @@ class Workload:
             q = f"pre-quantised {self.prequant.upper()} pass-through"
         if self.static_scale > 0:
             q = f"static int8 (scale {self.static_scale:g})"
+        if self.epilogue:
+            q += ", combine + shared expert + residual + RMSNorm"
         return (f"{self.num_tokens} tokens x hidden {self.hidden}, "
                 f"{self.num_experts} experts / {self.num_ranks} virtual ranks, "
                 f"top-{self.num_topk} {self.routing}, alignment {self.expert_alignment}, {q}")
@@ -102,6 +105,8 @@ NEXT_WORKLOADS = [
              QUANT_FP8_E5M2_PER_TOKEN, routing="zipf", zipf_s=1.1, x_sigma=2.0, seed_index=2),
     Workload("mxfp8e5m2_8192x4096_e128_top8_drop", 8192, 4096, 128, 8, 8, 32, QUANT_MXFP8_E5M2,
              drop_prob=0.1, outlier_prob=0.01, outlier_scale=50.0, seed_index=3),
+    Workload("bf16_4096x7168_e256_top8_shared_addrmsnorm", 4096, 7168, 256, 8, 8, 1, QUANT_NONE,
+             seed_index=1, epilogue="shared_residual_rmsnorm"),
     Workload("fp8e4m3_pergroup_8192x7168_e256_top8_zipf", 8192, 7168, 256, 16, 8, 128,
              QUANT_FP8_E4M3_PER_GROUP, routing="zipf", zipf_s=1.1, x_sigma=2.0, seed_index=2),
     Workload("int8_static_8192x7168_e256_top8_zipf", 8192, 7168, 256, 16, 8, 128, QUANT_NONE,

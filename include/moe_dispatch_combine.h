@@ -244,6 +244,34 @@ int moe_combine(const void *expert_out, int64_t recv_capacity, int num_tokens, i
                 int num_topk, const int32_t *token_row, const float *topk_weights, void *out,
                 hipStream_t stream);
 
+/*
+ * Combine with epilogues (EPBatchManager page, ep_combine(): in fused
+ * shared-expert mode the shared expert's outputs are added to the reduced
+ * routed outputs; CANN page: the aclnnMoeDistributeCombineAddRmsNorm
+ * companion of dispatch, a combine followed by a residual add and an RMS
+ * normalisation).
+ *
+ *   s[t, :]        = sum_k w[t, k] * expert_out[token_row[t, k], :]     (as moe_combine)
+ *                    + shared_out[t, :]  (if not NULL)  + residual[t, :]  (if not NULL)
+ *   out[t, :]      = bf16(s[t, :])
+ *   out_norm[t, :] = bf16(s[t, :] / sqrt(mean(s[t, :]^2) + rms_eps) * rms_weight[:])
+ *                    (only if out_norm is not NULL)
+ * All in fp32 from the fp32 sum (the fma chain of moe_combine, then the
+ * shared and residual adds in that order); the sum of squares is reduced in
+ * a fixed order.  A caller whose buffer holds the shared expert's rows first
+ * ([T rows of shared output][routed rows], as the EPBatchManager page
+ * describes) passes shared_out = that buffer and expert_out = buffer + T rows.
+ * Inputs (device): as moe_combine, plus shared_out / residual bf16 [T, H] or
+ *   NULL, rms_weight bf16 [H] (required with out_norm).
+ * Outputs (device): out bf16 [T, H]; out_norm bf16 [T, H] or NULL.
+ * rms_eps: finite and >= 0.  All row buffers 16-byte aligned.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP.
+ */
+int moe_combine_fused(const void *expert_out, int64_t recv_capacity, int num_tokens, int hidden,
+                      int num_topk, const int32_t *token_row, const float *topk_weights,
+                      const void *shared_out, const void *residual, const void *rms_weight,
+                      float rms_eps, void *out, void *out_norm, hipStream_t stream);
+
 /* Static text for a status code. */
 const char *moe_status_string(int status);
 

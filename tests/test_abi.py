@@ -165,3 +165,14 @@ def test_static_pointer_rules(L):
     assert f(BAD, 16, 1024, 4, BAD, None, 1000, ctypes.c_void_p(0x1004), 1024, BAD, None, None) == -1
     assert f(BAD, 16, 48, 4, BAD, None, 1000, BAD, 1, BAD, None, None) == -1
     assert f(None, 0, 1024, 4, None, None, 1000, None, 1, None, None, None) == 0
+
+
+def test_combine_fused_rules(L):
+    f = L.moe_combine_fused
+    assert f(BAD, 1000, 16, 48, 4, BAD, None, None, None, None, 1e-6, BAD, None, None) == -1
+    assert f(BAD, 1000, 16, 64, 4, BAD, None, None, None, None, 1e-6, BAD, BAD, None) == -1      # norm without gamma
+    assert f(BAD, 1000, 16, 64, 4, BAD, None, None, None, BAD, -1.0, BAD, BAD, None) == -1       # eps < 0
+    assert f(BAD, 1000, 16, 64, 4, BAD, None, None, None, BAD, float("nan"), BAD, BAD, None) == -1
+    assert f(BAD, 1000, 16, 64, 4, BAD, None, ctypes.c_void_p(0x1002), None, None, 0.0, BAD, None, None) == -1
+    assert f(BAD, 1000, 16, 64, 4, None, None, None, None, None, 0.0, BAD, None, None) == -1
+    assert f(None, 1000, 0, 64, 4, None, None, None, None, None, 0.0, None, None, None) == 0

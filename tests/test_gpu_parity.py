@@ -373,3 +373,41 @@ def test_dispatch_static_parity(per_channel):
     np.testing.assert_array_equal(rx.cpu().numpy(), orx)
     used = ol.recv_src >= 0
     np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
+
+
+@pytest.mark.parametrize("variant", ["shared", "residual", "shared_residual_norm", "norm_only",
+                                     "norm_h16384_k16"])
+def test_combine_fused_parity(variant):
+    """Combine epilogues against the fp64 oracle.  Sum: the combine bound with
+    the two extra terms.  Normalised output: one bf16 rounding (2^-9,
+    doubled) plus 2e-4 relative for the fp32 sum of squares and the
+    reciprocal square root, plus the sum's own error scaled by gamma / rms."""
+    rng = np.random.default_rng(zlib.crc32(variant.encode()))
+    T, H, K, E = (64, 16384, 16, 64) if variant == "norm_h16384_k16" else (900, 7168, 8, 64)
+    idx, wts = _routing(rng, T, K, E, drop=0.05)
+    wts = rng.standard_normal((T, K)).astype(np.float32)
+    ol = oracle.layout(idx, E, 8, 4)
+    lay = gpu_layout(idx, E, 8, 4)
+    y = W.random_bf16_rows(ol.recv_capacity, H, 11)
+    sh = W.random_bf16_rows(T, H, 12) if "shared" in variant else None
+    res = W.random_bf16_rows(T, H, 13, sigma=2.0) if "residual" in variant else None
+    norm = "norm" in variant
+    gamma = W.f32_to_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32)) if norm else None
+    eps = 1e-5
+    dv = lambda a: None if a is None else bf16_dev(a)
+    out, out_norm = moe.moe_combine_fused(bf16_dev(y), lay, torch.from_numpy(wts).to(DEV), dv(sh),
+                                          dv(res), dv(gamma), eps, with_norm=norm)
+    ro, rn = oracle.combine_fused(y, ol.token_row, wts, sh, res, gamma, eps, with_norm=norm)
+    absb = lambda a: None if a is None else (a & np.uint16(0x7FFF)).astype(np.uint16)
+    S, _ = oracle.combine_fused(absb(y), ol.token_row, np.abs(wts), absb(sh), absb(res))
+    g = W.bf16_bits_to_f32(bf16_host_bits(out)).astype(np.float64)
+    err_bound = (K + 3) * 2.0 ** -24 * S
+    assert (np.abs(g - ro) <= 2.0 ** -8 * np.abs(ro) + err_bound).all()
+    if norm:
+        gn = W.bf16_bits_to_f32(bf16_host_bits(out_norm)).astype(np.float64)
+        rms = np.sqrt((ro ** 2).mean(axis=1, keepdims=True) + eps)
+        gam = np.abs(W.bf16_bits_to_f32(gamma).astype(np.float64))[None, :]
+        bound = (2.0 ** -8 + 2e-4) * np.abs(rn) + gam / rms * err_bound * 2
+        assert (np.abs(gn - rn) <= bound).all(), float(np.max(np.abs(gn - rn) - bound))
+    else:
+        assert out_norm is None
