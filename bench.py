@@ -13,6 +13,10 @@ the stream the kernels run on, around each stage of every Nth step
 a record does not flush caches to system scope; recording them on a sample
 of steps keeps their cost out of the headline.
 
+Cold-cache legs follow the timed region (--cold-reps): each stage alone,
+after 1 GiB of unrelated device traffic (a fill, then separately a read),
+reported as `cold_cache` beside the back-to-back figures.
+
 Prints ONE JSON line.  `value` = effective HBM GB/s = algorithmic bytes per
 step * K / elapsed; algorithmic bytes count x read once, each valid expanded
 row written once and read once, the output written once, and the index
@@ -51,6 +55,10 @@ def parse():
                    help="CPU time budget for the oracle baseline (0 = skip)")
     p.add_argument("--event-every", type=int, default=10,
                    help="record stage events on every Nth timed step")
+    p.add_argument("--cold-reps", type=int, default=10,
+                   help="after timing, repetitions of the cold-cache legs: each stage timed alone "
+                        "after 1 GiB of device traffic (a fill, or a read) has evicted L2 and the "
+                        "memory-side cache (0 = skip)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run sanity check")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run 3 torch copies of 256 MiB: a kernel of known traffic "
@@ -346,6 +354,35 @@ def main():
     gbs = step_bytes * args.steps / elapsed / 1e9
     tokens_per_s = T * args.steps / elapsed
 
+    # cold-cache legs (outside the timed region): before each stage, 1 GiB of
+    # unrelated traffic evicts the 4 MB L2s and the 256 MB memory-side cache;
+    # each stage is then timed alone and a cold step is the sum of the stage
+    # medians.  "fill" writes the 1 GiB (the caches are left holding dirty
+    # lines, whose write-back the next stage pays for); "read" reads it (the
+    # caches are left holding clean lines: only the stage's own misses count).
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        flush64 = flush.view(torch.int64)
+        stages = [("layout", lambda: moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)),
+                  ("dispatch", run_dispatch), ("combine", run_combine)]
+        cold = {"reps": args.cold_reps}
+        for kind, evict in (("fill", lambda n: flush.fill_(n)), ("read", lambda n: flush64.sum())):
+            cev = [[(timer.new(), timer.new()) for _ in stages] for _ in range(args.cold_reps)]
+            torch.cuda.synchronize()
+            for rep in cev:
+                for (name, fn), (e0, e1) in zip(stages, rep):
+                    evict(len(name))
+                    timer.record(e0)
+                    fn()
+                    timer.record(e1)
+            torch.cuda.synchronize()
+            med = {name: float(np.median([timer.elapsed_us(*rep[j]) for rep in cev]))
+                   for j, (name, _) in enumerate(stages)}
+            cold[kind] = {"stage_median_us": {k: round(v, 2) for k, v in med.items()},
+                          "step_us": round(sum(med.values()), 2)}
+        del flush, flush64
+
     dom = max(("dispatch", "combine"), key=lambda k: avg_us[k])
     achieved = sb[dom] / (avg_us[dom] * 1e-6) / 1e9
 
@@ -412,6 +449,13 @@ def main():
                      "avg_launch_us": round(avg_us[dom], 2)},
         "cpu_baseline": cpu,
     }
+    if cold is not None:
+        for kind in ("fill", "read"):
+            c = cold[kind]
+            c["gbs"] = round(step_bytes / (c["step_us"] * 1e-6) / 1e9, 1)
+            c["frac_of_hbm_peak"] = round(c["gbs"] / HBM_PEAK_GBS, 4)
+            c["tokens_per_s"] = round(T / (c["step_us"] * 1e-6), 1)
+        rec["cold_cache"] = cold
     print(json.dumps(rec), flush=True)
 
 
