@@ -411,3 +411,25 @@ def test_combine_fused_parity(variant):
         assert (np.abs(gn - rn) <= bound).all(), float(np.max(np.abs(gn - rn) - bound))
     else:
         assert out_norm is None
+
+
+@pytest.mark.parametrize("quant", [4, 0x24], ids=["mxfp8_e4m3", "mxfp8_e5m2"])
+def test_mx_every_element_and_shared_exponent(quant):
+    """MX dispatch on rows that pair every finite bf16 element with every block
+    exponent it can meet (8.6 M elements): codes and e8m0 bytes bit-exact
+    against the oracle, scatter over 8 experts with a ragged expert size."""
+    from mx_exhaustive import exhaustive_mx_rows
+    x_bits, _ = exhaustive_mx_rows(1024)
+    T, H = x_bits.shape
+    E = 8
+    idx = np.ascontiguousarray((np.arange(T, dtype=np.int64) * 5 % E)[:, None])
+    ol = oracle.layout(idx, E, 2, 4)
+    lay = gpu_layout(idx, E, 2, 4)
+    assert_layout_equal(layout_to_host(lay), ol)
+    cap = ol.recv_capacity
+    orx, ors = oracle_poisoned(cap, H, quant)
+    orx, ors, _ = oracle.dispatch(x_bits, ol.token_row, cap, None, quant, recv_x=orx, recv_scales=ors)
+    rx, rs, _ = poisoned_recv(lay, H, quant)
+    moe.moe_dispatch(bf16_dev(x_bits), lay, None, quant, recv_x=rx, recv_scales=rs)
+    np.testing.assert_array_equal(recv_to_host(rx, quant), orx)
+    np.testing.assert_array_equal(rs.cpu().numpy(), ors)
