@@ -187,35 +187,49 @@ def cpu_baseline(inp, w, quant, budget_s, bytes_fn, prequant=None):
         from combine_moe_get_dispatch_amd import workloads as W
         epi = (W.random_bf16_rows(w.num_tokens, w.hidden, 21), W.random_bf16_rows(w.num_tokens, w.hidden, 22),
                np.full(w.hidden, 0x3F80, np.uint16))
-    reps, total_bytes = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        ol = oracle.layout(inp.topk_idx, E, R, a)
-        if prequant is not None:
-            oracle.dispatch_prequantized(prequant[0], prequant[1], ol.token_row, ol.recv_capacity)
-            y = prequant[2]
-        elif w.static_scale > 0:
-            oracle.dispatch_static(inp.x_bits, ol.token_row, ol.recv_capacity,
-                                   np.array([w.static_scale], np.float32))
-            y = np.zeros((ol.recv_capacity, w.hidden), np.uint16)
-        else:
-            rx, rs, _ = oracle.dispatch(inp.x_bits, ol.token_row, ol.recv_capacity, None, quant)
-            y = rx if quant == 0 else np.zeros((ol.recv_capacity, w.hidden), np.uint16)
-        if w.epilogue:
-            oracle.combine_fused(y, ol.token_row, inp.topk_weights, epi[0], epi[1], epi[2], 1e-6,
-                                 with_norm=True)
-        else:
-            oracle.combine(y, ol.token_row, inp.topk_weights)
-        reps += 1
-        V = int((inp.topk_idx >= 0).sum())
-        total_bytes += sum(bytes_fn(V, ol.recv_capacity).values())
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": round(total_bytes / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"full workload ({w.num_tokens} tokens), layout+dispatch+combine, {reps} repetition(s) "
-                      f"in {el:.1f} s", "tokens_per_s": round(reps * w.num_tokens / el, 1)}
+    V = int((inp.topk_idx >= 0).sum())
+
+    def leg(budget):
+        reps, total_bytes = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            ol = oracle.layout(inp.topk_idx, E, R, a)
+            if prequant is not None:
+                oracle.dispatch_prequantized(prequant[0], prequant[1], ol.token_row, ol.recv_capacity)
+                y = prequant[2]
+            elif w.static_scale > 0:
+                oracle.dispatch_static(inp.x_bits, ol.token_row, ol.recv_capacity,
+                                       np.array([w.static_scale], np.float32))
+                y = np.zeros((ol.recv_capacity, w.hidden), np.uint16)
+            else:
+                rx, rs, _ = oracle.dispatch(inp.x_bits, ol.token_row, ol.recv_capacity, None, quant)
+                y = rx if quant == 0 else np.zeros((ol.recv_capacity, w.hidden), np.uint16)
+            if w.epilogue:
+                oracle.combine_fused(y, ol.token_row, inp.topk_weights, epi[0], epi[1], epi[2], 1e-6,
+                                     with_norm=True)
+            else:
+                oracle.combine(y, ol.token_row, inp.topk_weights)
+            reps += 1
+            total_bytes += sum(bytes_fn(V, ol.recv_capacity).values())
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, total_bytes, el
+
+    threads = oracle.num_threads()
+    reps, total_bytes, el = leg(budget_s)
+    res = {"value": round(total_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"full workload ({w.num_tokens} tokens), layout+dispatch+combine, {reps} repetition(s) "
+                     f"in {el:.1f} s", "tokens_per_s": round(reps * w.num_tokens / el, 1)}
+    # the same oracle on one thread (its layout is sequential in both legs)
+    oracle.set_num_threads(1)
+    try:
+        reps1, bytes1, el1 = leg(budget_s / 2)
+    finally:
+        oracle.set_num_threads(threads)
+    res["single_thread"] = {"value": round(bytes1 / el1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                            "sample": f"{reps1} repetition(s) in {el1:.1f} s"}
+    return res
 
 
 def main():

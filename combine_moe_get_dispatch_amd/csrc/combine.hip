@@ -7,21 +7,24 @@
 // (half to even).  Entries whose row is -1 (dropped) are skipped; no weights
 // means weight 1.
 //
-// Design (gfx950): one workgroup per token, one 16-byte vector (8 hidden
-// elements) per lane (896 lanes for H = 7168; two vectors per lane above
-// H = 8192).  A lane issues the loads of all K
-// rows for that vector before the first FMA, so K independent 16-byte reads
-// per lane are in flight (K <= 16 gives at most 64 VGPRs of staging).  The
-// expanded rows are read exactly once; the rows of one token are scattered
-// over the receive buffer, but each load instruction of a wave reads 1 KiB
-// contiguous bytes of one row.  Row indices and weights are uniform per
-// workgroup and live in scalar registers.
+// Design (gfx950): one single-wave workgroup per (token, 1 KiB slice of the
+// row), one 16-byte vector (8 hidden elements) per lane: 14 workgroups per
+// token at H = 7168.  A lane issues the loads of all K rows for its vector
+// before the first FMA, so K independent 16-byte reads per lane are in
+// flight (K <= 16 gives at most 64 VGPRs of staging).  The expanded rows are
+// read exactly once; the rows of one token are scattered over the receive
+// buffer, but each load instruction reads 1 KiB contiguous bytes of one row.
+// Row indices and weights are uniform per workgroup and live in scalar
+// registers.  One-wave workgroups let a CU hold its full 32 waves at any H
+// (whole-row workgroups of 896 lanes stop at 28) and shorten the grid's tail.
 //
-// combine_fused_kernel adds the epilogues named by the pages (EPBatchManager
+// The epilogues named by the pages (EPBatchManager
 // page, ep_combine(): shared expert outputs added to the reduced routed
 // outputs; CANN page: the CombineAddRmsNorm companion): the shared-expert row
 // and the residual row of the token are loaded with the expert rows and
-// added to the fp32 sum, which is stored, and optionally normalised,
+// added to the fp32 sum (in the slice kernel when there is no
+// normalisation), which is stored, and optionally normalised
+// (combine_fused_kernel, one workgroup per token),
 //   norm = s / sqrt(mean(s^2) + eps) * gamma,
 // from the fp32 values (sum of squares: per lane, then wave shuffles, then
 // the waves in order through LDS -- a fixed order, so results are
@@ -33,35 +36,45 @@
 
 namespace moe {
 
-template <int VPT, int KMAX>
-__global__ __launch_bounds__(kRowMaxThreads) void combine_kernel(
-    const u32x4 *__restrict__ y, int nvec, int K, const int32_t *__restrict__ token_row,
-    const float *__restrict__ topk_weights, int64_t cap, u32x4 *__restrict__ out)
+// One wave per (token, 64-vector slice of its row): 1 KiB of each of the
+// token's K rows in, 1 KiB out.  Small one-wave workgroups let every CU hold
+// its full complement of waves whatever H is (a whole-row workgroup of 896
+// lanes at H = 7168 leaves a CU at 28 of 32 waves) and keep the tail of the
+// grid short.  shared / residual (nullable) are the un-normalised epilogues.
+template <int KMAX>
+__global__ __launch_bounds__(kWave) void combine_slice_kernel(
+    const u32x4 *__restrict__ y, int nvec, int nslices, int64_t nitems, int K,
+    const int32_t *__restrict__ token_row, const float *__restrict__ topk_weights, int64_t cap,
+    const u32x4 *__restrict__ shared, const u32x4 *__restrict__ residual,
+    u32x4 *__restrict__ out)
 {
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    int rows[KMAX];
-    float wts[KMAX];
+    for (int64_t b = blockIdx.x; b < nitems; b += gridDim.x) {
+        const int64_t t = b / nslices;
+        const int i = (int)(b - t * nslices) * kWave + (int)threadIdx.x;
+        int rows[KMAX];
+        float wts[KMAX];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        rows[k] = -1;
-        wts[k] = 0.0f;
-        if (k < K) {
-            const int r = token_row[(int64_t)t * K + k];
-            rows[k] = (r >= 0 && r < cap) ? r : -1;
-            wts[k] = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;
+        for (int k = 0; k < KMAX; ++k) {
+            rows[k] = -1;
+            wts[k] = 0.0f;
+            if (k < K) {
+                const int r = token_row[t * K + k];
+                rows[k] = (r >= 0 && r < cap) ? r : -1;
+                wts[k] = topk_weights ? topk_weights[t * K + k] : 1.0f;
+            }
         }
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const int i = tid + j * (int)blockDim.x;
         if (i >= nvec)
-            break;
+            continue;
         u32x4 yv[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             if (rows[k] >= 0)
                 yv[k] = __builtin_nontemporal_load(y + (int64_t)rows[k] * nvec + i);
+        u32x4 sv = u32x4{0u, 0u, 0u, 0u}, rv = u32x4{0u, 0u, 0u, 0u};
+        if (shared)
+            sv = shared[t * nvec + i];
+        if (residual)
+            rv = residual[t * nvec + i];
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -76,11 +89,23 @@ __global__ __launch_bounds__(kRowMaxThreads) void combine_kernel(
                 acc[2 * c + 1] = __builtin_fmaf(wts[k], bf16_hi(yv[k][c]), acc[2 * c + 1]);
             }
         }
+        if (shared)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc[2 * c] += bf16_lo(sv[c]);
+                acc[2 * c + 1] += bf16_hi(sv[c]);
+            }
+        if (residual)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc[2 * c] += bf16_lo(rv[c]);
+                acc[2 * c + 1] += bf16_hi(rv[c]);
+            }
         u32x4 o;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             o[c] = pack_bf16x2(acc[2 * c], acc[2 * c + 1]);
-        out[(int64_t)t * nvec + i] = o;
+        out[t * nvec + i] = o;
     }
 }
 
@@ -188,23 +213,22 @@ __global__ __launch_bounds__(kRowMaxThreads) void combine_fused_kernel(
     }
 }
 
-template <int VPT>
-static hipError_t launch_combine_k(int kmax, dim3 grid, dim3 block, hipStream_t stream,
-                                   const u32x4 *y, int nvec, int K, const int32_t *token_row,
-                                   const float *w, int64_t cap, u32x4 *out)
+static hipError_t launch_slices(int K, int64_t T, int nvec, hipStream_t stream, const u32x4 *y,
+                                const int32_t *token_row, const float *w, int64_t cap,
+                                const u32x4 *sh, const u32x4 *res, u32x4 *out)
 {
-    switch (kmax) {
-    case 1:
-        return launch_kernel(combine_kernel<VPT, 1>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-    case 2:
-        return launch_kernel(combine_kernel<VPT, 2>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-    case 4:
-        return launch_kernel(combine_kernel<VPT, 4>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-    case 8:
-        return launch_kernel(combine_kernel<VPT, 8>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-    default:
-        return launch_kernel(combine_kernel<VPT, 16>, grid, block, 0, stream, y, nvec, K, token_row, w, cap, out);
-    }
+    const int nslices = (nvec + kWave - 1) / kWave;
+    const int64_t nitems = T * nslices;
+    const dim3 grid((unsigned)(nitems < kMaxGrid ? nitems : kMaxGrid)), block(kWave);
+    if (K <= 1)
+        return launch_kernel(combine_slice_kernel<1>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
+    if (K <= 2)
+        return launch_kernel(combine_slice_kernel<2>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
+    if (K <= 4)
+        return launch_kernel(combine_slice_kernel<4>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
+    if (K <= 8)
+        return launch_kernel(combine_slice_kernel<8>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
+    return launch_kernel(combine_slice_kernel<16>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
 }
 
 hipError_t launch_combine(const void *y, int64_t cap, int T, int H, int K,
@@ -213,16 +237,8 @@ hipError_t launch_combine(const void *y, int64_t cap, int T, int H, int K,
 {
     if (T == 0)
         return hipSuccess;
-    const int nvec = H / 8;
-    const int threads = row_block_threads(nvec);
-    const int vpt = (nvec + threads - 1) / threads; // 1 or 2 (H <= 16384)
-    const int kmax = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : 16;
-    const dim3 grid(T), block(threads);
-    const u32x4 *yv = (const u32x4 *)y;
-    u32x4 *ov = (u32x4 *)out;
-    if (vpt == 1)
-        return launch_combine_k<1>(kmax, grid, block, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
-    return launch_combine_k<2>(kmax, grid, block, stream, yv, nvec, K, token_row, topk_weights, cap, ov);
+    return launch_slices(K, T, H / 8, stream, (const u32x4 *)y, token_row, topk_weights, cap,
+                         nullptr, nullptr, (u32x4 *)out);
 }
 
 template <int VPT>
@@ -253,6 +269,9 @@ hipError_t launch_combine_fused(const void *y, int64_t cap, int T, int H, int K,
     if (T == 0)
         return hipSuccess;
     const int nvec = H / 8;
+    if (!out_norm) // no row-wide reduction: the slice kernel
+        return launch_slices(K, T, nvec, stream, (const u32x4 *)y, token_row, topk_weights, cap,
+                             (const u32x4 *)shared, (const u32x4 *)residual, (u32x4 *)out);
     const int threads = row_block_threads(nvec);
     const int vpt = (nvec + threads - 1) / threads;
     const int kmax = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : 16;

@@ -38,6 +38,9 @@ hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
 // ceil(nvec / 64) waves (at most 16), and a lane takes a second vector only
 // when the row has more than 1024 vectors (H > 8192).
 constexpr int kRowMaxThreads = 1024;
+// Upper bound on the grid of grid-stride kernels (work items beyond it are
+// taken by the same workgroups in later iterations).
+constexpr int64_t kMaxGrid = int64_t(1) << 24;
 inline int row_block_threads(int nvec)
 {
     const int t = (nvec + 63) / 64 * 64;

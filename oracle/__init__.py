@@ -348,3 +348,8 @@ def quant_mxfp8_rows(x_bits: np.ndarray):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the OpenMP loops of dispatch and combine use from now on."""
+    lib().oracle_set_num_threads(int(n))

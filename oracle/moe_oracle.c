@@ -775,6 +775,16 @@ int oracle_combine_fused(const uint16_t *y, int64_t cap, int T, int H, int K,
     return ORC_OK;
 }
 
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
