@@ -68,6 +68,31 @@ class MoeError(RuntimeError):
 _lib: Optional[ctypes.CDLL] = None
 
 
+def declare_signatures(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Give the C ABI's functions their argument and result types on a loaded
+    copy of the library."""
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    L.moe_recv_capacity_bound.argtypes = [i32, i32, i32, i32]
+    L.moe_recv_capacity_bound.restype = i64
+    L.moe_layout_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.moe_layout_workspace_bytes.restype = sz
+    L.moe_get_dispatch_layout.argtypes = [P, i32, i32, i32, i32, i32, i64] + [P] * 8 + [P, sz, P]
+    L.moe_get_dispatch_layout.restype = i32
+    L.moe_dispatch.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
+    L.moe_dispatch.restype = i32
+    L.moe_dispatch_static.argtypes = [P, i32, i32, i32, P, P, i64, P, i32, P, P, P]
+    L.moe_dispatch_static.restype = i32
+    L.moe_dispatch_prequantized.argtypes = [P, i32, i32, P, i32, i32, P, P, i64, P, P, P, P]
+    L.moe_dispatch_prequantized.restype = i32
+    L.moe_combine.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
+    L.moe_combine.restype = i32
+    L.moe_combine_fused.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, P, P, P]
+    L.moe_combine_fused.restype = i32
+    L.moe_status_string.argtypes = [i32]
+    L.moe_status_string.restype = ctypes.c_char_p
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """Load the HIP library (raises if it has not been built)."""
     global _lib
@@ -76,27 +101,7 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with combine_moe_get_dispatch_amd.build_lib.build() "
                 "(hipcc, gfx950). There is no CPU fallback.")
-        L = ctypes.CDLL(LIB_PATH)
-        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
-        L.moe_recv_capacity_bound.argtypes = [i32, i32, i32, i32]
-        L.moe_recv_capacity_bound.restype = i64
-        L.moe_layout_workspace_bytes.argtypes = [i32, i32, i32, i32]
-        L.moe_layout_workspace_bytes.restype = sz
-        L.moe_get_dispatch_layout.argtypes = [P, i32, i32, i32, i32, i32, i64] + [P] * 8 + [P, sz, P]
-        L.moe_get_dispatch_layout.restype = i32
-        L.moe_dispatch.argtypes = [P, i32, i32, i32, P, P, i64, i32, P, P, P, P]
-        L.moe_dispatch.restype = i32
-        L.moe_dispatch_static.argtypes = [P, i32, i32, i32, P, P, i64, P, i32, P, P, P]
-        L.moe_dispatch_static.restype = i32
-        L.moe_dispatch_prequantized.argtypes = [P, i32, i32, P, i32, i32, P, P, i64, P, P, P, P]
-        L.moe_dispatch_prequantized.restype = i32
-        L.moe_combine.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
-        L.moe_combine.restype = i32
-        L.moe_combine_fused.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, P, P, P]
-        L.moe_combine_fused.restype = i32
-        L.moe_status_string.argtypes = [i32]
-        L.moe_status_string.restype = ctypes.c_char_p
-        _lib = L
+        _lib = declare_signatures(ctypes.CDLL(LIB_PATH))
     return _lib
 
 

@@ -18,6 +18,10 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmoe_dispatch_combine.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+# Test build of the same sources with a grid cap of 2^6 workgroups, so that the
+# grid-stride iterations of the kernels run at test sizes.
+SMALL_GRID_LIB_PATH = os.path.join(HERE, "libmoe_dispatch_combine_smallgrid.so")
+SMALL_GRID_FLAGS = ["-DMOE_MAX_GRID_LOG2=6"]
 SOURCES = ["moe_api.hip", "layout.hip", "dispatch.hip", "combine.hip"]
 HEADERS = ["device_common.h", "launch.h"]
 
@@ -35,14 +39,28 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build(verbose: bool = True, extra_flags=None) -> str:
-    out_tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-           *sources(), "-o", out_tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(out_tmp, LIB_PATH)
+def _command(out_path, extra_flags):
+    return [HIPCC, *FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
+            *sources(), "-o", out_path]
+
+
+def build(verbose: bool = True, extra_flags=None, with_test_build: bool = False) -> str:
+    """Compile the library (and, with with_test_build, the small-grid test
+    build alongside it, in parallel)."""
+    jobs = [(LIB_PATH, extra_flags)]
+    if with_test_build:
+        jobs.append((SMALL_GRID_LIB_PATH, SMALL_GRID_FLAGS + list(extra_flags or [])))
+    procs = []
+    for path, flags in jobs:
+        cmd = _command(path + ".tmp", flags)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((path, subprocess.Popen(cmd)))
+    failed = [path for path, p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, f"hipcc ({', '.join(failed)})")
+    for path, _ in procs:
+        os.replace(path + ".tmp", path)
     return LIB_PATH
 
 

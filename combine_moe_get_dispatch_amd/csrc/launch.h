@@ -39,8 +39,12 @@ hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
 // when the row has more than 1024 vectors (H > 8192).
 constexpr int kRowMaxThreads = 1024;
 // Upper bound on the grid of grid-stride kernels (work items beyond it are
-// taken by the same workgroups in later iterations).
-constexpr int64_t kMaxGrid = int64_t(1) << 24;
+// taken by the same workgroups in later iterations).  A test build lowers it
+// so that the later iterations run at small sizes.
+#ifndef MOE_MAX_GRID_LOG2
+#define MOE_MAX_GRID_LOG2 24
+#endif
+constexpr int64_t kMaxGrid = int64_t(1) << MOE_MAX_GRID_LOG2;
 inline int row_block_threads(int nvec)
 {
     const int t = (nvec + 63) / 64 * 64;
