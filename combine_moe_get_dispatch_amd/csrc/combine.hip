@@ -1,7 +1,8 @@
 // combine.hip -- top-k weighted sum of every token's expert-output rows.
 //
-// What is computed (Normal Mode API page, combine: "multiply by weights and
-// sum"; EPBatchManager page, ep_combine(): output (num_local_tokens, hidden)):
+// What is computed (Normal Mode API page, combine Description: the expert
+// outputs are weighted and summed; EPBatchManager page, ep_combine(): output
+// (num_local_tokens, hidden)):
 //   out[t] = bf16( sum_k  w[t,k] * y[row(t,k)] )
 // as an fp32 fused multiply-add chain in ascending k, rounded once to bf16
 // (half to even).  Entries whose row is -1 (dropped) are skipped; no weights

@@ -3,7 +3,7 @@
 //
 // What is computed (Normal Mode API page, dispatch Parameters / Return
 // Values; EPBatchManager page, ep_dispatch() Returns; CANN
-// aclnnMoeDistributeDispatchV2 page, Constraint 1 "deterministic"):
+// aclnnMoeDistributeDispatchV2 page, Constraint 1, results are deterministic):
 //   c[e]        = number of entries with topk_idx == e
 //   off[e]      = sum over e' < e of ceil(c[e'] / a) * a
 //   row(t, k)   = off[e] + #{ (t', k') : idx[t', k'] == e, t'K + k' < tK + k }

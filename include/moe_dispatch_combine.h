@@ -15,7 +15,7 @@
  *     Values and Constraints; combine Description / Parameters.
  *   Huawei CANN "aclnnMoeDistributeDispatchV2": Formula Cases 1, 3 and 5;
  *     Constraints 1 (deterministic), 7 (shapes), 11 (integer division); the
- *     two-phase "workspace size, then run" calling pattern.
+ *     two-phase calling pattern (query the workspace size, then run).
  *   Modular MAX "EPBatchManager": ep_dispatch() and ep_combine() Returns.
  *
  * Conventions for every entry point:
@@ -226,7 +226,8 @@ int moe_dispatch_prequantized(const void *data, int num_tokens, int row_bytes, c
                               void *recv_scales, float *recv_weights, hipStream_t stream);
 
 /*
- * Combine (Normal Mode API page, combine: "multiply by weights and sum";
+ * Combine (Normal Mode API page, combine Description: expert outputs weighted
+ * and summed;
  * EPBatchManager page, ep_combine(): output (num_local_tokens, hidden)).
  *
  *   out[t, :] = bf16( sum over k with 0 <= token_row[t, k] < recv_capacity of

@@ -500,7 +500,7 @@ static void quant_static_int8_row(const uint16_t *x, int H, const float *scales,
  * Dispatch copies every token to each of its selected experts' rows of the
  * expert-grouped receive buffer ([NMA] dispatch description; [CANN]
  * Description and Formula Case 1: expandXOut holds the tokens; [EPBM]
- * ep_dispatch(): output_tokens "ready for grouped matmul").  Quantisation,
+ * ep_dispatch(): output_tokens grouped by expert for a grouped matmul).  Quantisation,
  * when asked for, is applied to the source token once and the same codes and
  * scale go to all of its rows ([CANN] Formula: quantOut is formed from X
  * before the exchange).
@@ -698,7 +698,7 @@ void oracle_quant_fp8_pertoken_rows(const uint16_t *x, int T, int H, int fmt, ui
 
 /*
  * Combine brings each token's expert outputs back and takes their weighted
- * sum ([NMA] combine Description: "multiply by weights and sum"; [EPBM]
+ * sum ([NMA] combine Description: the expert outputs are weighted and summed; [EPBM]
  * ep_combine(): weighted sum of routed expert outputs, result
  * (num_local_tokens, hidden)):
  *   out[t, h] = sum over valid k of  w[t, k] * y[token_row[t, k], h]
