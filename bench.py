@@ -96,11 +96,20 @@ def stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows=None, static=False, 
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and whitespace (string literals kept)."""
+    import re
+    text = re.sub(r'//[^\n]*|/\*.*?\*/', " ", text, flags=re.S)
+    return re.sub(r"\s+", "", text)
+
+
 def kernel_source_sha(stage: str) -> str:
+    """First 16 hex digits of sha256 over the code of the kernel's source
+    files; edits to comments or layout leave it unchanged."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[stage]:
-        with open(os.path.join(ROOT, "combine_moe_get_dispatch_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "combine_moe_get_dispatch_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
