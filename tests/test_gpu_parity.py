@@ -485,3 +485,50 @@ def test_combine_grid_stride_iterations():
             S = combine_bound(y_bits, ol.token_row, wts, K) + np.abs(W.bf16_bits_to_f32(sh_bits)) \
                 + np.abs(W.bf16_bits_to_f32(res_bits))
         check_combine(bf16_host_bits(got), exact, S, K + 2, north_star=False)
+
+
+ALL_MODES = [0, 2, 4, 0x12, 0x22, 0x24, 0x13, 0x23]
+
+
+def _random_config(i):
+    rng = np.random.default_rng(1000 + i)
+    E = int(rng.choice([1, 2, 3, 8, 12, 64, 96, 256, 512]))
+    R = int(rng.choice([r for r in (1, 2, 3, 4, 8, 16, 64) if E % r == 0]))
+    dup = bool(rng.random() < 0.3)
+    K = int(rng.integers(1, min(16, E) + 1)) if not dup else int(rng.integers(1, 17))
+    T = int(rng.choice([0, 1, 2, 63, 64, 65, 257, int(rng.integers(3, 900))]))
+    H = 32 * int(rng.choice([1, 2, 3, 5, 16, 33, 64, 100, 128]))
+    a = int(rng.choice([1, 2, 7, 32, 128]))
+    quant = ALL_MODES[i % len(ALL_MODES)]
+    drop = float(rng.choice([0.0, 0.0, 0.3, 1.0]))
+    return rng, T, H, E, R, K, a, quant, dup, drop
+
+
+@pytest.mark.parametrize("i", range(48), ids=[f"cfg{i}" for i in range(48)])
+def test_random_configurations(i):
+    """Seeded random shapes over the whole valid range (including T = 0, one
+    expert, all entries dropped, ragged hidden sizes, every quant mode): the
+    full path against the oracle, plus the expert-side weighting round trip
+    (rows scaled by the per-row weights dispatch returns, then an unweighted
+    combine)."""
+    rng, T, H, E, R, K, a, quant, dup, drop = _random_config(i)
+    print(f"[cfg{i}] T={T} H={H} E={E} R={R} K={K} a={a} quant={quant:#x} dup={dup} drop={drop}", flush=True)
+    idx, wts = _routing(rng, T, K, E, dup, drop)
+    wts[idx < 0] = 0.0
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    run_full_case(x, idx, wts, E, R, a, quant, north_star=False)
+    if quant != 0 or T == 0:
+        return
+    # expert applies the row weights that dispatch returned; combine unweighted
+    ol = oracle.layout(idx, E, R, a)
+    lay = gpu_layout(idx, E, R, a)
+    rx, _, rw = poisoned_recv(lay, H, 0)
+    moe.moe_dispatch(bf16_dev(x), lay, torch.from_numpy(wts).to(DEV), 0, recv_x=rx, recv_weights=rw)
+    used = torch.from_numpy(ol.recv_src >= 0).to(DEV)
+    y = torch.zeros_like(rx)
+    y[used] = (rx[used].float() * rw[used, None]).to(torch.bfloat16)
+    y_bits = bf16_host_bits(y)
+    out = moe.moe_combine(y, lay, None)
+    exact = oracle.combine(y_bits, ol.token_row, None)
+    S = combine_bound(y_bits, ol.token_row, None, K)
+    check_combine(bf16_host_bits(out), exact, S, K, north_star=False)
