@@ -58,18 +58,26 @@ inline int row_block_threads(int nvec)
 constexpr int kLayoutTargetChunks = 64;
 constexpr int kMaxChunkEntries = 8192;
 constexpr int kMaxChunkFlags = 16384;
+// Batches of at most this many routing entries (and T*R <= kMaxChunkFlags)
+// are laid out by one workgroup in one launch.
+constexpr int kSingleLayoutMaxEntries = 4096;
 
 struct LayoutPlan {
     int tokens_per_chunk;
     int num_chunks;
     size_t workspace_bytes; // count table [chunks][E rounded up to 4] + rank table [chunks][R] + flags [chunks]
+    bool single;            // the whole batch in one workgroup (no workspace, one launch)
 };
 
 inline LayoutPlan plan_layout(int T, int K, int E, int R)
 {
-    LayoutPlan p{0, 0, 0};
-    if (T <= 0)
+    LayoutPlan p{0, 0, 0, false};
+    if ((int64_t)T * K <= kSingleLayoutMaxEntries && (int64_t)T * R <= kMaxChunkFlags) {
+        p.single = true; // includes T == 0
+        p.tokens_per_chunk = T;
+        p.num_chunks = T > 0 ? 1 : 0;
         return p;
+    }
     int tpc = (T + kLayoutTargetChunks - 1) / kLayoutTargetChunks;
     if (tpc > kMaxChunkEntries / K)
         tpc = kMaxChunkEntries / K;

@@ -10,8 +10,10 @@
 //   recv_src    = inverse of row (-1 on padding / unused rows)
 //   is_token_in_rank[t, r], num_tokens_per_rank[r]  with rank(e) = e / (E / R)
 //
-// Design (gfx950, wave64): the T*K entries are split into chunks of whole
-// tokens, one workgroup per chunk.
+// Design (gfx950, wave64): a small batch (at most kSingleLayoutMaxEntries
+// entries) is laid out by layout_single_kernel, one workgroup and one launch
+// (below).  Larger batches are split into chunks of whole tokens, one
+// workgroup per chunk, in two launches:
 //   layout_count_kernel: per-chunk expert histogram.  Lanes of a wave holding
 //     the same expert are found with one ballot per key bit; the lowest of them
 //     adds the group's popcount to an LDS counter, so a hot expert costs one
@@ -402,6 +404,212 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     }
 }
 
+// n / d for 0 <= n < 2^24 and 1 <= d <= 2^24 without the integer division
+// sequence: a float quotient is within one of the exact one, then fixed.
+__device__ __forceinline__ int div_small(int n, int d)
+{
+    int q = (int)((float)n * __frcp_rn((float)d));
+    q += (q + 1) * d <= n ? 1 : 0;
+    q -= q * d > n ? 1 : 0;
+    return q;
+}
+
+// One workgroup for a whole small batch (T*K <= kSingleLayoutMaxEntries
+// entries and T*R <= kMaxChunkFlags token x rank cells): every entry lives in
+// LDS, so the histogram, the aligned scan and the ranks need no count table
+// and no second launch.  All the ballot matching runs on one CU, so its cost
+// grows with the batch (about 1.3 ns per entry); the two-launch layout
+// (~13 us) wins above about 4096 entries.  The per-wave expert counts are the histogram: their sum over the
+// waves is the expert total, their exclusive prefix over the waves the wave's
+// base, exactly as in layout_rank_kernel with a single chunk.  Counts are
+// held in 16 bits (at most kMaxChunkEntries entries per batch).
+__global__ __launch_bounds__(kRankThreads) void layout_single_kernel(
+    const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int L, int a, int nbits,
+    int64_t cap, int32_t *__restrict__ itr, int32_t *__restrict__ ntpr, int32_t *__restrict__ ntpe,
+    int32_t *__restrict__ nrtpe, int32_t *__restrict__ off, int32_t *__restrict__ token_row,
+    int32_t *__restrict__ recv_src, int32_t *__restrict__ error_flag)
+{
+    static_assert(kMaxChunkEntries <= 32767, "16-bit per-wave counts");
+    __shared__ int16_t s_e[kMaxChunkEntries];
+    __shared__ uint8_t s_flags[kMaxChunkFlags];
+    __shared__ int16_t s_w[kRankWaves][MOE_MAX_EXPERTS];
+    __shared__ int s_tot[MOE_MAX_EXPERTS];
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_rcnt[MOE_MAX_EXPERTS];
+    __shared__ int s_wsum[kRankWaves];
+    __shared__ int s_bad;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int ne = T * K;
+
+    int64_t idx_reg[kIdxPerThread];
+    prefetch_idx(topk_idx, 0, ne, idx_reg); // in flight while LDS is cleared
+
+    for (int i = tid; i < kRankWaves * E; i += kRankThreads)
+        s_w[i / E][i % E] = 0;
+    for (int i = tid; i < R; i += kRankThreads)
+        s_rcnt[i] = 0;
+    for (int i = tid; i < T * R; i += kRankThreads)
+        s_flags[i] = 0;
+    if (tid == 0)
+        s_bad = 0;
+    __syncthreads();
+
+    // ids into LDS (out-of-range ids become -1 and raise the error bit) and
+    // token x rank membership
+    int bad = 0;
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u) {
+        const int i = tid + u * kRankThreads;
+        if (i < ne) {
+            const int64_t v = idx_reg[u];
+            int e = -1;
+            if (v < -1 || v >= E)
+                bad = 1;
+            else
+                e = (int)v;
+            s_e[i] = (int16_t)e;
+            if (e >= 0)
+                s_flags[div_small(i, K) * R + div_small(e, L)] = 1;
+        }
+    }
+    if (bad)
+        atomicOr(&s_bad, 1);
+    __syncthreads();
+
+    // per-wave expert counts; each wave owns a contiguous run of entries in
+    // flat order.  The match masks and ids stay in registers for the ranking
+    // pass below (at most kIdxPerThread iterations per wave; the iteration
+    // guard is uniform over the workgroup, so the ballots stay convergent).
+    const int per_wave = ((ne + kRankWaves * kWave - 1) / (kRankWaves * kWave)) * kWave;
+    const int w_lo = wave * per_wave;
+    const int w_hi = min(ne, w_lo + per_wave);
+    uint64_t same_reg[kIdxPerThread];
+    int e_reg[kIdxPerThread];
+#pragma unroll
+    for (int it = 0; it < kIdxPerThread; ++it) {
+        same_reg[it] = 0;
+        e_reg[it] = -1;
+        if (it * kWave < per_wave) {
+            const int j = w_lo + it * kWave + lane;
+            const int e = (j < w_hi) ? (int)s_e[j] : -1;
+            const bool has = e >= 0;
+            const uint64_t same = match_same_key(e, has, nbits);
+            same_reg[it] = same;
+            e_reg[it] = e;
+            if (has && count_below(same) == 0) // one writer per (wave, expert)
+                s_w[wave][e] = (int16_t)(s_w[wave][e] + __popcll(same));
+        }
+    }
+    // is_token_in_rank rows and per-rank token counts: thread (r, part) owns
+    // rank r of tokens part, part + parts, ...
+    {
+        const int parts = kRankThreads / R;
+        if (tid < parts * R) {
+            const int r = tid % R;
+            const int part = tid / R;
+            int cnt = 0;
+            for (int t = part; t < T; t += parts) {
+                const int f = s_flags[t * R + r];
+                itr[(int64_t)t * R + r] = f;
+                cnt += f;
+            }
+            if (cnt)
+                atomicAdd(&s_rcnt[r], cnt);
+        }
+    }
+    __syncthreads();
+
+    // expert totals and each wave's exclusive base, one thread per expert
+    for (int e = tid; e < E; e += kRankThreads) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kRankWaves; ++w) {
+            const int v = s_w[w][e];
+            s_w[w][e] = (int16_t)run;
+            run += v;
+        }
+        s_tot[e] = run;
+    }
+    __syncthreads();
+
+    // aligned counts and their exclusive prefix sum ("/" is integer division,
+    // CANN page Constraint 11); E <= 512 < kRankThreads
+    int ac = 0;
+    if (tid < E) {
+        const int c = s_tot[tid];
+        ac = ((c + a - 1) / a) * a;
+    }
+    int incl = ac;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int v = __shfl_up(incl, d, kWave);
+        if (lane >= d)
+            incl += v;
+    }
+    if (lane == kWave - 1)
+        s_wsum[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int total;
+        const int v = lane < kRankWaves ? s_wsum[lane] : 0;
+        const int ex = exclusive_scan16(v, &total);
+        if (lane < kRankWaves)
+            s_wsum[lane] = ex;
+    }
+    __syncthreads();
+    if (tid < E)
+        s_off[tid] = s_wsum[wave] + incl - ac;
+    if (tid == E - 1)
+        s_off[E] = s_wsum[wave] + incl;
+    __syncthreads();
+
+    // small outputs
+    for (int e = tid; e < E; e += kRankThreads) {
+        ntpe[e] = s_tot[e];
+        nrtpe[e] = s_off[e + 1] - s_off[e];
+    }
+    for (int e = tid; e <= E; e += kRankThreads)
+        off[e] = s_off[e];
+    for (int r = tid; r < R; r += kRankThreads)
+        ntpr[r] = s_rcnt[r];
+    if (tid == 0)
+        *error_flag = s_bad;
+
+    // rows holding no entry: alignment padding inside each expert (wave w
+    // takes experts w, w + 16, ...), then every row up to the capacity
+    for (int e = wave; e < E; e += kRankWaves) {
+        const int lo = s_off[e] + s_tot[e];
+        const int hi = s_off[e + 1];
+        for (int row = lo + lane; row < hi; row += kWave)
+            recv_src[row] = -1;
+    }
+    for (int64_t row = (int64_t)s_off[E] + tid; row < cap; row += kRankThreads)
+        recv_src[row] = -1;
+
+    // ranks: expert base + this wave's base + position among equal keys
+#pragma unroll
+    for (int it = 0; it < kIdxPerThread; ++it) {
+        if (it * kWave < per_wave) {
+            const int j = w_lo + it * kWave + lane;
+            const int e = e_reg[it];
+            const uint64_t same = same_reg[it];
+            const int below = count_below(same);
+            if (e >= 0) {
+                const int row = s_off[e] + s_w[wave][e] + below;
+                token_row[j] = row;
+                recv_src[row] = j;
+            } else if (j < w_hi) {
+                token_row[j] = -1;
+            }
+            if (e >= 0 && below == 0) // after every lane of the wave has read the running count
+                s_w[wave][e] = (int16_t)(s_w[wave][e] + __popcll(same));
+        }
+    }
+}
+
 static int key_bits(int E)
 {
     int b = 0;
@@ -415,6 +623,10 @@ hipError_t launch_layout(const LayoutArgs &A, const LayoutPlan &P, hipStream_t s
     const int L = A.E / A.R;
     const int nbits = key_bits(A.E);
     const int nchunks = P.num_chunks;
+    if (P.single)
+        return launch_kernel(layout_single_kernel, dim3(1), dim3(kRankThreads), 0, stream,
+                             A.topk_idx, A.T, A.K, A.E, A.R, L, A.a, nbits, A.cap, A.itr, A.ntpr,
+                             A.ntpe, A.nrtpe, A.off, A.token_row, A.recv_src, A.error_flag);
     int32_t *cnt_tab = A.workspace;
     int32_t *rank_tab = cnt_tab ? cnt_tab + (size_t)nchunks * ((A.E + 3) & ~3) : nullptr;
     int32_t *flag_tab = rank_tab ? rank_tab + (size_t)nchunks * A.R : nullptr;

@@ -98,9 +98,22 @@ def test_layout_capacity_errors(L, orc):
 def test_layout_rejects_null_outputs_and_small_workspace(L):
     cap = 100 * 4 + 16 * 7
     assert _layout_call(L, 100, 4, 16, 4, 8, cap, ptrs=False) == -1
-    need = L.moe_layout_workspace_bytes(100, 4, 16, 4)
-    assert _layout_call(L, 100, 4, 16, 4, 8, cap, ws=None) == -3
-    assert _layout_call(L, 100, 4, 16, 4, 8, cap, ws_bytes=need - 1) == -3
+    # a batch too large for the one-workgroup layout needs the count table
+    T = 3000
+    cap = T * 4 + 16 * 7
+    need = L.moe_layout_workspace_bytes(T, 4, 16, 4)
+    assert need > 0
+    assert _layout_call(L, T, 4, 16, 4, 8, cap, ws=None) == -3
+    assert _layout_call(L, T, 4, 16, 4, 8, cap, ws_bytes=need - 1) == -3
+    assert _layout_call(L, T, 4, 16, 4, 8, cap, ws=ctypes.c_void_p(0x1008)) == -3   # misaligned
+
+
+def test_small_batches_need_no_workspace(L):
+    # one workgroup takes the whole batch when T*K <= 4096 and T*R <= 16384
+    assert L.moe_layout_workspace_bytes(512, 8, 256, 8) == 0
+    assert L.moe_layout_workspace_bytes(4096, 1, 64, 4) == 0
+    assert L.moe_layout_workspace_bytes(513, 8, 256, 8) > 0
+    assert L.moe_layout_workspace_bytes(1024, 2, 512, 32) > 0     # T*R > 16384
 
 
 ROWS_CASES = [(16, 48, 4, 0), (16, 16, 4, 0), (16, 16416, 4, 0), (16, 1024, 4, 1), (16, 1024, 4, 3),
