@@ -59,6 +59,9 @@ def parse():
                    help="after timing, repetitions of the cold-cache legs: each stage timed alone "
                         "after 1 GiB of device traffic (a fill, or a read) has evicted L2 and the "
                         "memory-side cache (0 = skip)")
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of one captured HIP graph of the step instead of eager launches "
+                        "(stage times then come from an eager pass with events before it)")
     p.add_argument("--no-check", action="store_true", help="skip the post-run sanity check")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run 3 torch copies of 256 MiB: a kernel of known traffic "
@@ -355,10 +358,31 @@ def main():
     # stream the kernels use
     every = max(1, args.event_every)
     events = {i: [timer.new() for _ in range(4)] for i in range(0, args.steps, every)}
+    graph = None
+    if args.graph:
+        # stage times from an eager pass with events; then the step captured once
+        for i in range(args.steps):
+            step(events.get(i))
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events.get(i))
+    if graph is not None:
+        for i in range(args.steps):
+            graph.replay()
+    else:
+        for i in range(args.steps):
+            step(events.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -464,7 +488,10 @@ def main():
         "stage_bytes": sb,
         "stage_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
         "stage_median_us": {k: round(v, 2) for k, v in med_us.items()},
-        "stage_events": {"kind": timer.kind, "every_nth_step": every, "samples": len(events)},
+        "stage_events": {"kind": timer.kind, "every_nth_step": every, "samples": len(events),
+                         "timed_region": "eager pass before the graph replays" if graph is not None
+                         else "the timed steps"},
+        "launch": "graph replay" if graph is not None else "eager",
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic(w.name, dom),

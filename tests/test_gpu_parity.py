@@ -265,14 +265,15 @@ def test_pending_unrelated_hip_error_does_not_fail_calls():
     assert_layout_equal(layout_to_host(lay), oracle.layout(idx, 8, 2, 1))
 
 
-@pytest.mark.parametrize("quant", [0, 2, 4])
-def test_graph_capture_replays_match_eager(quant):
+@pytest.mark.parametrize("quant,T", [(0, 300), (2, 300), (4, 300), (0, 2000), (4, 2000)])
+def test_graph_capture_replays_match_eager(quant, T):
     """The three calls allocate nothing and never synchronise, so a step can be
     captured in a HIP graph.  Replay it several times, with eager work and
     synchronisations in between, and check every replay against the eager
-    result (layout, rows, scales, combine output)."""
-    rng = np.random.default_rng(40 + quant)
-    T, H, K, E, R, a = 300, 512, 4, 32, 4, 8
+    result (layout, rows, scales, combine output).  T = 300 takes the
+    one-workgroup layout, T = 2000 the two-launch one."""
+    rng = np.random.default_rng(40 + quant + T)
+    H, K, E, R, a = 512, 4, 32, 4, 8
     idx, wts = _routing(rng, T, K, E, drop=0.05)
     x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     idx_d = torch.from_numpy(idx).to(DEV)
