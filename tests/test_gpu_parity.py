@@ -318,15 +318,18 @@ def test_graph_capture_replays_match_eager(quant, T):
                 assert torch.equal(a_, b_)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "no_scales"])
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "no_scales", "wide_rows_odd_scales"])
 def test_dispatch_prequantized_parity(fmt):
     """Pre-quantised (data, scale) rows are copied byte for byte: whole
-    receive buffers equal the oracle's, sentinels included."""
+    receive buffers equal the oracle's, sentinels included.  The last case
+    takes 32 KiB rows (two 16-byte vectors per lane) and 5-byte scale rows."""
     rng = np.random.default_rng(zlib.crc32(fmt.encode()))
     T, H, K, E, R, a = 900, 7168, 8, 64, 8, 32
+    if fmt == "wide_rows_odd_scales":
+        T, H = 200, 16384
     idx, wts = _routing(rng, T, K, E, drop=0.05)
-    row_bytes = H if fmt == "mxfp8" else H // 2
-    scale_bytes = 0 if fmt == "no_scales" else H // 32
+    row_bytes = {"mxfp8": H, "mxfp4": H // 2, "no_scales": H // 2, "wide_rows_odd_scales": 2 * H}[fmt]
+    scale_bytes = {"no_scales": 0, "wide_rows_odd_scales": 5}.get(fmt, H // 32)
     data = rng.integers(0, 256, size=(T, row_bytes), dtype=np.uint8)
     sc = rng.integers(100, 140, size=(T, scale_bytes), dtype=np.uint8) if scale_bytes else None
     ol = oracle.layout(idx, E, R, a)
@@ -350,12 +353,14 @@ def test_dispatch_prequantized_parity(fmt):
     np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
 
 
-@pytest.mark.parametrize("per_channel", [False, True])
-def test_dispatch_static_parity(per_channel):
+@pytest.mark.parametrize("per_channel,H", [(False, 7168), (True, 7168), (False, 16384), (True, 16384),
+                                           (True, 96)])
+def test_dispatch_static_parity(per_channel, H):
     """Static int8 (caller scales, saturating): whole receive buffers equal
-    the oracle's, sentinels included."""
-    rng = np.random.default_rng(77 + per_channel)
-    T, H, K, E, R, a = 600, 7168, 8, 64, 8, 4
+    the oracle's, sentinels included.  H = 16384 takes two vectors per lane;
+    H = 96 a partial wave."""
+    rng = np.random.default_rng(77 + per_channel + H)
+    T, K, E, R, a = 600, 8, 64, 8, 4
     idx, wts = _routing(rng, T, K, E, drop=0.05)
     x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     if per_channel:
