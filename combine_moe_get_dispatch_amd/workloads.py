@@ -99,6 +99,10 @@ WORKLOADS = [
 # Further rows: the other 8-bit destinations the pages allow and the
 # pre-quantised tuple input, on the shapes of the measured workloads.
 NEXT_WORKLOADS = [
+    # a decode-sized batch at the headline's expert shape (one-workgroup layout)
+    Workload("bf16_128x7168_e256_top8_decode", 128, 7168, 256, 8, 8, 1, QUANT_NONE, seed_index=1),
+    Workload("fp8e4m3_128x7168_e256_top8_decode", 128, 7168, 256, 8, 8, 1,
+             QUANT_FP8_E4M3_PER_TOKEN, seed_index=1),
     Workload("fp8e4m3_pertoken_8192x7168_e256_top8_zipf", 8192, 7168, 256, 16, 8, 128,
              QUANT_FP8_E4M3_PER_TOKEN, routing="zipf", zipf_s=1.1, x_sigma=2.0, seed_index=2),
     Workload("fp8e5m2_pertoken_8192x7168_e256_top8_zipf", 8192, 7168, 256, 16, 8, 128,

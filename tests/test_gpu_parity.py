@@ -68,6 +68,18 @@ def test_workload_full_parity(w):
     print(f"{w.name}: combine max relative error {rel:.3e}")
 
 
+DECODE = [w for w in W.NEXT_WORKLOADS if w.name.endswith("_decode")]
+
+
+@pytest.mark.parametrize("w", DECODE, ids=[w.name for w in DECODE])
+def test_decode_workload_full_parity(w):
+    """Decode-sized batches (the one-workgroup layout) at the headline's
+    expert shape, whole path."""
+    inp = W.generate(w)
+    run_full_case(inp.x_bits, inp.topk_idx, inp.topk_weights, w.num_experts, w.num_ranks,
+                  w.expert_alignment, w.quant_mode)
+
+
 def test_large_workload_layout_full_rows_sampled():
     """32768 x 7168, 512 experts, top-16: layout compared in full; every
     dispatched row checked on the GPU against its source token; a sample of
