@@ -26,9 +26,12 @@
 // row is read from HBM exactly once and held in VGPRs; it is quantised there
 // once; then each of the K copies is written with 16-byte (bf16) or 8-byte
 // (1-byte codes) stores, one contiguous row per wave instruction group.  The
-// stores are nontemporal: every expanded row is written once and only read
-// again by the next stage, so it should not evict the routing tables from
-// L2.  Row offsets are 64-bit (the largest receive buffers exceed 4 GiB).
+// stores are nontemporal: every expanded row is written once and read only
+// by a later stage.  Ordinary stores finish this kernel sooner but leave up
+// to a few hundred MB dirty in the L2s and the memory-side cache, and the
+// write-back then slows the kernels that follow by more than was gained
+// (measured over whole steps).  Row offsets are 64-bit (the largest receive
+// buffers exceed 4 GiB).
 #include "device_common.h"
 #include "launch.h"
 
