@@ -550,3 +550,86 @@ def test_random_configurations(i):
     exact = oracle.combine(y_bits, ol.token_row, None)
     S = combine_bound(y_bits, ol.token_row, None, K)
     check_combine(bf16_host_bits(out), exact, S, K, north_star=False)
+
+
+BENCH_WORKLOADS = W.WORKLOADS + W.NEXT_WORKLOADS
+
+
+@pytest.mark.parametrize("w", BENCH_WORKLOADS, ids=[w.name for w in BENCH_WORKLOADS])
+def test_bench_workload_full_size_sampled(w):
+    """Every workload bench.py can time, at its full size and through the same
+    calls and launch configuration: the whole layout against the oracle; the
+    rows (codes, scales, weights) of a seeded sample of 256 tokens bit-exact;
+    the combine of the sample (with the fused epilogues where the workload
+    has them) within the combine bound, on seeded bf16 expert outputs."""
+    T, H, K, E, R, a = w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks, w.expert_alignment
+    print(f"[full-size] {w.name}", flush=True)
+    if w.prequant:
+        data, scales, idx, wts = W.generate_prequant(w)
+        x_bits = None
+    else:
+        inp = W.generate(w)
+        idx, wts, x_bits = inp.topk_idx, inp.topk_weights, inp.x_bits
+    ol = oracle.layout(idx, E, R, a)
+    lay = gpu_layout(idx, E, R, a)
+    assert_layout_equal(layout_to_host(lay), ol)
+    cap = ol.recv_capacity
+    w_dev = torch.from_numpy(wts).to(DEV)
+    rng = np.random.default_rng(zlib.crc32(w.name.encode()))
+    sample = np.sort(rng.choice(T, min(256, T), replace=False))
+    rows = ol.token_row[sample]                       # [S, K], -1 where dropped
+    sub_rows = np.where(rows >= 0, np.arange(rows.size, dtype=np.int32).reshape(rows.shape), -1).astype(np.int32)
+    take = torch.from_numpy(np.maximum(rows, 0).reshape(-1).astype(np.int64)).to(DEV)
+    valid = (rows >= 0).reshape(-1)
+
+    if w.prequant:
+        rd = torch.empty((cap, data.shape[1]), dtype=torch.uint8, device=DEV)
+        rsc = torch.empty((cap, scales.shape[1]), dtype=torch.uint8, device=DEV)
+        rw = torch.empty(cap, dtype=torch.float32, device=DEV)
+        moe.moe_dispatch_prequantized(torch.from_numpy(data).to(DEV), torch.from_numpy(scales).to(DEV), lay,
+                                      w_dev, rd, rsc, rw)
+        od, osc, ow = oracle.dispatch_prequantized(data[sample], scales[sample], sub_rows, rows.size,
+                                                   wts[sample], with_weights=True)
+        np.testing.assert_array_equal(rd[take].cpu().numpy()[valid], od[valid])
+        np.testing.assert_array_equal(rsc[take].cpu().numpy()[valid], osc[valid])
+    elif w.static_scale > 0:
+        sc = np.array([w.static_scale], np.float32)
+        rx = torch.empty((cap, H), dtype=torch.int8, device=DEV)
+        rw = torch.empty(cap, dtype=torch.float32, device=DEV)
+        moe.moe_dispatch_static(bf16_dev(x_bits), lay, torch.from_numpy(sc).to(DEV), w_dev, recv_x=rx,
+                                recv_weights=rw)
+        orx, ow = oracle.dispatch_static(x_bits[sample], sub_rows, rows.size, sc, wts[sample], with_weights=True)
+        np.testing.assert_array_equal(rx[take].cpu().numpy()[valid], orx[valid])
+    else:
+        rx, rs, rw = moe.allocate_recv(lay, H, w.quant_mode, with_weights=True)
+        moe.moe_dispatch(bf16_dev(x_bits), lay, w_dev, w.quant_mode, recv_x=rx, recv_scales=rs, recv_weights=rw)
+        orx, ors, ow = oracle.dispatch(x_bits[sample], sub_rows, rows.size, wts[sample], w.quant_mode,
+                                       with_weights=True)
+        np.testing.assert_array_equal(recv_to_host(rx[take], w.quant_mode)[valid], orx[valid])
+        if rs is not None:
+            got = rs[take].cpu().numpy()
+            if got.dtype == np.float32:
+                got, ors = got.view(np.uint32), ors.view(np.uint32)
+            np.testing.assert_array_equal(got[valid], ors[valid])
+    np.testing.assert_array_equal(rw[take].cpu().numpy()[valid], ow[valid])
+
+    # combine on seeded expert outputs; the sample's rows gathered for the oracle
+    y_sub = W.random_bf16_rows(rows.size, H, 31)
+    y = torch.zeros((cap, H), dtype=torch.bfloat16, device=DEV)
+    y[take[torch.from_numpy(valid).to(DEV)]] = bf16_dev(y_sub)[torch.from_numpy(valid).to(DEV)]
+    sel = torch.from_numpy(sample.astype(np.int64)).to(DEV)
+    if w.epilogue:
+        sh_bits, res_bits = W.random_bf16_rows(T, H, 21), W.random_bf16_rows(T, H, 22)
+        gamma_bits = np.full(H, 0x3F80, np.uint16)
+        out, out_norm = moe.moe_combine_fused(y, lay, w_dev, bf16_dev(sh_bits), bf16_dev(res_bits),
+                                              bf16_dev(gamma_bits), 1e-6)
+        exact, _ = oracle.combine_fused(y_sub, sub_rows, wts[sample], sh_bits[sample], res_bits[sample],
+                                        gamma_bits, 1e-6, with_norm=True)
+        S = combine_bound(y_sub, sub_rows, wts[sample], K) + np.abs(W.bf16_bits_to_f32(sh_bits[sample])) \
+            + np.abs(W.bf16_bits_to_f32(res_bits[sample]))
+        check_combine(bf16_host_bits(out[sel]), exact, S, K + 2, north_star=False)
+    else:
+        out = moe.moe_combine(y, lay, w_dev)
+        exact = oracle.combine(y_sub, sub_rows, wts[sample])
+        S = combine_bound(y_sub, sub_rows, wts[sample], K)
+        check_combine(bf16_host_bits(out[sel]), exact, S, K, north_star=False)
