@@ -4,19 +4,30 @@
  *
  * One step of a Mixture-of-Experts layer's token routing on one GPU:
  *
- *   moe_get_dispatch_layout   counts and a stable expert-grouped row for every
- *                             (token, k) routing entry
- *   moe_dispatch              copy (optionally quantise) every token into the
- *                             rows of its selected experts
- *   moe_combine               top-k weighted sum of every token's expert rows
+ *   moe_get_dispatch_layout    counts and a stable expert-grouped row for every
+ *                              (token, k) routing entry
+ *   moe_dispatch               copy every token into the rows of its selected
+ *                              experts, optionally quantised once per token
+ *                              (int8, FP8 per token or per group of 128, MX)
+ *   moe_dispatch_static        the same with int8 and caller-given scales
+ *   moe_dispatch_prequantized  the same for rows the caller has quantised
+ *                              (data and scale bytes moved unchanged)
+ *   moe_combine                top-k weighted sum of every token's expert rows
+ *   moe_combine_fused          the same plus shared-expert and residual adds
+ *                              and an optional RMS normalisation
+ * plus the size queries moe_recv_capacity_bound and moe_layout_workspace_bytes.
  *
  * Sources, by page title and section:
  *   sgl-kernel-npu deep_ep "Normal Mode API": dispatch Parameters, Return
- *     Values and Constraints; combine Description / Parameters.
- *   Huawei CANN "aclnnMoeDistributeDispatchV2": Formula Cases 1, 3 and 5;
- *     Constraints 1 (deterministic), 7 (shapes), 11 (integer division); the
- *     two-phase calling pattern (query the workspace size, then run).
- *   Modular MAX "EPBatchManager": ep_dispatch() and ep_combine() Returns.
+ *     Values, Constraints and Quantization Selection Priority; combine
+ *     Description / Parameters.
+ *   Huawei CANN "aclnnMoeDistributeDispatchV2": Formula Cases 1 to 5;
+ *     Constraints 1 (deterministic), 7 (shapes), 8 and 9 (destination types,
+ *     per-group sizing), 11 (integer division); the companion combine with
+ *     residual add and RMS normalisation; the two-phase calling pattern (query
+ *     the workspace size, then run).
+ *   Modular MAX "EPBatchManager": ep_dispatch() and ep_combine() Returns, and
+ *     the shared-expert mode of ep_combine().
  *
  * Conventions for every entry point:
  *   - Pointers named as device pointers must point to GPU memory that the
@@ -73,7 +84,9 @@ extern "C" {
 
 /* Limits.  Top-k and expert counts are the ranges of the Normal Mode API page
  * (Constraints: num_topk in (0, 16], num_experts in (0, 512]); hidden must be
- * a multiple of 32 (CANN page, Constraint 7 "H"; also the MX block). */
+ * a multiple of 32 (CANN page, Constraint 7 "H"; also the MX block).  The
+ * hidden size is at most 16384, a limit of this library: a token row is held
+ * in one 1024-lane workgroup, at most two 16-byte vectors per lane. */
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_HIDDEN 16384
