@@ -132,7 +132,7 @@ def combine_bound(y_bits, token_row, w, K):
     return S
 
 
-def check_combine(g_bits: np.ndarray, exact: np.ndarray, S: np.ndarray, K: int, north_star=True):
+def check_combine(g_bits: np.ndarray, exact: np.ndarray, S: np.ndarray, K: int, max_rel_1e2=True):
     g = W.bf16_bits_to_f32(g_bits).astype(np.float64)
     err = np.abs(g - exact)
     bound = 2.0 ** -8 * np.abs(exact) + (K + 1) * 2.0 ** -24 * S
@@ -140,7 +140,7 @@ def check_combine(g_bits: np.ndarray, exact: np.ndarray, S: np.ndarray, K: int, 
     assert not bad.any(), f"{bad.sum()} elements exceed the bound; worst {err[bad].max()}"
     zero = exact == 0
     assert (g[zero] == 0).all()
-    if north_star:
+    if max_rel_1e2:
         nz = ~zero
         rel = np.max(err[nz] / np.abs(exact[nz])) if nz.any() else 0.0
         assert rel <= 1e-2, rel

@@ -1,5 +1,5 @@
 /*
- * Host driver that runs every oracle entry point on small seeded inputs with
+ * Host program that runs every oracle entry point on small seeded inputs with
  * exactly sized heap buffers, built with AddressSanitizer and
  * UndefinedBehaviorSanitizer by tests/test_oracle_sanitize.py: an access
  * outside a buffer or undefined arithmetic in the oracle aborts the run.

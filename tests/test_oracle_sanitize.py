@@ -1,5 +1,5 @@
 """The oracle under AddressSanitizer and UndefinedBehaviorSanitizer (host code
-only): a C driver runs every entry point on small seeded inputs with exactly
+only): a C program runs every entry point on small seeded inputs with exactly
 sized buffers, including an empty batch, one token, 512 experts with top-16,
 alignment larger than every count, out-of-range expert ids and all quant
 modes."""
