@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="bf16_4096x7168_e256_top8")
+    p.add_argument("--tokens", type=int, default=0,
+                   help="draw the workload with this many tokens instead of its own T (0 = its own)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU time budget for the oracle baseline (0 = skip)")
     p.add_argument("--event-every", type=int, default=10,
@@ -261,6 +263,9 @@ def main():
     from combine_moe_get_dispatch_amd import workloads as W
 
     w = W.BY_NAME[args.workload]
+    if args.tokens > 0:
+        import dataclasses
+        w = dataclasses.replace(w, name=f"{w.name}@T{args.tokens}", num_tokens=args.tokens)
     T, H, K, E, R, a, quant = (w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
                                w.expert_alignment, w.quant_mode)
     dev = torch.device("cuda", 0)
