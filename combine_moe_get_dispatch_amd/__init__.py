@@ -128,6 +128,25 @@ def _check(t: torch.Tensor, name: str, dtype, shape=None, device=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _check_layout(layout, device=None, full: bool = False):
+    """The layout's tensors must match its sizes before any pointer of it goes
+    to a kernel (token_row always; every output with full=True)."""
+    T, K, E, R, cap = (layout.num_tokens, layout.num_topk, layout.num_experts, layout.num_ranks,
+                       layout.recv_capacity)
+    dev = layout.token_row.device if device is None else device
+    _check(layout.token_row, "layout.token_row", torch.int32, (T, K), dev)
+    if not full:
+        return
+    _check(layout.num_tokens_per_rank, "layout.num_tokens_per_rank", torch.int32, (R,), dev)
+    _check(layout.num_tokens_per_expert, "layout.num_tokens_per_expert", torch.int32, (E,), dev)
+    _check(layout.is_token_in_rank, "layout.is_token_in_rank", torch.int32, (T, R), dev)
+    _check(layout.num_recv_tokens_per_expert, "layout.num_recv_tokens_per_expert", torch.int32, (E,), dev)
+    _check(layout.expert_offsets, "layout.expert_offsets", torch.int32, (E + 1,), dev)
+    _check(layout.recv_src, "layout.recv_src", torch.int32, (max(cap, 0),), dev)
+    _check(layout.error_flag, "layout.error_flag", torch.int32, (1,), dev)
+    _check(layout.workspace, "layout.workspace", torch.uint8, device=dev)
+
+
 def moe_recv_capacity_bound(num_tokens: int, num_topk: int, num_experts: int,
                             expert_alignment: int) -> int:
     return int(lib().moe_recv_capacity_bound(num_tokens, num_topk, num_experts, expert_alignment))
@@ -192,6 +211,7 @@ def moe_get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks:
     elif (out.num_tokens, out.num_topk, out.num_experts, out.num_ranks, out.expert_alignment) != (
             T, K, num_experts, num_ranks, expert_alignment):
         raise ValueError("preallocated layout was made for other sizes")
+    _check_layout(out, topk_idx.device, full=True)
     rc = lib().moe_get_dispatch_layout(
         _ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, out.recv_capacity,
         _ptr(out.num_tokens_per_rank), _ptr(out.num_tokens_per_expert), _ptr(out.is_token_in_rank),
@@ -249,6 +269,7 @@ def moe_dispatch(x: torch.Tensor, layout: DispatchLayout, topk_weights: Optional
         raise ValueError(f"x must be [{T}, hidden]")
     H = x.shape[1]
     dev = x.device
+    _check_layout(layout, dev)
     _check(x, "x", torch.bfloat16, device=dev)
     if topk_weights is not None:
         _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)
@@ -287,6 +308,7 @@ def moe_dispatch_static(x: torch.Tensor, layout: DispatchLayout, scales: torch.T
         raise ValueError(f"x must be [{T}, hidden]")
     H = x.shape[1]
     dev = x.device
+    _check_layout(layout, dev)
     _check(x, "x", torch.bfloat16, device=dev)
     _check(scales, "scales", torch.float32, device=dev)
     if scales.numel() not in (1, H):
@@ -327,6 +349,7 @@ def moe_dispatch_prequantized(data: torch.Tensor, scales: Optional[torch.Tensor]
     recv_scales, recv_weights) with the input dtypes."""
     T, K, cap = layout.num_tokens, layout.num_topk, layout.recv_capacity
     dev = data.device
+    _check_layout(layout, dev)
     if dev.type != "cuda":
         raise ValueError("data must be on a HIP device")
     d8 = _bytes2d(data, "data", T, dev)
@@ -364,6 +387,7 @@ def moe_combine(expert_out: torch.Tensor, layout: DispatchLayout,
         raise ValueError(f"expert_out must be [{cap}, hidden]")
     H = expert_out.shape[1]
     dev = expert_out.device
+    _check_layout(layout, dev)
     _check(expert_out, "expert_out", torch.bfloat16, device=dev)
     if topk_weights is not None:
         _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)
@@ -392,6 +416,7 @@ def moe_combine_fused(expert_out: torch.Tensor, layout: DispatchLayout,
         raise ValueError(f"expert_out must be [{cap}, hidden]")
     H = expert_out.shape[1]
     dev = expert_out.device
+    _check_layout(layout, dev)
     _check(expert_out, "expert_out", torch.bfloat16, device=dev)
     if topk_weights is not None:
         _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)

@@ -633,3 +633,30 @@ def test_bench_workload_full_size_sampled(w):
         exact = oracle.combine(y_sub, sub_rows, wts[sample])
         S = combine_bound(y_sub, sub_rows, wts[sample], K)
         check_combine(bf16_host_bits(out[sel]), exact, S, K, max_rel_1e2=False)
+
+
+def test_binding_rejects_mismatched_layouts():
+    """A layout whose tensors do not match its sizes (truncated, wrong dtype)
+    is refused by the binding before any pointer reaches a kernel."""
+    import dataclasses
+    rng = np.random.default_rng(91)
+    T, H, K, E, R, a = 64, 256, 4, 16, 4, 2
+    idx, wts = _routing(rng, T, K, E)
+    lay = gpu_layout(idx, E, R, a)
+    x = bf16_dev(W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    y = torch.zeros((lay.recv_capacity, H), dtype=torch.bfloat16, device=DEV)
+    short = dataclasses.replace(lay, token_row=lay.token_row[:-1])
+    wide = dataclasses.replace(lay, token_row=lay.token_row.to(torch.int64))
+    for bad in (short, wide):
+        with pytest.raises((ValueError, TypeError)):
+            moe.moe_dispatch(x, bad)
+        with pytest.raises((ValueError, TypeError)):
+            moe.moe_combine(y, bad)
+        with pytest.raises((ValueError, TypeError)):
+            moe.moe_combine_fused(y, bad)
+    with pytest.raises(ValueError):
+        moe.moe_get_dispatch_layout(torch.from_numpy(idx).to(DEV), E, R, a,
+                                    out=dataclasses.replace(lay, recv_src=lay.recv_src[:-1]))
+    # the genuine layout still works
+    moe.moe_combine(y, lay)
+    torch.cuda.synchronize()
