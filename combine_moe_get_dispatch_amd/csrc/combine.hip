@@ -218,9 +218,10 @@ static hipError_t launch_slices(int K, int64_t T, int nvec, hipStream_t stream, 
                                 const int32_t *token_row, const float *w, int64_t cap,
                                 const u32x4 *sh, const u32x4 *res, u32x4 *out)
 {
-    const int nslices = (nvec + kWave - 1) / kWave;
-    const int64_t nitems = T * nslices;
-    const dim3 grid((unsigned)(nitems < kMaxGrid ? nitems : kMaxGrid)), block(kWave);
+    const SliceGrid g = slice_grid(T, nvec, 1);
+    const int nslices = g.nslices;
+    const int64_t nitems = g.nitems;
+    const dim3 grid(g.blocks), block(kWave);
     if (K <= 1)
         return launch_kernel(combine_slice_kernel<1>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
     if (K <= 2)

@@ -21,17 +21,22 @@
 //   pre-quantised rows (the Normal Mode API page's (data, scale) tuple input):
 //               data row and scale row copied unchanged
 //
-// Design (gfx950): one workgroup per token, one 16-byte vector per lane
-// (896 lanes for H = 7168; two vectors per lane above H = 8192).  The token
-// row is read from HBM exactly once and held in VGPRs; it is quantised there
-// once; then each of the K copies is written with 16-byte (bf16) or 8-byte
-// (1-byte codes) stores, one contiguous row per wave instruction group.  The
-// stores are nontemporal: every expanded row is written once and read only
-// by a later stage.  Ordinary stores finish this kernel sooner but leave up
-// to a few hundred MB dirty in the L2s and the memory-side cache, and the
-// write-back then slows the kernels that follow by more than was gained
-// (measured over whole steps).  Row offsets are 64-bit (the largest receive
-// buffers exceed 4 GiB).
+// Design (gfx950): every 16-byte vector of x (8 bf16 elements) is read from
+// HBM exactly once, held in a VGPR, quantised there once, and then written
+// to each of the token's K rows with 16-byte (bf16) or 8-byte (1-byte codes)
+// stores.  Two launch shapes:
+//   - slices (bf16, MX, per group, static, pre-quantised rows): one wave per
+//     (token, 64-vector slice of its row), four waves per workgroup, so each
+//     wave reads 1 KiB of x and writes 1 KiB (or 512 bytes) to each row;
+//   - one workgroup per token (per-token scales, which need the maximum over
+//     the whole row): one vector per lane, 896 lanes at H = 7168, two vectors
+//     per lane above H = 8192, the row maximum through LDS.
+// The stores are nontemporal: every expanded row is written once and read
+// only by a later stage.  Ordinary stores finish this kernel sooner but
+// leave up to a few hundred MB dirty in the L2s and the memory-side cache,
+// and the write-back then slows the kernels that follow by more than was
+// gained (measured over whole steps).  Row offsets are 64-bit (the largest
+// receive buffers exceed 4 GiB).
 #include "device_common.h"
 #include "launch.h"
 
@@ -104,49 +109,57 @@ template <> struct DstTraits<Dst::E5M2> {
 __device__ __forceinline__ uint32_t sign_lo(uint32_t w) { return (w >> 8) & 0x80u; }
 __device__ __forceinline__ uint32_t sign_hi(uint32_t w) { return (w >> 24) & 0x80u; }
 
+// recv_weights[row(t, k)] = topk_weights[t, k] (1 without weights), written by
+// thread `tid` == k of the token's workgroup or wave
 __device__ __forceinline__ void write_row_weight(const int32_t *__restrict__ token_row,
                                                  const float *__restrict__ topk_weights,
-                                                 float *__restrict__ recv_weights, int t, int K,
-                                                 int64_t cap)
+                                                 float *__restrict__ recv_weights, int64_t t, int K,
+                                                 int64_t cap, int tid = (int)threadIdx.x)
 {
-    const int tid = threadIdx.x;
     if (recv_weights && tid < K) {
-        const int row = token_row[(int64_t)t * K + tid];
+        const int row = token_row[t * K + tid];
         if (row >= 0 && row < cap)
-            recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + tid] : 1.0f;
+            recv_weights[row] = topk_weights ? topk_weights[t * K + tid] : 1.0f;
     }
 }
 
-// --------------------------------------------------------------------------- bf16
+// --------------------------------------------------------------------------- bf16 (slices)
 
-template <int VPT>
-__global__ __launch_bounds__(kRowMaxThreads) void dispatch_bf16_kernel(
-    const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
-    const float *__restrict__ topk_weights, int64_t cap, u32x4 *__restrict__ recv,
-    float *__restrict__ recv_weights)
+// Rows copied unchanged need no row-wide value, so they are cut finer: one
+// wave per (token, 64-vector slice of its row), kSliceWaves waves per
+// workgroup, grid-stride beyond kMaxGrid workgroups.  A wave reads 1 KiB of
+// the token's row once and writes it to each of the K rows.  Small
+// workgroups give every CU its full 32 waves and many short-lived
+// independent items, which hides the latency of reading x from HBM:
+// measured against one 896-lane workgroup per token, equal at 4096 tokens
+// with x in the memory-side cache, 7-11 % faster at 4096-8192 tokens after
+// a cache flush, and 5-9 % faster at 32768 tokens (x beyond the cache).
+// The item index is left in vector registers on purpose: made wave-uniform
+// (readfirstlane), it turns the K token_row reads into scalar loads that
+// each stall the store loop, 6 % slower at 32768 tokens x top-16.
+__global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_bf16_slice_kernel(
+    const u32x4 *__restrict__ x, int nvec, int nslices, int64_t nitems, int K,
+    const int32_t *__restrict__ token_row, const float *__restrict__ topk_weights, int64_t cap,
+    u32x4 *__restrict__ recv, float *__restrict__ recv_weights)
 {
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const u32x4 *xt = x + (int64_t)t * nvec;
-    u32x4 v[VPT];
-    // branch-free loads (index clamped into the row) keep all VPT loads in flight
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-        v[j] = xt[min(tid + j * nthr, nvec - 1)];
-    for (int k = 0; k < K; ++k) {
-        const int row = token_row[(int64_t)t * K + k];
-        if (row < 0 || row >= cap)
-            continue;
-        u32x4 *dst = recv + (int64_t)row * nvec;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * nthr;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = (int)threadIdx.x / kWave;
+    for (int64_t b = (int64_t)blockIdx.x * kSliceWaves + wave; b < nitems;
+         b += (int64_t)gridDim.x * kSliceWaves) {
+        const int64_t t = b / nslices;
+        const int s = (int)(b - t * nslices);
+        const int i = s * kWave + lane;
+        const u32x4 v = x[t * nvec + min(i, nvec - 1)]; // clamped: always in bounds
+        for (int k = 0; k < K; ++k) {
+            const int row = token_row[t * K + k];
+            if (row < 0 || row >= cap)
+                continue;
             if (i < nvec)
-                __builtin_nontemporal_store(v[j], dst + i);
+                __builtin_nontemporal_store(v, recv + (int64_t)row * nvec + i);
         }
+        if (s == 0)
+            write_row_weight(token_row, topk_weights, recv_weights, t, K, cap, lane);
     }
-    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
 }
 
 // --------------------------------------------------------------------------- per-token dynamic
@@ -219,30 +232,29 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_pertoken_kernel(
     write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
 }
 
-// --------------------------------------------------------------------------- MX (32-element blocks)
+// --------------------------------------------------------------------------- element-wise codecs (slices)
 
-template <int VPT, Dst D>
-__global__ __launch_bounds__(kRowMaxThreads) void dispatch_mx_kernel(
-    const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
-    const float *__restrict__ topk_weights, int64_t cap, u32x2 *__restrict__ recv,
-    uint8_t *__restrict__ recv_scales, float *__restrict__ recv_weights)
-{
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int nblk = nvec / 4; // 32-element blocks per row; 4 lanes (8 elements each) per block
-    const u32x4 *xt = x + (int64_t)t * nvec;
-    u32x4 xin[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-        xin[j] = xt[min(tid + j * nthr, nvec - 1)]; // clamped: always in bounds
-    u32x2 q[VPT];
-    uint32_t sbyte[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        // lanes past the row end hold a copy of the row's last vector; since
-        // nvec % 4 == 0 a 4-lane block is entirely real or entirely such copies
-        const u32x4 xv = xin[j];
+// MX, per-group and static quantisation need no value wider than 128
+// elements, so they run in the slice form of the bf16 copy: one wave per
+// (token, 64-vector slice).  Each lane encodes its 8 elements once into 8
+// code bytes plus, where the format has one, its share of the scale row;
+// the codes are then stored to each of the K rows.  A codec provides
+//   encode(xv, i, aux) -> the lane's 8 codes (i = clamped vector index,
+//                         aux = the lane's scale payload)
+//   store_scale(row, i, aux)  -> its scale bytes for one destination row.
+// Measured against one workgroup per token: equal with x in the
+// memory-side cache; per group 10 % faster after a cache flush and 8 %
+// faster at 32768 tokens, MX 2.5 % faster at 32768 tokens.
+
+// MX (32-element blocks, one e8m0 byte each): a block is 4 lanes of 8
+// elements.  Lanes past the row end hold a copy of the row's last vector;
+// since nvec % 4 == 0 a 4-lane block is entirely real or entirely such
+// copies.
+template <Dst D> struct MxCodec {
+    uint8_t *__restrict__ scales; // [cap, nvec / 4]
+    int nblk;
+    __device__ u32x2 encode(const u32x4 xv, int, uint32_t &aux) const
+    {
         float m = 0.0f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_mx_kernel(
         const int ebits = (int)((__float_as_uint(m) >> 23) & 0xFFu);
         const int se = max(ebits - 127 - DstTraits<D>::kEmax, -127);
         const float inv = __uint_as_float((uint32_t)(127 - se) << 23); // 2^-se, normal for se in [-127, 119]
-        sbyte[j] = (uint32_t)(se + 127);
+        aux = (uint32_t)(se + 127);
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -266,54 +278,26 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_mx_kernel(
             const uint32_t hi = DstTraits<D>::code(bf16_hi(xv[c]) * inv, sign_hi(xv[c]));
             w[c >> 1] |= (lo | (hi << 8)) << (16 * (c & 1));
         }
-        q[j] = u32x2{w[0], w[1]};
+        return u32x2{w[0], w[1]};
     }
-
-    for (int k = 0; k < K; ++k) {
-        const int row = token_row[(int64_t)t * K + k];
-        if (row < 0 || row >= cap)
-            continue;
-        u32x2 *dst = recv + (int64_t)row * nvec;
-        uint8_t *sdst = recv_scales + (int64_t)row * nblk;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * nthr;
-            if (i < nvec) {
-                __builtin_nontemporal_store(q[j], dst + i);
-                if ((i & 3) == 0)
-                    sdst[i >> 2] = (uint8_t)sbyte[j];
-            }
-        }
+    __device__ void store_scale(int64_t row, int i, uint32_t aux) const
+    {
+        if ((i & 3) == 0)
+            scales[row * nblk + (i >> 2)] = (uint8_t)aux;
     }
-    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
-}
+};
 
-// --------------------------------------------------------------------------- per-group dynamic
-
-// A group of 128 elements is 16 lanes x 8 elements; 16-lane groups are
-// aligned inside the wave.  Lanes past the row end hold copies of the row's
-// last vector, which belongs to the row's last (possibly partial) group, so
-// they cannot change any group's maximum.
-template <int VPT, Dst D>
-__global__ __launch_bounds__(kRowMaxThreads) void dispatch_pergroup_kernel(
-    const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
-    const float *__restrict__ topk_weights, int64_t cap, u32x2 *__restrict__ recv,
-    float *__restrict__ recv_scales, float *__restrict__ recv_weights)
-{
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int ngroups = (nvec + 15) / 16;
-    const u32x4 *xt = x + (int64_t)t * nvec;
-    u32x4 xin[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-        xin[j] = xt[min(tid + j * nthr, nvec - 1)]; // clamped: always in bounds
-    u32x2 q[VPT];
-    float gscale[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const u32x4 xv = xin[j];
+// Per group of 128 elements (16 lanes x 8 elements; 16-lane groups are
+// aligned inside the wave, and slices start at multiples of 64 vectors):
+// the per-token formula on each group, one fp32 scale per group.  Lanes
+// past the row end hold copies of the row's last vector, which belongs to
+// the row's last (possibly partial) group, so they cannot change any
+// group's maximum.
+template <Dst D> struct GroupCodec {
+    float *__restrict__ scales; // [cap, ceil(nvec / 16)]
+    int ngroups;
+    __device__ u32x2 encode(const u32x4 xv, int, uint32_t &aux) const
+    {
         float m = 0.0f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -325,7 +309,7 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_pergroup_kernel(
             m = fmaxf(m, __shfl_xor(m, o, kWave));
         const float ds = DstTraits<D>::kMax / m; // IEEE division
         const bool degenerate = !(ds <= 3.402823466e38f);
-        gscale[j] = 1.0f / ds;
+        aux = __float_as_uint(1.0f / ds);
         uint32_t w[2] = {0u, 0u};
         if (!degenerate) {
 #pragma unroll
@@ -335,122 +319,124 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_pergroup_kernel(
                 w[c >> 1] |= (lo | (hi << 8)) << (16 * (c & 1));
             }
         }
-        q[j] = u32x2{w[0], w[1]};
+        return u32x2{w[0], w[1]};
     }
-
-    for (int k = 0; k < K; ++k) {
-        const int row = token_row[(int64_t)t * K + k];
-        if (row < 0 || row >= cap)
-            continue;
-        u32x2 *dst = recv + (int64_t)row * nvec;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * nthr;
-            if (i < nvec) {
-                __builtin_nontemporal_store(q[j], dst + i);
-                if ((i & 15) == 0)
-                    recv_scales[(int64_t)row * ngroups + (i >> 4)] = gscale[j];
-            }
-        }
+    __device__ void store_scale(int64_t row, int i, uint32_t aux) const
+    {
+        if ((i & 15) == 0)
+            scales[row * ngroups + (i >> 4)] = __uint_as_float(aux);
     }
-    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
-}
+};
 
-// --------------------------------------------------------------------------- static int8
-
-template <int VPT>
-__global__ __launch_bounds__(kRowMaxThreads) void dispatch_static_kernel(
-    const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
-    const float *__restrict__ topk_weights, int64_t cap, const float *__restrict__ scales,
-    int per_channel, u32x2 *__restrict__ recv, float *__restrict__ recv_weights)
-{
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const u32x4 *xt = x + (int64_t)t * nvec;
-    const float4 *sc4 = (const float4 *)scales;
-    u32x4 xin[VPT];
-    float4 s_lo[VPT], s_hi[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const int i = min(tid + j * nthr, nvec - 1); // clamped: always in bounds
-        xin[j] = xt[i];
-        if (per_channel) { // uniform: the 8 channel scales of this vector
-            s_lo[j] = sc4[2 * i];
-            s_hi[j] = sc4[2 * i + 1];
+// Static int8 with the caller's scales: one coefficient, or one per channel
+// (the 8 channel scales of vector i as two 16-byte loads).  No scale output.
+struct StaticCodec {
+    const float *__restrict__ scales; // [1] or [H], 16-byte aligned when [H]
+    int per_channel;
+    __device__ u32x2 encode(const u32x4 xv, int i, uint32_t &) const
+    {
+        float4 s_lo, s_hi;
+        if (per_channel) { // uniform
+            const float4 *sc4 = (const float4 *)scales;
+            s_lo = sc4[2 * i];
+            s_hi = sc4[2 * i + 1];
         } else {
             const float s0 = scales[0];
-            s_lo[j] = float4{s0, s0, s0, s0};
-            s_hi[j] = s_lo[j];
+            s_lo = float4{s0, s0, s0, s0};
+            s_hi = s_lo;
         }
-    }
-    u32x2 q[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const float sv[8] = {s_lo[j].x, s_lo[j].y, s_lo[j].z, s_lo[j].w,
-                             s_hi[j].x, s_hi[j].y, s_hi[j].z, s_hi[j].w};
+        const float sv[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             // one fp32 multiply, round half to even, saturate to [-128, 127]
-            const float lo = fminf(fmaxf(__builtin_rintf(bf16_lo(xin[j][c]) * sv[2 * c]), -128.0f), 127.0f);
-            const float hi = fminf(fmaxf(__builtin_rintf(bf16_hi(xin[j][c]) * sv[2 * c + 1]), -128.0f), 127.0f);
+            const float lo = fminf(fmaxf(__builtin_rintf(bf16_lo(xv[c]) * sv[2 * c]), -128.0f), 127.0f);
+            const float hi = fminf(fmaxf(__builtin_rintf(bf16_hi(xv[c]) * sv[2 * c + 1]), -128.0f), 127.0f);
             const uint32_t b = ((uint32_t)(int)lo & 0xFFu) | (((uint32_t)(int)hi & 0xFFu) << 8);
             w[c >> 1] |= b << (16 * (c & 1));
         }
-        q[j] = u32x2{w[0], w[1]};
+        return u32x2{w[0], w[1]};
     }
-    for (int k = 0; k < K; ++k) {
-        const int row = token_row[(int64_t)t * K + k];
-        if (row < 0 || row >= cap)
-            continue;
-        u32x2 *dst = recv + (int64_t)row * nvec;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * nthr;
-            if (i < nvec)
-                __builtin_nontemporal_store(q[j], dst + i);
+    __device__ void store_scale(int64_t, int, uint32_t) const {}
+};
+
+template <class Codec>
+__global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_codec_slice_kernel(
+    const u32x4 *__restrict__ x, int nvec, int nslices, int64_t nitems, int K,
+    const int32_t *__restrict__ token_row, const float *__restrict__ topk_weights, int64_t cap,
+    u32x2 *__restrict__ recv, float *__restrict__ recv_weights, const Codec codec)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = (int)threadIdx.x / kWave; // kept in vector registers, as in the bf16 kernel
+    for (int64_t b = (int64_t)blockIdx.x * kSliceWaves + wave; b < nitems;
+         b += (int64_t)gridDim.x * kSliceWaves) {
+        const int64_t t = b / nslices;
+        const int s = (int)(b - t * nslices);
+        const int i = s * kWave + lane;
+        const int ic = min(i, nvec - 1); // clamped: always in bounds
+        uint32_t aux = 0u;
+        const u32x2 q = codec.encode(x[t * nvec + ic], ic, aux);
+        for (int k = 0; k < K; ++k) {
+            const int row = token_row[t * K + k];
+            if (row < 0 || row >= cap)
+                continue;
+            if (i < nvec) {
+                __builtin_nontemporal_store(q, recv + (int64_t)row * nvec + i);
+                codec.store_scale(row, i, aux);
+            }
         }
+        if (s == 0)
+            write_row_weight(token_row, topk_weights, recv_weights, t, K, cap, lane);
     }
-    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
 }
 
 // --------------------------------------------------------------------------- pre-quantised rows
 
-template <int VPT>
-__global__ __launch_bounds__(kRowMaxThreads) void dispatch_rows_kernel(
-    const u32x4 *__restrict__ data, int nvec, const uint8_t *__restrict__ scales, int scale_bytes,
-    int K, const int32_t *__restrict__ token_row, const float *__restrict__ topk_weights,
-    int64_t cap, u32x4 *__restrict__ recv_data, uint8_t *__restrict__ recv_scales,
+// As the bf16 slices: one wave per (token, 64-vector slice of the data row);
+// the scale row's bytes are spread over the token's slices, one byte per
+// lane (H/32 bytes for MX data: 224 at H = 7168).
+__global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_rows_slice_kernel(
+    const u32x4 *__restrict__ data, int nvec, int nslices, int64_t nitems,
+    const uint8_t *__restrict__ scales, int scale_bytes, int K,
+    const int32_t *__restrict__ token_row, const float *__restrict__ topk_weights, int64_t cap,
+    u32x4 *__restrict__ recv_data, uint8_t *__restrict__ recv_scales,
     float *__restrict__ recv_weights)
 {
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const u32x4 *dt = data + (int64_t)t * nvec;
-    u32x4 v[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-        v[j] = dt[min(tid + j * nthr, nvec - 1)]; // clamped: always in bounds
-    for (int k = 0; k < K; ++k) {
-        const int row = token_row[(int64_t)t * K + k];
-        if (row < 0 || row >= cap)
-            continue;
-        u32x4 *dst = recv_data + (int64_t)row * nvec;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * nthr;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = (int)threadIdx.x / kWave;
+    for (int64_t b = (int64_t)blockIdx.x * kSliceWaves + wave; b < nitems;
+         b += (int64_t)gridDim.x * kSliceWaves) {
+        const int64_t t = b / nslices;
+        const int s = (int)(b - t * nslices);
+        const int i = s * kWave + lane;
+        const u32x4 v = data[t * nvec + min(i, nvec - 1)]; // clamped: always in bounds
+        for (int k = 0; k < K; ++k) {
+            const int row = token_row[t * K + k];
+            if (row < 0 || row >= cap)
+                continue;
             if (i < nvec)
-                __builtin_nontemporal_store(v[j], dst + i);
+                __builtin_nontemporal_store(v, recv_data + (int64_t)row * nvec + i);
+            // the scale row is small: re-read from cache per copy
+            for (int j = i; j < scale_bytes; j += nslices * kWave)
+                recv_scales[(int64_t)row * scale_bytes + j] = scales[t * scale_bytes + j];
         }
-        // the scale row (H/32 bytes for MX data) is small: re-read from cache per copy
-        for (int i = tid; i < scale_bytes; i += nthr)
-            recv_scales[(int64_t)row * scale_bytes + i] = scales[(int64_t)t * scale_bytes + i];
+        if (s == 0)
+            write_row_weight(token_row, topk_weights, recv_weights, t, K, cap, lane);
     }
-    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
 }
 
 // --------------------------------------------------------------------------- launch
+
+template <class Codec>
+static hipError_t launch_codec(const Codec &codec, const SliceGrid &g, hipStream_t stream,
+                               const u32x4 *x, int nvec, int K, const int32_t *token_row,
+                               const float *topk_weights, int64_t cap, u32x2 *recv,
+                               float *recv_weights)
+{
+    return launch_kernel(dispatch_codec_slice_kernel<Codec>, dim3(g.blocks),
+                         dim3(kSliceWaves * kWave), 0, stream, x, nvec, g.nslices, g.nitems, K,
+                         token_row, topk_weights, cap, recv, recv_weights, codec);
+}
 
 template <int V>
 static hipError_t launch_dispatch_v(dim3 grid, dim3 block, hipStream_t stream, const u32x4 *xv,
@@ -459,9 +445,6 @@ static hipError_t launch_dispatch_v(dim3 grid, dim3 block, hipStream_t stream, c
                                     void *recv_x, void *recv_scales, float *recv_weights)
 {
     switch (quant_mode) {
-    case MOE_QUANT_NONE:
-        return launch_kernel(dispatch_bf16_kernel<V>, grid, block, 0, stream, xv, nvec, K,
-                             token_row, topk_weights, cap, (u32x4 *)recv_x, recv_weights);
     case MOE_QUANT_INT8_PER_TOKEN:
         return launch_kernel(dispatch_pertoken_kernel<V, Dst::Int8>, grid, block, 0, stream, xv,
                              nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x,
@@ -472,22 +455,6 @@ static hipError_t launch_dispatch_v(dim3 grid, dim3 block, hipStream_t stream, c
                              (float *)recv_scales, recv_weights);
     case MOE_QUANT_FP8_E5M2_PER_TOKEN:
         return launch_kernel(dispatch_pertoken_kernel<V, Dst::E5M2>, grid, block, 0, stream, xv,
-                             nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x,
-                             (float *)recv_scales, recv_weights);
-    case MOE_QUANT_MXFP8_E4M3:
-        return launch_kernel(dispatch_mx_kernel<V, Dst::E4M3>, grid, block, 0, stream, xv, nvec,
-                             K, token_row, topk_weights, cap, (u32x2 *)recv_x,
-                             (uint8_t *)recv_scales, recv_weights);
-    case MOE_QUANT_MXFP8_E5M2:
-        return launch_kernel(dispatch_mx_kernel<V, Dst::E5M2>, grid, block, 0, stream, xv, nvec,
-                             K, token_row, topk_weights, cap, (u32x2 *)recv_x,
-                             (uint8_t *)recv_scales, recv_weights);
-    case MOE_QUANT_FP8_E4M3_PER_GROUP:
-        return launch_kernel(dispatch_pergroup_kernel<V, Dst::E4M3>, grid, block, 0, stream, xv,
-                             nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x,
-                             (float *)recv_scales, recv_weights);
-    case MOE_QUANT_FP8_E5M2_PER_GROUP:
-        return launch_kernel(dispatch_pergroup_kernel<V, Dst::E5M2>, grid, block, 0, stream, xv,
                              nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x,
                              (float *)recv_scales, recv_weights);
     default:
@@ -502,6 +469,30 @@ hipError_t launch_dispatch(const void *x, int T, int H, int K, const int32_t *to
     if (T == 0)
         return hipSuccess;
     const int nvec = H / 8; // 16-byte vectors of bf16 per row
+    const SliceGrid g = slice_grid(T, nvec, kSliceWaves);
+    const dim3 sgrid(g.blocks), sblock(kSliceWaves * kWave);
+    const u32x4 *xs = (const u32x4 *)x;
+    u32x2 *rq = (u32x2 *)recv_x;
+    switch (quant_mode) {
+    case MOE_QUANT_NONE:
+        return launch_kernel(dispatch_bf16_slice_kernel, sgrid, sblock, 0, stream, xs, nvec,
+                             g.nslices, g.nitems, K, token_row, topk_weights, cap,
+                             (u32x4 *)recv_x, recv_weights);
+    case MOE_QUANT_MXFP8_E4M3:
+        return launch_codec(MxCodec<Dst::E4M3>{(uint8_t *)recv_scales, nvec / 4}, g, stream, xs,
+                            nvec, K, token_row, topk_weights, cap, rq, recv_weights);
+    case MOE_QUANT_MXFP8_E5M2:
+        return launch_codec(MxCodec<Dst::E5M2>{(uint8_t *)recv_scales, nvec / 4}, g, stream, xs,
+                            nvec, K, token_row, topk_weights, cap, rq, recv_weights);
+    case MOE_QUANT_FP8_E4M3_PER_GROUP:
+        return launch_codec(GroupCodec<Dst::E4M3>{(float *)recv_scales, (nvec + 15) / 16}, g,
+                            stream, xs, nvec, K, token_row, topk_weights, cap, rq, recv_weights);
+    case MOE_QUANT_FP8_E5M2_PER_GROUP:
+        return launch_codec(GroupCodec<Dst::E5M2>{(float *)recv_scales, (nvec + 15) / 16}, g,
+                            stream, xs, nvec, K, token_row, topk_weights, cap, rq, recv_weights);
+    default: // per token: one workgroup per token (below)
+        break;
+    }
     const int threads = row_block_threads(nvec);
     const int vpt = (nvec + threads - 1) / threads; // 1 or 2 (H <= 16384)
     const dim3 grid(T), block(threads);
@@ -521,17 +512,9 @@ hipError_t launch_dispatch_static(const void *x, int T, int H, int K, const int3
     if (T == 0)
         return hipSuccess;
     const int nvec = H / 8;
-    const int threads = row_block_threads(nvec);
-    const int vpt = (nvec + threads - 1) / threads;
-    const dim3 grid(T), block(threads);
-    const int per_channel = num_scales == H ? 1 : 0;
-    if (vpt == 1)
-        return launch_kernel(dispatch_static_kernel<1>, grid, block, 0, stream, (const u32x4 *)x,
-                             nvec, K, token_row, topk_weights, cap, scales, per_channel,
-                             (u32x2 *)recv_x, recv_weights);
-    return launch_kernel(dispatch_static_kernel<2>, grid, block, 0, stream, (const u32x4 *)x, nvec,
-                         K, token_row, topk_weights, cap, scales, per_channel, (u32x2 *)recv_x,
-                         recv_weights);
+    const SliceGrid g = slice_grid(T, nvec, kSliceWaves);
+    return launch_codec(StaticCodec{scales, num_scales == H ? 1 : 0}, g, stream, (const u32x4 *)x,
+                        nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x, recv_weights);
 }
 
 hipError_t launch_dispatch_rows(const void *data, int T, int row_bytes, const void *scales,
@@ -542,15 +525,9 @@ hipError_t launch_dispatch_rows(const void *data, int T, int row_bytes, const vo
     if (T == 0)
         return hipSuccess;
     const int nvec = row_bytes / 16;
-    const int threads = row_block_threads(nvec);
-    const int vpt = (nvec + threads - 1) / threads; // 1 or 2 (row_bytes <= 32768)
-    const dim3 grid(T), block(threads);
-    if (vpt == 1)
-        return launch_kernel(dispatch_rows_kernel<1>, grid, block, 0, stream, (const u32x4 *)data,
-                             nvec, (const uint8_t *)scales, scale_bytes, K, token_row,
-                             topk_weights, cap, (u32x4 *)recv_data, (uint8_t *)recv_scales,
-                             recv_weights);
-    return launch_kernel(dispatch_rows_kernel<2>, grid, block, 0, stream, (const u32x4 *)data, nvec,
+    const SliceGrid g = slice_grid(T, nvec, kSliceWaves);
+    return launch_kernel(dispatch_rows_slice_kernel, dim3(g.blocks), dim3(kSliceWaves * kWave), 0,
+                         stream, (const u32x4 *)data, nvec, g.nslices, g.nitems,
                          (const uint8_t *)scales, scale_bytes, K, token_row, topk_weights, cap,
                          (u32x4 *)recv_data, (uint8_t *)recv_scales, recv_weights);
 }

@@ -33,10 +33,10 @@ hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
                              std::index_sequence_for<KArgs...>{});
 }
 
-// Launch shape of the row kernels (dispatch, combine): one workgroup per
-// token, one 16-byte vector per lane; the workgroup covers the row with
-// ceil(nvec / 64) waves (at most 16), and a lane takes a second vector only
-// when the row has more than 1024 vectors (H > 8192).
+// Launch shape of the row kernels (per-token dispatch, normalised combine):
+// one workgroup per token, one 16-byte vector per lane; the workgroup covers
+// the row with ceil(nvec / 64) waves (at most 16), and a lane takes a second
+// vector only when the row has more than 1024 vectors (H > 8192).
 constexpr int kRowMaxThreads = 1024;
 // Upper bound on the grid of grid-stride kernels (work items beyond it are
 // taken by the same workgroups in later iterations).  A test build lowers it
@@ -49,6 +49,26 @@ inline int row_block_threads(int nvec)
 {
     const int t = (nvec + 63) / 64 * 64;
     return t < kRowMaxThreads ? t : kRowMaxThreads;
+}
+
+// Launch shape of the slice kernels: one wave per (token, 64-vector slice of
+// the row), `waves` such items per workgroup, at most kMaxGrid workgroups
+// (grid-stride beyond).  Unquantised and pre-quantised dispatch use four
+// waves per workgroup, combine one.
+constexpr int kSliceWaves = 4;
+struct SliceGrid {
+    int nslices;    // slices per row
+    int64_t nitems; // T * nslices
+    unsigned blocks;
+};
+inline SliceGrid slice_grid(int64_t T, int nvec, int waves)
+{
+    SliceGrid g;
+    g.nslices = (nvec + 63) / 64;
+    g.nitems = T * g.nslices;
+    const int64_t b = (g.nitems + waves - 1) / waves;
+    g.blocks = (unsigned)(b < kMaxGrid ? b : kMaxGrid);
+    return g;
 }
 
 // How the layout splits the T*K routing entries into chunks of whole tokens.

@@ -505,6 +505,81 @@ def test_combine_grid_stride_iterations():
         check_combine(bf16_host_bits(got), exact, S, K + 2, max_rel_1e2=False)
 
 
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8_e4m3", "mxfp8_e5m2", "group_e4m3", "group_e5m2",
+                                  "static", "static_channel", "prequantized"])
+def test_dispatch_grid_stride_iterations(mode):
+    """The slice dispatch kernels (unquantised, MX, per group, static,
+    pre-quantised) take (token, slice) items beyond their grid cap in later
+    iterations.  The small-grid test build (cap 64 workgroups of 4 waves)
+    runs those iterations here; whole receive buffers, sentinels included,
+    must equal the oracle's.  The pre-quantised scale rows (200 bytes over 3
+    slices of 64 lanes) also take a second pass."""
+    import ctypes
+    from combine_moe_get_dispatch_amd import build_lib
+    if not os.path.exists(build_lib.SMALL_GRID_LIB_PATH):
+        pytest.skip("small-grid test build not present (built by __graft_entry__.build())")
+    small = moe.declare_signatures(ctypes.CDLL(build_lib.SMALL_GRID_LIB_PATH))
+    rng = np.random.default_rng(79)
+    T, H, K, E, R, a = 300, 1056, 5, 24, 4, 3         # 132 vectors: 3 slices, 900 items
+    idx, wts = _routing(rng, T, K, E, dup=True, drop=0.1)
+    ol = oracle.layout(idx, E, R, a)
+    lay = gpu_layout(idx, E, R, a)
+    cap = ol.recv_capacity
+    used = ol.recv_src >= 0
+    st = ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream)
+    w_dev = torch.from_numpy(wts).to(DEV)
+    x_bits = W.random_bf16_rows(T, H, 81)
+    x_dev = bf16_dev(x_bits)
+
+    if mode == "prequantized":
+        row_bytes, scale_bytes = 2 * H, 200
+        data = rng.integers(0, 256, size=(T, row_bytes), dtype=np.uint8)
+        sc = rng.integers(0, 256, size=(T, scale_bytes), dtype=np.uint8)
+        ord_, ors, orw = oracle.dispatch_prequantized(
+            data, sc, ol.token_row, cap, wts, np.full((cap, row_bytes), 0xA5, np.uint8),
+            np.full((cap, scale_bytes), 0x5A, np.uint8), with_weights=True)
+        rd = torch.full((cap, row_bytes), 0xA5, dtype=torch.uint8, device=DEV)
+        rs = torch.full((cap, scale_bytes), 0x5A, dtype=torch.uint8, device=DEV)
+        rw = torch.full((cap,), -3.0, device=DEV)
+        d_dev, s_dev = torch.from_numpy(data).to(DEV), torch.from_numpy(sc).to(DEV)
+        assert small.moe_dispatch_prequantized(d_dev.data_ptr(), T, row_bytes, s_dev.data_ptr(), scale_bytes,
+                                               K, lay.token_row.data_ptr(), w_dev.data_ptr(), cap,
+                                               rd.data_ptr(), rs.data_ptr(), rw.data_ptr(), st) == 0
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rd.cpu().numpy(), ord_)
+        np.testing.assert_array_equal(rs.cpu().numpy(), ors)
+    elif mode.startswith("static"):
+        n = H if mode == "static_channel" else 1
+        scales = (rng.random(n, dtype=np.float32) * 40 + 1).astype(np.float32)
+        orx = np.full((cap, H), 0x7B, np.int8)
+        orx, orw = oracle.dispatch_static(x_bits, ol.token_row, cap, scales, wts, recv_x=orx,
+                                          with_weights=True)
+        rx = torch.full((cap, H), 0x7B, dtype=torch.int8, device=DEV)
+        rw = torch.full((cap,), -3.0, device=DEV)
+        sc_dev = torch.from_numpy(scales).to(DEV)
+        assert small.moe_dispatch_static(x_dev.data_ptr(), T, H, K, lay.token_row.data_ptr(), w_dev.data_ptr(),
+                                         cap, sc_dev.data_ptr(), n, rx.data_ptr(), rw.data_ptr(), st) == 0
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+    else:
+        quant = {"bf16": 0, "mxfp8_e4m3": 4, "mxfp8_e5m2": 0x24, "group_e4m3": 0x13, "group_e5m2": 0x23}[mode]
+        orx, ors = oracle_poisoned(cap, H, quant)
+        orx, ors, orw = oracle.dispatch(x_bits, ol.token_row, cap, wts, quant, recv_x=orx, recv_scales=ors,
+                                        with_weights=True)
+        rx, rs, rw = poisoned_recv(lay, H, quant)
+        assert small.moe_dispatch(x_dev.data_ptr(), T, H, K, lay.token_row.data_ptr(), w_dev.data_ptr(), cap,
+                                  quant, rx.data_ptr(), None if rs is None else rs.data_ptr(), rw.data_ptr(),
+                                  st) == 0
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(recv_to_host(rx, quant), orx)
+        if rs is not None and rs.dtype == torch.float32:
+            np.testing.assert_array_equal(rs.cpu().numpy().view(np.uint32), ors.view(np.uint32))
+        elif rs is not None:
+            np.testing.assert_array_equal(rs.cpu().numpy(), ors)
+    np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
+    assert (rw.cpu().numpy()[~used] == -3.0).all()
+
+
 ALL_MODES = [0, 2, 4, 0x12, 0x22, 0x24, 0x13, 0x23]
 
 
