@@ -128,23 +128,47 @@ def _check(t: torch.Tensor, name: str, dtype, shape=None, device=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def _check_layout(layout, device=None, full: bool = False):
-    """The layout's tensors must match its sizes before any pointer of it goes
-    to a kernel (token_row always; every output with full=True)."""
+def _check_fields(t: torch.Tensor, name: str, dtype, shape, device):
+    """Shape, dtype, contiguity and device of one layout tensor (any device
+    type: a layout may be allocated on the host, calls refuse it)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _validate_layout(layout):
+    """Every tensor of a layout matches its sizes and sits on one device."""
     T, K, E, R, cap = (layout.num_tokens, layout.num_topk, layout.num_experts, layout.num_ranks,
                        layout.recv_capacity)
-    dev = layout.token_row.device if device is None else device
-    _check(layout.token_row, "layout.token_row", torch.int32, (T, K), dev)
-    if not full:
-        return
-    _check(layout.num_tokens_per_rank, "layout.num_tokens_per_rank", torch.int32, (R,), dev)
-    _check(layout.num_tokens_per_expert, "layout.num_tokens_per_expert", torch.int32, (E,), dev)
-    _check(layout.is_token_in_rank, "layout.is_token_in_rank", torch.int32, (T, R), dev)
-    _check(layout.num_recv_tokens_per_expert, "layout.num_recv_tokens_per_expert", torch.int32, (E,), dev)
-    _check(layout.expert_offsets, "layout.expert_offsets", torch.int32, (E + 1,), dev)
-    _check(layout.recv_src, "layout.recv_src", torch.int32, (max(cap, 0),), dev)
-    _check(layout.error_flag, "layout.error_flag", torch.int32, (1,), dev)
-    _check(layout.workspace, "layout.workspace", torch.uint8, device=dev)
+    if min(T, K, E, R, layout.expert_alignment) < 0 or cap < 0:
+        raise ValueError("layout sizes must be non-negative")
+    dev = layout.token_row.device
+    _check_fields(layout.token_row, "layout.token_row", torch.int32, (T, K), dev)
+    _check_fields(layout.num_tokens_per_rank, "layout.num_tokens_per_rank", torch.int32, (R,), dev)
+    _check_fields(layout.num_tokens_per_expert, "layout.num_tokens_per_expert", torch.int32, (E,), dev)
+    _check_fields(layout.is_token_in_rank, "layout.is_token_in_rank", torch.int32, (T, R), dev)
+    _check_fields(layout.num_recv_tokens_per_expert, "layout.num_recv_tokens_per_expert", torch.int32,
+                  (E,), dev)
+    _check_fields(layout.expert_offsets, "layout.expert_offsets", torch.int32, (E + 1,), dev)
+    _check_fields(layout.recv_src, "layout.recv_src", torch.int32, (cap,), dev)
+    _check_fields(layout.error_flag, "layout.error_flag", torch.int32, (1,), dev)
+    _check_fields(layout.workspace, "layout.workspace", torch.uint8, None, dev)
+
+
+def _check_layout(layout, device):
+    """A call's layout: a DispatchLayout (validated when it was made) on the
+    call's device."""
+    if not isinstance(layout, DispatchLayout):
+        raise TypeError("layout must be a DispatchLayout")
+    if layout.token_row.device != device:
+        raise ValueError(f"layout is on {layout.token_row.device}, expected {device}")
 
 
 def moe_recv_capacity_bound(num_tokens: int, num_topk: int, num_experts: int,
@@ -156,10 +180,15 @@ def moe_layout_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int,
     return int(lib().moe_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks))
 
 
-@dataclasses.dataclass
+@dataclasses.dataclass(frozen=True)
 class DispatchLayout:
     """Outputs of moe_get_dispatch_layout; (expert_offsets, token_row,
-    recv_src) plus the sizes form the handle combine needs."""
+    recv_src) plus the sizes form the handle combine needs.
+
+    Every tensor is checked against the sizes when the layout is made (here
+    or through dataclasses.replace), and the fields cannot be reassigned, so
+    calls only check the layout's device.  Its tensors must not be resized
+    or re-pointed in place afterwards."""
     num_tokens_per_rank: torch.Tensor          # int32 [R]
     num_tokens_per_expert: torch.Tensor        # int32 [E]
     is_token_in_rank: torch.Tensor             # int32 [T, R]
@@ -175,6 +204,9 @@ class DispatchLayout:
     num_ranks: int
     expert_alignment: int
     recv_capacity: int
+
+    def __post_init__(self):
+        _validate_layout(self)
 
 
 def allocate_layout(num_tokens: int, num_topk: int, num_experts: int, num_ranks: int,
@@ -211,7 +243,7 @@ def moe_get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks:
     elif (out.num_tokens, out.num_topk, out.num_experts, out.num_ranks, out.expert_alignment) != (
             T, K, num_experts, num_ranks, expert_alignment):
         raise ValueError("preallocated layout was made for other sizes")
-    _check_layout(out, topk_idx.device, full=True)
+    _check_layout(out, topk_idx.device)
     rc = lib().moe_get_dispatch_layout(
         _ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, out.recv_capacity,
         _ptr(out.num_tokens_per_rank), _ptr(out.num_tokens_per_expert), _ptr(out.is_token_in_rank),

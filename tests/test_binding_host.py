@@ -1,5 +1,7 @@
 """The Python binding on the CPU: every call refuses host tensors before any
 pointer reaches the library (there is no CPU path)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -35,3 +37,31 @@ def test_layout_sizes_follow_the_capacity_bound():
     assert tuple(lay.is_token_in_rank.shape) == (100, 4) and tuple(lay.expert_offsets.shape) == (17,)
     with pytest.raises(ValueError):
         moe.allocate_layout(-1, 4, 16, 4, 8, device="cpu")
+
+
+def test_layouts_are_checked_when_made():
+    """Every tensor of a layout is checked against its sizes when the layout
+    is made, and the fields cannot be reassigned afterwards."""
+    lay = moe.allocate_layout(64, 4, 16, 4, 2, device="cpu")
+    bad_fields = [
+        ("token_row", lay.token_row[:-1]),
+        ("token_row", lay.token_row.to(torch.int64)),
+        ("recv_src", lay.recv_src[:-1]),
+        ("is_token_in_rank", torch.empty((4, 64), dtype=torch.int32).t()),   # right shape, not contiguous
+        ("expert_offsets", lay.expert_offsets[:-1]),
+        ("num_tokens_per_rank", torch.empty(5, dtype=torch.int32)),
+        ("num_tokens_per_expert", torch.empty(16, dtype=torch.int64)),
+        ("num_recv_tokens_per_expert", torch.empty(15, dtype=torch.int32)),
+        ("error_flag", torch.empty(2, dtype=torch.int32)),
+        ("workspace", torch.empty(8, dtype=torch.int32)),
+        ("recv_src", torch.empty(lay.recv_capacity, dtype=torch.int32, device="meta")),  # another device
+    ]
+    for field, bad in bad_fields:
+        with pytest.raises((ValueError, TypeError)):
+            dataclasses.replace(lay, **{field: bad})
+    with pytest.raises((ValueError, TypeError)):
+        dataclasses.replace(lay, num_tokens=63)
+    with pytest.raises(dataclasses.FrozenInstanceError):
+        lay.token_row = lay.token_row.clone()
+    ok = dataclasses.replace(lay, token_row=lay.token_row.clone())
+    assert ok.token_row.shape == (64, 4)

@@ -712,7 +712,9 @@ def test_bench_workload_full_size_sampled(w):
 
 def test_binding_rejects_mismatched_layouts():
     """A layout whose tensors do not match its sizes (truncated, wrong dtype)
-    is refused by the binding before any pointer reaches a kernel."""
+    cannot be made, and calls take only layouts, so no such pointer reaches a
+    kernel; the genuine layout still works."""
+    import collections
     import dataclasses
     rng = np.random.default_rng(91)
     T, H, K, E, R, a = 64, 256, 4, 16, 4, 2
@@ -720,18 +722,20 @@ def test_binding_rejects_mismatched_layouts():
     lay = gpu_layout(idx, E, R, a)
     x = bf16_dev(W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
     y = torch.zeros((lay.recv_capacity, H), dtype=torch.bfloat16, device=DEV)
-    short = dataclasses.replace(lay, token_row=lay.token_row[:-1])
-    wide = dataclasses.replace(lay, token_row=lay.token_row.to(torch.int64))
-    for bad in (short, wide):
+    for field, bad in (("token_row", lay.token_row[:-1]), ("token_row", lay.token_row.to(torch.int64)),
+                       ("recv_src", lay.recv_src[:-1]), ("token_row", lay.token_row.cpu())):
         with pytest.raises((ValueError, TypeError)):
-            moe.moe_dispatch(x, bad)
-        with pytest.raises((ValueError, TypeError)):
-            moe.moe_combine(y, bad)
-        with pytest.raises((ValueError, TypeError)):
-            moe.moe_combine_fused(y, bad)
-    with pytest.raises(ValueError):
-        moe.moe_get_dispatch_layout(torch.from_numpy(idx).to(DEV), E, R, a,
-                                    out=dataclasses.replace(lay, recv_src=lay.recv_src[:-1]))
-    # the genuine layout still works
+            dataclasses.replace(lay, **{field: bad})
+    fake = collections.namedtuple("Fake", [f.name for f in dataclasses.fields(lay)])(
+        *[getattr(lay, f.name) for f in dataclasses.fields(lay)])
+    with pytest.raises(TypeError):
+        moe.moe_dispatch(x, fake)
+    with pytest.raises(TypeError):
+        moe.moe_combine(y, fake)
+    with pytest.raises(TypeError):
+        moe.moe_combine_fused(y, fake)
+    with pytest.raises(TypeError):
+        moe.moe_get_dispatch_layout(torch.from_numpy(idx).to(DEV), E, R, a, out=fake)
     moe.moe_combine(y, lay)
+    moe.moe_dispatch(x, lay)
     torch.cuda.synchronize()
