@@ -25,12 +25,13 @@
 // HBM exactly once, held in a VGPR, quantised there once, and then written
 // to each of the token's K rows with 16-byte (bf16) or 8-byte (1-byte codes)
 // stores.  Two launch shapes:
-//   - slices (bf16, MX, per group, static, pre-quantised rows): one wave per
-//     (token, 64-vector slice of its row), four waves per workgroup, so each
-//     wave reads 1 KiB of x and writes 1 KiB (or 512 bytes) to each row;
+//   - slices (bf16, static int8, pre-quantised rows): one wave per (token,
+//     64-vector slice of its row), four waves per workgroup, so each wave
+//     reads 1 KiB of x and writes 1 KiB (or 512 bytes) to each row;
 //   - one workgroup per token (per-token scales, which need the maximum over
-//     the whole row): one vector per lane, 896 lanes at H = 7168, two vectors
-//     per lane above H = 8192, the row maximum through LDS.
+//     the whole row, and MX and per-group scales, measured faster so): one
+//     vector per lane, 896 lanes at H = 7168, two vectors per lane above
+//     H = 8192.
 // The stores are nontemporal: every expanded row is written once and read
 // only by a later stage.  Ordinary stores finish this kernel sooner but
 // leave up to a few hundred MB dirty in the L2s and the memory-side cache,
@@ -235,16 +236,20 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_pertoken_kernel(
 // --------------------------------------------------------------------------- element-wise codecs (slices)
 
 // MX, per-group and static quantisation need no value wider than 128
-// elements, so they run in the slice form of the bf16 copy: one wave per
-// (token, 64-vector slice).  Each lane encodes its 8 elements once into 8
-// code bytes plus, where the format has one, its share of the scale row;
-// the codes are then stored to each of the K rows.  A codec provides
+// elements.  Each lane encodes its 8 elements once into 8 code bytes plus,
+// where the format has one, its share of the scale row; the codes are then
+// stored to each of the K rows.  A codec provides
 //   encode(xv, i, aux) -> the lane's 8 codes (i = clamped vector index,
 //                         aux = the lane's scale payload)
-//   store_scale(row, i, aux)  -> its scale bytes for one destination row.
-// Measured against one workgroup per token: equal with x in the
-// memory-side cache; per group 10 % faster after a cache flush and 8 %
-// faster at 32768 tokens, MX 2.5 % faster at 32768 tokens.
+//   store_scale(row, i, aux)  -> its scale bytes for one destination row
+// and runs in one of two launch forms, chosen by measurement inside whole
+// steps, with x in the memory-side cache and after flushing it by a 1 GiB
+// fill and by a 1 GiB read:
+//   - static int8 in the slice form of the bf16 copy (one wave per token and
+//     64-vector slice): equal warm, 7-14 % faster cold;
+//   - MX and per group in the one-workgroup-per-token form: the slice form
+//     was equal warm but 8-20 % slower after the read flush (per group 10 %
+//     faster after the fill flush).
 
 // MX (32-element blocks, one e8m0 byte each): a block is 4 lanes of 8
 // elements.  Lanes past the row end hold a copy of the row's last vector;
@@ -360,6 +365,42 @@ struct StaticCodec {
     __device__ void store_scale(int64_t, int, uint32_t) const {}
 };
 
+// The same codecs in the one-workgroup-per-token form (VPT vectors per lane).
+template <int VPT, class Codec>
+__global__ __launch_bounds__(kRowMaxThreads) void dispatch_codec_row_kernel(
+    const u32x4 *__restrict__ x, int nvec, int K, const int32_t *__restrict__ token_row,
+    const float *__restrict__ topk_weights, int64_t cap, u32x2 *__restrict__ recv,
+    float *__restrict__ recv_weights, const Codec codec)
+{
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const u32x4 *xt = x + (int64_t)t * nvec;
+    u32x4 xin[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+        xin[j] = xt[min(tid + j * nthr, nvec - 1)]; // clamped: always in bounds
+    u32x2 q[VPT];
+    uint32_t aux[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+        q[j] = codec.encode(xin[j], min(tid + j * nthr, nvec - 1), aux[j]);
+    for (int k = 0; k < K; ++k) {
+        const int row = token_row[(int64_t)t * K + k];
+        if (row < 0 || row >= cap)
+            continue;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int i = tid + j * nthr;
+            if (i < nvec) {
+                __builtin_nontemporal_store(q[j], recv + (int64_t)row * nvec + i);
+                codec.store_scale(row, i, aux[j]);
+            }
+        }
+    }
+    write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
+}
+
 template <class Codec>
 __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_codec_slice_kernel(
     const u32x4 *__restrict__ x, int nvec, int nslices, int64_t nitems, int K,
@@ -438,6 +479,21 @@ static hipError_t launch_codec(const Codec &codec, const SliceGrid &g, hipStream
                          token_row, topk_weights, cap, recv, recv_weights, codec);
 }
 
+template <class Codec>
+static hipError_t launch_codec_rows(const Codec &codec, int T, int nvec, hipStream_t stream,
+                                    const u32x4 *x, int K, const int32_t *token_row,
+                                    const float *topk_weights, int64_t cap, u32x2 *recv,
+                                    float *recv_weights)
+{
+    const int threads = row_block_threads(nvec);
+    const dim3 grid(T), block(threads);
+    if (nvec <= threads)
+        return launch_kernel(dispatch_codec_row_kernel<1, Codec>, grid, block, 0, stream, x, nvec,
+                             K, token_row, topk_weights, cap, recv, recv_weights, codec);
+    return launch_kernel(dispatch_codec_row_kernel<2, Codec>, grid, block, 0, stream, x, nvec, K,
+                         token_row, topk_weights, cap, recv, recv_weights, codec);
+}
+
 template <int V>
 static hipError_t launch_dispatch_v(dim3 grid, dim3 block, hipStream_t stream, const u32x4 *xv,
                                     int nvec, int K, const int32_t *token_row,
@@ -479,17 +535,19 @@ hipError_t launch_dispatch(const void *x, int T, int H, int K, const int32_t *to
                              g.nslices, g.nitems, K, token_row, topk_weights, cap,
                              (u32x4 *)recv_x, recv_weights);
     case MOE_QUANT_MXFP8_E4M3:
-        return launch_codec(MxCodec<Dst::E4M3>{(uint8_t *)recv_scales, nvec / 4}, g, stream, xs,
-                            nvec, K, token_row, topk_weights, cap, rq, recv_weights);
+        return launch_codec_rows(MxCodec<Dst::E4M3>{(uint8_t *)recv_scales, nvec / 4}, T, nvec,
+                                 stream, xs, K, token_row, topk_weights, cap, rq, recv_weights);
     case MOE_QUANT_MXFP8_E5M2:
-        return launch_codec(MxCodec<Dst::E5M2>{(uint8_t *)recv_scales, nvec / 4}, g, stream, xs,
-                            nvec, K, token_row, topk_weights, cap, rq, recv_weights);
+        return launch_codec_rows(MxCodec<Dst::E5M2>{(uint8_t *)recv_scales, nvec / 4}, T, nvec,
+                                 stream, xs, K, token_row, topk_weights, cap, rq, recv_weights);
     case MOE_QUANT_FP8_E4M3_PER_GROUP:
-        return launch_codec(GroupCodec<Dst::E4M3>{(float *)recv_scales, (nvec + 15) / 16}, g,
-                            stream, xs, nvec, K, token_row, topk_weights, cap, rq, recv_weights);
+        return launch_codec_rows(GroupCodec<Dst::E4M3>{(float *)recv_scales, (nvec + 15) / 16}, T,
+                                 nvec, stream, xs, K, token_row, topk_weights, cap, rq,
+                                 recv_weights);
     case MOE_QUANT_FP8_E5M2_PER_GROUP:
-        return launch_codec(GroupCodec<Dst::E5M2>{(float *)recv_scales, (nvec + 15) / 16}, g,
-                            stream, xs, nvec, K, token_row, topk_weights, cap, rq, recv_weights);
+        return launch_codec_rows(GroupCodec<Dst::E5M2>{(float *)recv_scales, (nvec + 15) / 16}, T,
+                                 nvec, stream, xs, K, token_row, topk_weights, cap, rq,
+                                 recv_weights);
     default: // per token: one workgroup per token (below)
         break;
     }

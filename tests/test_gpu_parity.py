@@ -508,12 +508,14 @@ def test_combine_grid_stride_iterations():
 @pytest.mark.parametrize("mode", ["bf16", "mxfp8_e4m3", "mxfp8_e5m2", "group_e4m3", "group_e5m2",
                                   "static", "static_channel", "prequantized"])
 def test_dispatch_grid_stride_iterations(mode):
-    """The slice dispatch kernels (unquantised, MX, per group, static,
-    pre-quantised) take (token, slice) items beyond their grid cap in later
-    iterations.  The small-grid test build (cap 64 workgroups of 4 waves)
-    runs those iterations here; whole receive buffers, sentinels included,
-    must equal the oracle's.  The pre-quantised scale rows (200 bytes over 3
-    slices of 64 lanes) also take a second pass."""
+    """The slice dispatch kernels (unquantised, static, pre-quantised) take
+    (token, slice) items beyond their grid cap in later iterations.  The
+    small-grid test build (cap 64 workgroups of 4 waves) runs those
+    iterations here; whole receive buffers, sentinels included, must equal
+    the oracle's (the MX and per-group modes, one workgroup per token, run
+    through the same build as a check of that build).  The pre-quantised
+    scale rows (200 bytes over 3 slices of 64 lanes) also take a second
+    pass."""
     import ctypes
     from combine_moe_get_dispatch_amd import build_lib
     if not os.path.exists(build_lib.SMALL_GRID_LIB_PATH):
