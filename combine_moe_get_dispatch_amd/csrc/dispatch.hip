@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kRowMaxThreads) void dispatch_pertoken_kernel(
     write_row_weight(token_row, topk_weights, recv_weights, t, K, cap);
 }
 
-// --------------------------------------------------------------------------- element-wise codecs (slices)
+// --------------------------------------------------------------------------- element-wise codecs
 
 // MX, per-group and static quantisation need no value wider than 128
 // elements.  Each lane encodes its 8 elements once into 8 code bytes plus,
@@ -293,7 +293,8 @@ template <Dst D> struct MxCodec {
 };
 
 // Per group of 128 elements (16 lanes x 8 elements; 16-lane groups are
-// aligned inside the wave, and slices start at multiples of 64 vectors):
+// aligned inside the wave, and every wave starts at a multiple of 64
+// vectors of the row):
 // the per-token formula on each group, one fp32 scale per group.  Lanes
 // past the row end hold copies of the row's last vector, which belongs to
 // the row's last (possibly partial) group, so they cannot change any
