@@ -599,7 +599,7 @@ def _random_config(i):
     return rng, T, H, E, R, K, a, quant, dup, drop
 
 
-@pytest.mark.parametrize("i", range(48), ids=[f"cfg{i}" for i in range(48)])
+@pytest.mark.parametrize("i", range(200), ids=[f"cfg{i}" for i in range(200)])
 def test_random_configurations(i):
     """Seeded random shapes over the whole valid range (including T = 0, one
     expert, all entries dropped, ragged hidden sizes, every quant mode): the
