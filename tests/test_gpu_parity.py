@@ -505,17 +505,17 @@ def test_combine_grid_stride_iterations():
         check_combine(bf16_host_bits(got), exact, S, K + 2, max_rel_1e2=False)
 
 
-@pytest.mark.parametrize("mode", ["bf16", "mxfp8_e4m3", "mxfp8_e5m2", "group_e4m3", "group_e5m2",
-                                  "static", "static_channel", "prequantized"])
+@pytest.mark.parametrize("mode", ["bf16", "int8_token", "e4m3_token", "e5m2_token", "mxfp8_e4m3",
+                                  "mxfp8_e5m2", "group_e4m3", "group_e5m2", "static", "static_channel",
+                                  "prequantized"])
 def test_dispatch_grid_stride_iterations(mode):
     """The slice dispatch kernels (unquantised, static, pre-quantised) take
     (token, slice) items beyond their grid cap in later iterations.  The
     small-grid test build (cap 64 workgroups of 4 waves) runs those
     iterations here; whole receive buffers, sentinels included, must equal
-    the oracle's (the MX and per-group modes, one workgroup per token, run
-    through the same build as a check of that build).  The pre-quantised
-    scale rows (200 bytes over 3 slices of 64 lanes) also take a second
-    pass."""
+    the oracle's (the modes with one workgroup per token run through the
+    same build as a check of that build).  The pre-quantised scale rows (200
+    bytes over 3 slices of 64 lanes) also take a second pass."""
     import ctypes
     from combine_moe_get_dispatch_amd import build_lib
     if not os.path.exists(build_lib.SMALL_GRID_LIB_PATH):
@@ -564,7 +564,8 @@ def test_dispatch_grid_stride_iterations(mode):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(rx.cpu().numpy(), orx)
     else:
-        quant = {"bf16": 0, "mxfp8_e4m3": 4, "mxfp8_e5m2": 0x24, "group_e4m3": 0x13, "group_e5m2": 0x23}[mode]
+        quant = {"bf16": 0, "int8_token": 2, "e4m3_token": 0x12, "e5m2_token": 0x22, "mxfp8_e4m3": 4,
+                 "mxfp8_e5m2": 0x24, "group_e4m3": 0x13, "group_e5m2": 0x23}[mode]
         orx, ors = oracle_poisoned(cap, H, quant)
         orx, ors, orw = oracle.dispatch(x_bits, ol.token_row, cap, wts, quant, recv_x=orx, recv_scales=ors,
                                         with_weights=True)
