@@ -85,8 +85,10 @@ extern "C" {
 /* Limits.  Top-k and expert counts are the ranges of the Normal Mode API page
  * (Constraints: num_topk in (0, 16], num_experts in (0, 512]); hidden must be
  * a multiple of 32 (CANN page, Constraint 7 "H"; also the MX block).  The
- * hidden size is at most 16384, a limit of this library: a token row is held
- * in one 1024-lane workgroup, at most two 16-byte vectors per lane. */
+ * hidden size is at most 16384, a limit of this library: the kernels that
+ * keep one workgroup per token (per-token, MX and per-group scales, the RMS
+ * normalisation) hold the row in one 1024-lane workgroup, at most two
+ * 16-byte vectors per lane. */
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_HIDDEN 16384
