@@ -493,6 +493,7 @@ def main():
         "stage_bytes": sb,
         "stage_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
         "stage_median_us": {k: round(v, 2) for k, v in med_us.items()},
+        "stage_achieved_gbs": {k: round(sb[k] / (v * 1e-6) / 1e9, 1) for k, v in avg_us.items() if v > 0},
         "stage_events": {"kind": timer.kind, "every_nth_step": every, "samples": len(events),
                          "timed_region": "eager pass before the graph replays" if graph is not None
                          else "the timed steps"},
