@@ -189,6 +189,34 @@ def test_out_of_range_ids_flagged():
     assert_layout_equal(gl, ol)
 
 
+@pytest.mark.parametrize("T", [100, 3000], ids=["one_workgroup", "chunked"])
+def test_capacity_above_the_bound(T):
+    """A caller may size the receive buffer above T*K + E*(a-1): the whole
+    layout, rows past the last expert included (recv_src -1), equals the
+    oracle's at that capacity, and dispatch and combine run unchanged on it."""
+    rng = np.random.default_rng(4242 + T)
+    H, K, E, R, a = 256, 4, 16, 4, 8
+    idx, wts = _routing(rng, T, K, E, drop=0.1)
+    cap = oracle.recv_capacity_bound(T, K, E, a) + 777
+    ol = oracle.layout(idx, E, R, a, recv_capacity=cap)
+    lay = gpu_layout(idx, E, R, a, cap=cap)
+    assert lay.recv_capacity == cap
+    gl = layout_to_host(lay)
+    assert_layout_equal(gl, ol)
+    assert (gl["recv_src"][ol.expert_offsets[-1]:] == -1).all()
+    x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    orx, _ = oracle_poisoned(cap, H, 0)
+    orx, _, _ = oracle.dispatch(x_bits, ol.token_row, cap, wts, 0, recv_x=orx, with_weights=True)
+    rx, _, rw = poisoned_recv(lay, H, 0)
+    w_dev = torch.from_numpy(wts).to(DEV)
+    moe.moe_dispatch(bf16_dev(x_bits), lay, w_dev, 0, recv_x=rx, recv_weights=rw)
+    np.testing.assert_array_equal(recv_to_host(rx, 0), orx)
+    out = moe.moe_combine(rx, lay, w_dev)
+    exact = oracle.combine(orx, ol.token_row, wts)
+    S = combine_bound(orx, ol.token_row, wts, K)
+    check_combine(bf16_host_bits(out), exact, S, K)
+
+
 def test_zero_tokens():
     idx = np.zeros((0, 4), np.int64)
     ol = oracle.layout(idx, 16, 4, 8)
