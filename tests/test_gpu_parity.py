@@ -154,6 +154,11 @@ EDGE = [
     ("fp8_e5m2_per_group", 700, 4096, 64, 8, 8, 16, 0x23, True, 0.05),
     ("fp8_e4m3_per_group_partial", 300, 160, 16, 4, 4, 8, 0x13, False, 0.1),
     ("fp8_e5m2_per_group_max_hidden", 40, 16384, 128, 8, 8, 32, 0x23, False, 0.0),
+    # the limits of the one-workgroup layout: T*K <= 4096 and T*R <= 16384
+    ("single_layout_max_entries", 512, 64, 256, 8, 8, 1, 0, False, 0.0),
+    ("chunked_layout_min_entries", 513, 64, 256, 8, 8, 1, 0, False, 0.0),
+    ("single_layout_max_flags", 2048, 32, 64, 8, 2, 2, 0, False, 0.05),
+    ("chunked_layout_flags_over", 1024, 32, 512, 32, 4, 1, 0, False, 0.0),
 ]
 
 
