@@ -82,16 +82,25 @@ constexpr int kMaxChunkFlags = 16384;
 // are laid out by one workgroup in one launch.
 constexpr int kSingleLayoutMaxEntries = 4096;
 
+// From this many count-table cells (chunks x E rounded up to 4) on, a
+// column-scan launch between the two kernels forms each chunk's prefix row
+// and the expert totals once, so that a rank workgroup reads two rows
+// instead of reducing the whole table itself (whose size grows as chunks x E
+// when many ranks force small chunks).
+constexpr int64_t kLayoutScanMinCells = 131072;
+
 struct LayoutPlan {
     int tokens_per_chunk;
     int num_chunks;
-    size_t workspace_bytes; // count table [chunks][E rounded up to 4] + rank table [chunks][R] + flags [chunks]
+    size_t workspace_bytes; // count table [chunks][Ep] + rank table [chunks][R] + flags [chunks]
+                            // (+ prefix table [chunks][Ep] + totals [Ep] with scan), Ep = E rounded up to 4
     bool single;            // the whole batch in one workgroup (no workspace, one launch)
+    bool scan;              // three launches: count, column scan, rank
 };
 
 inline LayoutPlan plan_layout(int T, int K, int E, int R)
 {
-    LayoutPlan p{0, 0, 0, false};
+    LayoutPlan p{0, 0, 0, false, false};
     if ((int64_t)T * K <= kSingleLayoutMaxEntries && (int64_t)T * R <= kMaxChunkFlags) {
         p.single = true; // includes T == 0
         p.tokens_per_chunk = T;
@@ -107,7 +116,12 @@ inline LayoutPlan plan_layout(int T, int K, int E, int R)
         tpc = 1;
     p.tokens_per_chunk = tpc;
     p.num_chunks = (T + tpc - 1) / tpc;
-    p.workspace_bytes = (size_t)p.num_chunks * (size_t)(((E + 3) & ~3) + R + 1) * sizeof(int32_t);
+    const size_t Ep = (size_t)((E + 3) & ~3);
+    p.scan = (int64_t)p.num_chunks * (int64_t)Ep >= kLayoutScanMinCells;
+    size_t cells = (size_t)p.num_chunks * (Ep + (size_t)R + 1);
+    if (p.scan)
+        cells += (size_t)p.num_chunks * Ep + Ep;
+    p.workspace_bytes = cells * sizeof(int32_t);
     return p;
 }
 

@@ -25,6 +25,10 @@
 //     exclusive scan over waves, and within a wave the position among equal
 //     keys by masked popcount.  Ranks therefore come from prefix sums only
 //     (never from atomic return order), which makes the result deterministic.
+// When many ranks force many small chunks, the table is large (from
+// kLayoutScanMinCells cells on) and layout_scan_kernel runs between the two:
+// it forms the column prefix sums and the totals once, and each rank
+// workgroup reads its own prefix row and the totals instead.
 #include "device_common.h"
 #include "launch.h"
 
@@ -153,10 +157,52 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
         flag_tab[chunk] = s_bad;
 }
 
+// Column scan of the count table, for large tables only: cb_tab[c][e] =
+// sum over chunks c' < c of cnt_tab[c'][e], and tot_tab[e] = the sum over all
+// chunks.  One workgroup per 16 columns; its 64 groups of 16 lanes each own a
+// contiguous run of chunks: they sum their run, take the exclusive prefix of
+// the group sums from LDS, then walk the run again writing running prefixes.
+constexpr int kScanCols = 16;
+constexpr int kScanGroups = 1024 / kScanCols;
+
+__global__ __launch_bounds__(1024) void layout_scan_kernel(const int32_t *__restrict__ cnt_tab,
+                                                           int nchunks, int Ep,
+                                                           int32_t *__restrict__ cb_tab,
+                                                           int32_t *__restrict__ tot_tab)
+{
+    __shared__ int s_part[kScanGroups][kScanCols];
+    const int c = threadIdx.x % kScanCols;
+    const int g = threadIdx.x / kScanCols;
+    const int col = blockIdx.x * kScanCols + c;
+    const int per = (nchunks + kScanGroups - 1) / kScanGroups;
+    const int r0 = min(nchunks, g * per);
+    const int r1 = min(nchunks, r0 + per);
+    int sum = 0;
+    if (col < Ep)
+        for (int r = r0; r < r1; ++r)
+            sum += cnt_tab[(int64_t)r * Ep + col];
+    s_part[g][c] = sum;
+    __syncthreads();
+    int base = 0;
+    for (int h = 0; h < g; ++h)
+        base += s_part[h][c];
+    if (col < Ep) {
+        if (g == kScanGroups - 1)
+            tot_tab[col] = base + sum;
+        int run = base;
+        for (int r = r0; r < r1; ++r) {
+            const int v = cnt_tab[(int64_t)r * Ep + col];
+            cb_tab[(int64_t)r * Ep + col] = run;
+            run += v;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int a, int tpc, int nchunks,
     int nbits, int64_t cap, const int32_t *__restrict__ cnt_tab, const int32_t *__restrict__ rank_tab,
-    const int32_t *__restrict__ flag_tab, int32_t *__restrict__ ntpr, int32_t *__restrict__ ntpe,
+    const int32_t *__restrict__ flag_tab, const int32_t *__restrict__ cb_tab,
+    const int32_t *__restrict__ tot_tab, int32_t *__restrict__ ntpr, int32_t *__restrict__ ntpe,
     int32_t *__restrict__ nrtpe, int32_t *__restrict__ off, int32_t *__restrict__ token_row,
     int32_t *__restrict__ recv_src, int32_t *__restrict__ error_flag)
 {
@@ -199,8 +245,9 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     const int parts = kRankThreads / groups; // >= 8
     const int g = tid % groups;
     const int part = tid / groups;
-    const bool tab_thread = tid < parts * groups;
-    const int rb = min(kTabRows, (nchunks + parts - 1) / parts); // rows per thread and pass (uniform)
+    const bool scanned = tot_tab != nullptr; // the scan launch left totals and this chunk's prefix row
+    const bool tab_thread = tid < parts * groups && !scanned;
+    const int rb = scanned ? 0 : min(kTabRows, (nchunks + parts - 1) / parts); // rows per thread and pass (uniform)
     const int4 *tab4 = (const int4 *)cnt_tab;
     int4 tab_reg[kTabRows];
 #pragma unroll
@@ -225,6 +272,11 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     if (chunk == 0)
         for (int c = tid; c < nchunks; c += kRankThreads)
             flag_reg |= flag_tab[c];
+    int tot_reg = 0, cb_reg = 0; // scanned: expert tid's total and prefix (E <= 512 < 1024 threads)
+    if (scanned && tid < E) {
+        tot_reg = tot_tab[tid];
+        cb_reg = has_chunk ? cb_tab[(int64_t)chunk * (4 * groups) + tid] : 0;
+    }
 
     // (1) expert totals over all chunks, and the part of them in chunks
     // before this one; this chunk's ids into LDS; this workgroup's rank sums
@@ -240,6 +292,10 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
         s_flag = 0;
     __syncthreads();
 
+    if (scanned && tid < E) {
+        s_tot[tid] = tot_reg;
+        s_cb[tid] = cb_reg;
+    }
     if (tab_thread && nchunks > 0) {
         int all[4] = {0, 0, 0, 0}, before[4] = {0, 0, 0, 0};
         auto add_row = [&](int r, const int4 v) {
@@ -627,20 +683,31 @@ hipError_t launch_layout(const LayoutArgs &A, const LayoutPlan &P, hipStream_t s
         return launch_kernel(layout_single_kernel, dim3(1), dim3(kRankThreads), 0, stream,
                              A.topk_idx, A.T, A.K, A.E, A.R, L, A.a, nbits, A.cap, A.itr, A.ntpr,
                              A.ntpe, A.nrtpe, A.off, A.token_row, A.recv_src, A.error_flag);
+    const int Ep = (A.E + 3) & ~3;
     int32_t *cnt_tab = A.workspace;
-    int32_t *rank_tab = cnt_tab ? cnt_tab + (size_t)nchunks * ((A.E + 3) & ~3) : nullptr;
+    int32_t *rank_tab = cnt_tab ? cnt_tab + (size_t)nchunks * Ep : nullptr;
     int32_t *flag_tab = rank_tab ? rank_tab + (size_t)nchunks * A.R : nullptr;
+    int32_t *cb_tab = P.scan ? flag_tab + nchunks : nullptr;
+    int32_t *tot_tab = P.scan ? cb_tab + (size_t)nchunks * Ep : nullptr;
     if (nchunks > 0) {
-        const hipError_t err = launch_kernel(
+        hipError_t err = launch_kernel(
             layout_count_kernel, dim3(nchunks), dim3(kCountThreads), 0, stream, A.topk_idx, A.T,
             A.K, A.E, A.R, L, P.tokens_per_chunk, nbits, A.itr, cnt_tab, rank_tab, flag_tab);
         if (err != hipSuccess)
             return err;
+        if (P.scan) {
+            err = launch_kernel(layout_scan_kernel, dim3((Ep + kScanCols - 1) / kScanCols),
+                                dim3(1024), 0, stream, (const int32_t *)cnt_tab, nchunks, Ep,
+                                cb_tab, tot_tab);
+            if (err != hipSuccess)
+                return err;
+        }
     }
     return launch_kernel(layout_rank_kernel, dim3(nchunks > 0 ? nchunks : 1), dim3(kRankThreads), 0,
                          stream, A.topk_idx, A.T, A.K, A.E, A.R, A.a, P.tokens_per_chunk, nchunks,
-                         nbits, A.cap, cnt_tab, rank_tab, flag_tab, A.ntpr, A.ntpe, A.nrtpe, A.off,
-                         A.token_row, A.recv_src, A.error_flag);
+                         nbits, A.cap, cnt_tab, rank_tab, flag_tab, (const int32_t *)cb_tab,
+                         (const int32_t *)tot_tab, A.ntpr, A.ntpe, A.nrtpe, A.off, A.token_row,
+                         A.recv_src, A.error_flag);
 }
 
 } // namespace moe

@@ -108,6 +108,14 @@ def test_layout_rejects_null_outputs_and_small_workspace(L):
     assert _layout_call(L, T, 4, 16, 4, 8, cap, ws=ctypes.c_void_p(0x1008)) == -3   # misaligned
 
 
+def test_scan_layout_workspace(L):
+    # many ranks force small chunks; from 131072 count-table cells on the layout
+    # adds a column scan, whose prefix table and totals live in the workspace
+    K, E, R, Ep = 2, 512, 512, 512
+    assert L.moe_layout_workspace_bytes(8192, K, E, R) == 4 * (256 * (Ep + R + 1) + 256 * Ep + Ep)
+    assert L.moe_layout_workspace_bytes(8160, K, E, R) == 4 * 255 * (Ep + R + 1)
+
+
 def test_small_batches_need_no_workspace(L):
     # one workgroup takes the whole batch when T*K <= 4096 and T*R <= 16384
     assert L.moe_layout_workspace_bytes(512, 8, 256, 8) == 0

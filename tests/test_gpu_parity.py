@@ -159,6 +159,10 @@ EDGE = [
     ("chunked_layout_min_entries", 513, 64, 256, 8, 8, 1, 0, False, 0.0),
     ("single_layout_max_flags", 2048, 32, 64, 8, 2, 2, 0, False, 0.05),
     ("chunked_layout_flags_over", 1024, 32, 512, 32, 4, 1, 0, False, 0.0),
+    # count tables of >= 131072 cells: the column-scan launch between count and rank
+    ("scan_layout_e512_r512", 8192, 32, 512, 512, 2, 1, 0, False, 0.0),
+    ("scan_layout_ragged_a7_drop", 8200, 64, 512, 512, 3, 7, 0, False, 0.2),
+    ("scan_layout_e256_r256_k1", 32768, 32, 256, 256, 1, 1, 0, False, 0.0),
 ]
 
 
