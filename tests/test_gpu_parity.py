@@ -314,15 +314,16 @@ def test_pending_unrelated_hip_error_does_not_fail_calls():
     assert_layout_equal(layout_to_host(lay), oracle.layout(idx, 8, 2, 1))
 
 
-@pytest.mark.parametrize("quant,T", [(0, 300), (2, 300), (4, 300), (0, 2000), (4, 2000)])
+@pytest.mark.parametrize("quant,T", [(0, 300), (2, 300), (4, 300), (0, 2000), (4, 2000), (0, 8192)])
 def test_graph_capture_replays_match_eager(quant, T):
     """The three calls allocate nothing and never synchronise, so a step can be
     captured in a HIP graph.  Replay it several times, with eager work and
     synchronisations in between, and check every replay against the eager
     result (layout, rows, scales, combine output).  T = 300 takes the
-    one-workgroup layout, T = 2000 the two-launch one."""
+    one-workgroup layout, T = 2000 the two-launch one, and T = 8192 with
+    512 experts over 512 ranks the three-launch one (column scan)."""
     rng = np.random.default_rng(40 + quant + T)
-    H, K, E, R, a = 512, 4, 32, 4, 8
+    H, K, E, R, a = (512, 4, 32, 4, 8) if T < 8192 else (64, 2, 512, 512, 1)
     idx, wts = _routing(rng, T, K, E, drop=0.05)
     x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     idx_d = torch.from_numpy(idx).to(DEV)
