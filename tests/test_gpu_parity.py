@@ -186,14 +186,17 @@ def test_skewed_routing_all_to_one_expert():
     run_full_case(x, idx, wts, E, 4, 7, 0, max_rel_1e2=False)
 
 
-def test_out_of_range_ids_flagged():
-    rng = np.random.default_rng(6)
-    T, K, E = 900, 4, 32
+@pytest.mark.parametrize("T,K,E,R", [(900, 4, 32, 4), (3000, 4, 32, 4), (8192, 2, 512, 512)],
+                         ids=["one_workgroup", "chunked", "chunked_scan"])
+def test_out_of_range_ids_flagged(T, K, E, R):
+    """Ids outside [-1, E) set the error flag and count as dropped, on every
+    layout path (bad ids placed in the first and the last chunk)."""
+    rng = np.random.default_rng(6 + T)
     idx, wts = _routing(rng, T, K, E)
     idx[5, 1] = E
-    idx[700, 3] = -9
-    ol = oracle.layout(idx, E, 4, 8)
-    gl = layout_to_host(gpu_layout(idx, E, 4, 8))
+    idx[T - 3, K - 1] = -9
+    ol = oracle.layout(idx, E, R, 8)
+    gl = layout_to_host(gpu_layout(idx, E, R, 8))
     assert ol.error_flag == 1
     assert_layout_equal(gl, ol)
 
