@@ -39,12 +39,15 @@ namespace moe {
 constexpr int kCountThreads = 1024;
 constexpr int kRankThreads = 1024;
 constexpr int kRankWaves = kRankThreads / kWave;
+constexpr int kCountWaves = kCountThreads / kWave;
 constexpr int kIdxPerThread = kMaxChunkEntries / 1024; // topk_idx entries prefetched per thread
 constexpr int kRankCellsPerThread = 2; // per-chunk rank counts prefetched per thread
 constexpr int kRankSumSlots = 512;     // ranks one workgroup can sum (R <= 512)
 constexpr int kTabRows = 16;           // expert-table rows prefetched per thread
 
 static_assert(kCountThreads == 1024 && kRankThreads == 1024, "prefetch sizes assume 1024 threads");
+static_assert(kMaxChunkEntries <= 65536 && MOE_MAX_EXPERTS <= 32768,
+              "packed (expert << 16 | rank) entries between the count and rank kernels");
 
 // Issue this chunk's topk_idx loads (one per thread and pass of 1024 entries;
 // the pass guard is uniform over the workgroup, the index clamped into range).
@@ -74,25 +77,35 @@ __device__ __forceinline__ int exclusive_scan16(int v, int *total)
 __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int L, int tpc, int nbits,
     int32_t *__restrict__ itr, int32_t *__restrict__ cnt_tab, int32_t *__restrict__ rank_tab,
-    int32_t *__restrict__ flag_tab)
+    int32_t *__restrict__ flag_tab, int32_t *__restrict__ token_row)
 {
-    __shared__ int s_hist[MOE_MAX_EXPERTS];
+    __shared__ int s_w[kCountWaves * MOE_MAX_EXPERTS]; // [wave][e], row stride E
     __shared__ int s_rcnt[MOE_MAX_EXPERTS];
     __shared__ uint8_t s_flags[kMaxChunkFlags];
     __shared__ int s_bad;
 
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const int chunk = blockIdx.x;
     const int t0 = chunk * tpc;
-    const int nt = min(tpc, T - t0);
+    const int nt = min(tpc, T - t0); // >= 1: chunks cover [0, T) and T > 0 on this path
     const int ne = nt * K;
     const int64_t base = (int64_t)t0 * K;
 
+    // Each wave owns a contiguous run of entries in flat (token, k) order,
+    // at most kIdxPerThread vectors of 64; the ids are loaded at once (index
+    // clamped into the chunk, entries past the run masked afterwards).
+    const int per_wave = ((ne + kCountThreads - 1) / kCountThreads) * kWave;
+    const int w_lo = wave * per_wave;
+    const int w_hi = min(ne, w_lo + per_wave);
     int64_t idx_reg[kIdxPerThread];
-    prefetch_idx(topk_idx, base, ne, idx_reg); // in flight while LDS is cleared
+#pragma unroll
+    for (int it = 0; it < kIdxPerThread; ++it)
+        idx_reg[it] = it * kWave < per_wave ? topk_idx[base + min(w_lo + it * kWave + lane, ne - 1)] : -1;
 
-    for (int i = tid; i < E; i += kCountThreads)
-        s_hist[i] = 0;
+    for (int i = tid; i < kCountWaves * E; i += kCountThreads)
+        s_w[i] = 0;
     for (int i = tid; i < R; i += kCountThreads)
         s_rcnt[i] = 0;
     for (int i = tid; i < nt * R; i += kCountThreads)
@@ -101,31 +114,62 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
         s_bad = 0;
     __syncthreads();
 
+    // per-wave expert counts: lanes holding the same expert are matched by
+    // one ballot per key bit and the lowest of them adds the group's size
+    // (one writer per (wave, expert) and vector; a wave's vectors are in
+    // program order).  Each lane keeps its expert, its position among the
+    // equal keys of its vector and their number (below | count << 8) in
+    // registers for the ranking below.
+    int e_reg[kIdxPerThread];
+    int pos_reg[kIdxPerThread];
     int bad = 0;
 #pragma unroll
-    for (int u = 0; u < kIdxPerThread; ++u) {
-        if (u * kCountThreads >= ne) // uniform: ballots below stay convergent
-            break;
-        const int i = tid + u * kCountThreads;
-        int e = -1;
-        if (i < ne) {
-            const int64_t v = idx_reg[u];
-            if (v < -1 || v >= E)
-                bad = 1;
-            else
-                e = (int)v;
-        }
-        const bool has = e >= 0;
-        const uint64_t same = match_same_key(e, has, nbits);
-        if (has) {
-            if (count_below(same) == 0)
-                atomicAdd(&s_hist[e], __popcll(same));
-            s_flags[(i / K) * R + e / L] = 1;
+    for (int it = 0; it < kIdxPerThread; ++it) {
+        e_reg[it] = -1;
+        pos_reg[it] = 0;
+        if (it * kWave < per_wave) { // uniform: ballots below stay convergent
+            const int j = w_lo + it * kWave + lane;
+            int e = -1;
+            if (j < w_hi) {
+                const int64_t v = idx_reg[it];
+                if (v < -1 || v >= E)
+                    bad = 1;
+                else
+                    e = (int)v;
+            }
+            const bool has = e >= 0;
+            const uint64_t same = match_same_key(e, has, nbits);
+            const int below = count_below(same);
+            const int n = __popcll(same);
+            if (has) {
+                if (below == 0)
+                    s_w[wave * E + e] += n;
+                s_flags[(j / K) * R + e / L] = 1;
+            }
+            e_reg[it] = e;
+            pos_reg[it] = below | (n << 8);
         }
     }
     if (bad)
         atomicOr(&s_bad, 1);
     __syncthreads();
+
+    // every expert's count over the chunk (one table row) and the exclusive
+    // prefix of the per-wave counts in wave order: the base of each wave's
+    // entries among the chunk's entries of that expert
+    const int Ep = (E + 3) & ~3; // table rows padded to whole 16-byte vectors
+    for (int e = tid; e < Ep; e += kCountThreads) {
+        int run = 0;
+        if (e < E) {
+#pragma unroll
+            for (int w = 0; w < kCountWaves; ++w) {
+                const int v = s_w[w * E + e];
+                s_w[w * E + e] = run;
+                run += v;
+            }
+        }
+        cnt_tab[(int64_t)chunk * Ep + e] = run;
+    }
 
     // is_token_in_rank rows and per-rank token counts: thread (r, part) owns
     // rank r of tokens part, part + parts, ...; a wave's stores cover
@@ -148,9 +192,25 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     }
     __syncthreads();
 
-    const int Ep = (E + 3) & ~3; // table rows padded to whole 16-byte vectors
-    for (int e = tid; e < Ep; e += kCountThreads)
-        cnt_tab[(int64_t)chunk * Ep + e] = e < E ? s_hist[e] : 0;
+    // stable rank of every entry among the chunk's entries of its expert
+    // (wave base + position among the equal keys of its vector), stored in
+    // token_row packed with the expert, (e << 16) | rank, for the rank kernel
+    // to complete; dropped entries get their final -1 here
+#pragma unroll
+    for (int it = 0; it < kIdxPerThread; ++it) {
+        if (it * kWave < per_wave) {
+            const int j = w_lo + it * kWave + lane;
+            const int e = e_reg[it];
+            const int below = pos_reg[it] & 0xFF;
+            if (e >= 0)
+                token_row[base + j] = (e << 16) | (s_w[wave * E + e] + below);
+            else if (j < w_hi)
+                token_row[base + j] = -1;
+            if (e >= 0 && below == 0) // after every lane of the wave has read the running count
+                s_w[wave * E + e] += pos_reg[it] >> 8;
+        }
+    }
+
     for (int r = tid; r < R; r += kCountThreads)
         rank_tab[(int64_t)chunk * R + r] = s_rcnt[r];
     if (tid == 0)
@@ -199,8 +259,8 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(const int32_t *__rest
 }
 
 __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
-    const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int a, int tpc, int nchunks,
-    int nbits, int64_t cap, const int32_t *__restrict__ cnt_tab, const int32_t *__restrict__ rank_tab,
+    int T, int K, int E, int R, int a, int tpc, int nchunks, int64_t cap,
+    const int32_t *__restrict__ cnt_tab, const int32_t *__restrict__ rank_tab,
     const int32_t *__restrict__ flag_tab, const int32_t *__restrict__ cb_tab,
     const int32_t *__restrict__ tot_tab, int32_t *__restrict__ ntpr, int32_t *__restrict__ ntpe,
     int32_t *__restrict__ nrtpe, int32_t *__restrict__ off, int32_t *__restrict__ token_row,
@@ -210,14 +270,10 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     __shared__ int s_cb[MOE_MAX_EXPERTS];
     __shared__ int s_off[MOE_MAX_EXPERTS + 1];
     __shared__ int s_rsum[kRankSumSlots];
-    __shared__ int s_wsum[kRankWaves];
     __shared__ int s_flag;
-    __shared__ int s_w[kRankWaves][MOE_MAX_EXPERTS];
-    __shared__ int16_t s_e[kMaxChunkEntries];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     const int chunk = blockIdx.x;
     const int nblocks = gridDim.x;
     const bool has_chunk = chunk < nchunks; // false only when T == 0 (one workgroup then)
@@ -229,7 +285,8 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     // (0) Every global load the workgroup needs is issued here, before the
     // first barrier (a barrier waits for all outstanding loads), so that the
     // kernel pays one memory round trip:
-    //   - this chunk's topk_idx entries;
+    //   - this chunk's entries as the count kernel left them in token_row,
+    //     (expert << 16) | rank within the chunk, or -1;
     //   - the expert-count table [nchunks][Ep] (Ep = E rounded up to 4): a
     //     thread owns 4 adjacent columns (one 16-byte load per row) and up to
     //     kTabRows rows; rows beyond parts * kTabRows (very many chunks only)
@@ -238,8 +295,10 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     //     r = chunk, chunk + nblocks, ...), one (rank, chunk) cell per thread
     //     and pass;
     //   - in workgroup 0, the per-chunk error flags.
-    int64_t idx_reg[kIdxPerThread];
-    prefetch_idx(topk_idx, base, ne, idx_reg);
+    int32_t ent_reg[kIdxPerThread];
+#pragma unroll
+    for (int u = 0; u < kIdxPerThread; ++u)
+        ent_reg[u] = u * kRankThreads < ne ? token_row[base + min(tid + u * kRankThreads, ne - 1)] : -1;
 
     const int groups = (E + 3) / 4; // <= 128
     const int parts = kRankThreads / groups; // >= 8
@@ -279,13 +338,11 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     }
 
     // (1) expert totals over all chunks, and the part of them in chunks
-    // before this one; this chunk's ids into LDS; this workgroup's rank sums
+    // before this one; this workgroup's rank sums
     for (int e = tid; e < E; e += kRankThreads) {
         s_tot[e] = 0;
         s_cb[e] = 0;
     }
-    for (int i = tid; i < kRankWaves * E; i += kRankThreads)
-        s_w[i / E][i % E] = 0;
     for (int i = tid; i < kRankSumSlots; i += kRankThreads)
         s_rsum[i] = 0;
     if (tid == 0)
@@ -328,14 +385,6 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
         }
     }
 #pragma unroll
-    for (int u = 0; u < kIdxPerThread; ++u) {
-        const int i = tid + u * kRankThreads;
-        if (i < ne) {
-            const int64_t v = idx_reg[u];
-            s_e[i] = (v < 0 || v >= E) ? (int16_t)-1 : (int16_t)v;
-        }
-    }
-#pragma unroll
     for (int u = 0; u < kRankCellsPerThread; ++u) {
         const int cell = tid + u * kRankThreads;
         if (cell < rank_cells && rank_reg[u])
@@ -349,35 +398,33 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     __syncthreads();
 
     // (2) aligned counts and their exclusive prefix sum ("/" is integer
-    // division, CANN page Constraint 11).  No overflow: the host checked
-    // T*K + E*(a-1) < 2^31.
-    int ac = 0;
-    if (tid < E) {
-        const int c = s_tot[tid];
-        ac = ((c + a - 1) / a) * a;
-    }
-    int incl = ac;
+    // division, CANN page Constraint 11), by the first wave alone: lane l
+    // takes experts [l * per, (l + 1) * per), sums their aligned counts, and
+    // a shuffle scan over the 64 lane sums gives every lane its base.  No
+    // overflow: the host checked T*K + E*(a-1) < 2^31.
+    if (tid < kWave) {
+        const int per = (E + kWave - 1) / kWave; // <= 8
+        const int e0 = lane * per;
+        int sum = 0;
+        for (int c = 0; c < per; ++c)
+            if (e0 + c < E)
+                sum += ((s_tot[e0 + c] + a - 1) / a) * a;
+        int incl = sum;
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int v = __shfl_up(incl, d, kWave);
-        if (lane >= d)
-            incl += v;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int v = __shfl_up(incl, d, kWave);
+            if (lane >= d)
+                incl += v;
+        }
+        int run = incl - sum;
+        for (int c = 0; c < per; ++c)
+            if (e0 + c < E) {
+                s_off[e0 + c] = run;
+                run += ((s_tot[e0 + c] + a - 1) / a) * a;
+            }
+        if (lane == kWave - 1)
+            s_off[E] = incl;
     }
-    if (lane == kWave - 1)
-        s_wsum[wave] = incl;
-    __syncthreads();
-    if (wave == 0) { // exclusive scan of the 16 wave sums by the first 16 lanes
-        int total;
-        const int v = lane < kRankWaves ? s_wsum[lane] : 0;
-        const int ex = exclusive_scan16(v, &total);
-        if (lane < kRankWaves)
-            s_wsum[lane] = ex;
-    }
-    __syncthreads();
-    if (tid < E)
-        s_off[tid] = s_wsum[wave] + incl - ac;
-    if (tid == E - 1)
-        s_off[E] = s_wsum[wave] + incl;
     __syncthreads();
 
     // (3) the small outputs: per-expert ones and the error flag from workgroup
@@ -413,50 +460,18 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     if (!has_chunk)
         return;
 
-    // (5) rank this chunk's entries (ids in s_e); each wave owns a contiguous
-    // run of entries, in flat order
-    const int per_wave = ((ne + kRankWaves * kWave - 1) / (kRankWaves * kWave)) * kWave;
-    const int w_lo = wave * per_wave;
-    const int w_hi = min(ne, w_lo + per_wave);
-
-    for (int j0 = w_lo; j0 < w_lo + per_wave; j0 += kWave) {
-        const int j = j0 + lane;
-        const int e = (j < w_hi) ? (int)s_e[j] : -1;
-        const bool has = e >= 0;
-        const uint64_t same = match_same_key(e, has, nbits);
-        if (has && count_below(same) == 0)
-            s_w[wave][e] += __popcll(same); // one writer per (wave, expert)
-    }
-    __syncthreads();
-    // exclusive scan over the 16 waves of every expert's count, one thread per
-    // expert (consecutive experts: conflict-free LDS banks)
-    for (int e = tid; e < E; e += kRankThreads) {
-        int run = 0;
+    // (5) each entry's row: expert base + the expert's entries in earlier
+    // chunks + its rank within this chunk (dropped entries are already -1)
 #pragma unroll
-        for (int w = 0; w < kRankWaves; ++w) {
-            const int v = s_w[w][e];
-            s_w[w][e] = run;
-            run += v;
+    for (int u = 0; u < kIdxPerThread; ++u) {
+        const int i = tid + u * kRankThreads;
+        const int v = ent_reg[u];
+        if (i < ne && v >= 0) {
+            const int e = v >> 16;
+            const int row = s_off[e] + s_cb[e] + (v & 0xFFFF);
+            token_row[base + i] = row;
+            recv_src[row] = (int32_t)(base + i);
         }
-    }
-    __syncthreads();
-
-    for (int j0 = w_lo; j0 < w_lo + per_wave; j0 += kWave) {
-        const int j = j0 + lane;
-        const bool in = j < w_hi;
-        const int e = in ? (int)s_e[j] : -1;
-        const bool has = e >= 0;
-        const uint64_t same = match_same_key(e, has, nbits);
-        const int below = count_below(same);
-        if (has) {
-            const int row = s_off[e] + s_cb[e] + s_w[wave][e] + below;
-            token_row[base + j] = row;
-            recv_src[row] = (int32_t)(base + j);
-        } else if (in) {
-            token_row[base + j] = -1;
-        }
-        if (has && below == 0) // after every lane of the wave has read the running count
-            s_w[wave][e] += __popcll(same);
     }
 }
 
@@ -692,7 +707,8 @@ hipError_t launch_layout(const LayoutArgs &A, const LayoutPlan &P, hipStream_t s
     if (nchunks > 0) {
         hipError_t err = launch_kernel(
             layout_count_kernel, dim3(nchunks), dim3(kCountThreads), 0, stream, A.topk_idx, A.T,
-            A.K, A.E, A.R, L, P.tokens_per_chunk, nbits, A.itr, cnt_tab, rank_tab, flag_tab);
+            A.K, A.E, A.R, L, P.tokens_per_chunk, nbits, A.itr, cnt_tab, rank_tab, flag_tab,
+            A.token_row);
         if (err != hipSuccess)
             return err;
         if (P.scan) {
@@ -704,8 +720,8 @@ hipError_t launch_layout(const LayoutArgs &A, const LayoutPlan &P, hipStream_t s
         }
     }
     return launch_kernel(layout_rank_kernel, dim3(nchunks > 0 ? nchunks : 1), dim3(kRankThreads), 0,
-                         stream, A.topk_idx, A.T, A.K, A.E, A.R, A.a, P.tokens_per_chunk, nchunks,
-                         nbits, A.cap, cnt_tab, rank_tab, flag_tab, (const int32_t *)cb_tab,
+                         stream, A.T, A.K, A.E, A.R, A.a, P.tokens_per_chunk, nchunks, A.cap,
+                         cnt_tab, rank_tab, flag_tab, (const int32_t *)cb_tab,
                          (const int32_t *)tot_tab, A.ntpr, A.ntpe, A.nrtpe, A.off, A.token_row,
                          A.recv_src, A.error_flag);
 }
