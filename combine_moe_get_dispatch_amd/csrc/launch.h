@@ -80,7 +80,7 @@ constexpr int kMaxChunkEntries = 8192;
 constexpr int kMaxChunkFlags = 16384;
 // Batches of at most this many routing entries (and T*R <= kMaxChunkFlags)
 // are laid out by one workgroup in one launch.
-constexpr int kSingleLayoutMaxEntries = 4096;
+constexpr int kSingleLayoutMaxEntries = 3072;
 
 // From this many count-table cells (chunks x E rounded up to 4) on, a
 // column-scan launch between the two kernels forms each chunk's prefix row

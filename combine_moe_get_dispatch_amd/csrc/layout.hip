@@ -489,11 +489,13 @@ __device__ __forceinline__ int div_small(int n, int d)
 // entries and T*R <= kMaxChunkFlags token x rank cells): every entry lives in
 // LDS, so the histogram, the aligned scan and the ranks need no count table
 // and no second launch.  All the ballot matching runs on one CU, so its cost
-// grows with the batch (about 1.3 ns per entry); the two-launch layout
-// (~13 us) wins above about 4096 entries.  The per-wave expert counts are the histogram: their sum over the
-// waves is the expert total, their exclusive prefix over the waves the wave's
-// base, exactly as in layout_rank_kernel with a single chunk.  Counts are
-// held in 16 bits (at most kMaxChunkEntries entries per batch).
+// grows with the batch (about 1.3 ns per entry): measured as graph replays,
+// 4.6 us for 128 x 2 entries and 7.2 us for 128 x 8, level with the
+// two-launch layout (a flat ~10.2 us at these sizes) at 3072 entries and
+// 1.5 us slower at 4096.  The per-wave expert counts are the histogram: their
+// sum over the waves is the expert total, their exclusive prefix over the
+// waves the wave's base, as in layout_count_kernel with a single chunk.
+// Counts are held in 16 bits (at most kMaxChunkEntries entries per batch).
 __global__ __launch_bounds__(kRankThreads) void layout_single_kernel(
     const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int L, int a, int nbits,
     int64_t cap, int32_t *__restrict__ itr, int32_t *__restrict__ ntpr, int32_t *__restrict__ ntpe,

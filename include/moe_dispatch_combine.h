@@ -108,7 +108,7 @@ int64_t moe_recv_capacity_bound(int num_tokens, int num_topk, int num_experts,
  * Bytes of device workspace moe_get_dispatch_layout needs for these sizes
  * (first phase of the CANN page's two-phase pattern).  0 if the arguments are
  * invalid, and 0 when no workspace is needed: num_tokens is 0, or the batch is
- * small enough (num_tokens*num_topk <= 4096 and num_tokens*num_ranks <= 16384)
+ * small enough (num_tokens*num_topk <= 3072 and num_tokens*num_ranks <= 16384)
  * to be laid out by one workgroup in one launch.  Then workspace may be NULL.
  * The workspace needs no initialisation; its contents after the call are
  * unspecified.

@@ -117,10 +117,11 @@ def test_scan_layout_workspace(L):
 
 
 def test_small_batches_need_no_workspace(L):
-    # one workgroup takes the whole batch when T*K <= 4096 and T*R <= 16384
-    assert L.moe_layout_workspace_bytes(512, 8, 256, 8) == 0
-    assert L.moe_layout_workspace_bytes(4096, 1, 64, 4) == 0
-    assert L.moe_layout_workspace_bytes(513, 8, 256, 8) > 0
+    # one workgroup takes the whole batch when T*K <= 3072 and T*R <= 16384
+    assert L.moe_layout_workspace_bytes(384, 8, 256, 8) == 0
+    assert L.moe_layout_workspace_bytes(3072, 1, 64, 4) == 0
+    assert L.moe_layout_workspace_bytes(385, 8, 256, 8) > 0
+    assert L.moe_layout_workspace_bytes(512, 8, 256, 8) > 0
     assert L.moe_layout_workspace_bytes(1024, 2, 512, 32) > 0     # T*R > 16384
 
 

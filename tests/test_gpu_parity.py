@@ -154,11 +154,11 @@ EDGE = [
     ("fp8_e5m2_per_group", 700, 4096, 64, 8, 8, 16, 0x23, True, 0.05),
     ("fp8_e4m3_per_group_partial", 300, 160, 16, 4, 4, 8, 0x13, False, 0.1),
     ("fp8_e5m2_per_group_max_hidden", 40, 16384, 128, 8, 8, 32, 0x23, False, 0.0),
-    # the limits of the one-workgroup layout: T*K <= 4096 and T*R <= 16384
-    ("single_layout_max_entries", 512, 64, 256, 8, 8, 1, 0, False, 0.0),
-    ("chunked_layout_min_entries", 513, 64, 256, 8, 8, 1, 0, False, 0.0),
-    ("single_layout_max_flags", 2048, 32, 64, 8, 2, 2, 0, False, 0.05),
-    ("chunked_layout_flags_over", 1024, 32, 512, 32, 4, 1, 0, False, 0.0),
+    # the limits of the one-workgroup layout: T*K <= 3072 and T*R <= 16384
+    ("single_layout_max_entries", 384, 64, 256, 8, 8, 1, 0, False, 0.0),
+    ("chunked_layout_min_entries", 385, 64, 256, 8, 8, 1, 0, False, 0.0),
+    ("single_layout_max_flags", 2048, 32, 64, 8, 1, 2, 0, False, 0.05),
+    ("chunked_layout_flags_over", 1024, 32, 512, 32, 2, 1, 0, False, 0.0),
     # count tables of >= 131072 cells: the column-scan launch between count and rank
     ("scan_layout_e512_r512", 8192, 32, 512, 512, 2, 1, 0, False, 0.0),
     ("scan_layout_ragged_a7_drop", 8200, 64, 512, 512, 3, 7, 0, False, 0.2),
