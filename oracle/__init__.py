@@ -58,12 +58,22 @@ _lib = None
 _P = ctypes.c_void_p
 
 
+# A prebuilt copy of this oracle to load instead of oracle/libmoe_oracle.so.
+# Set only by the mutation test, which builds the oracle with one planted
+# mistake and checks that the pin tests fail against it.
+_OVERRIDE = os.environ.get("MOE_ORACLE_LIB_OVERRIDE")
+
+
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB_PATH)
+        if _OVERRIDE:
+            path = _OVERRIDE
+        else:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build()
+            path = _LIB_PATH
+        L = ctypes.CDLL(path)
         i32, i64 = ctypes.c_int, ctypes.c_int64
         L.oracle_recv_capacity_bound.argtypes = [i32, i32, i32, i32]
         L.oracle_recv_capacity_bound.restype = i64

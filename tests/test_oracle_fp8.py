@@ -8,7 +8,8 @@ MXFP8 e5m2 (CANN aclnnMoeDistributeDispatchV2, Formula Case 5, emax 15):
   hand-worked block, block exponent against frexp, block maximum lands in the
   top binade, reconstruction bound.
 Per-token FP8 (Formula Case 3 with dstTypeMax = 448 or 57344): rows whose
-  scale is exactly 1 or a power of two give the element casts; the fp32
+  scale is exactly 1 or a power of two give the element casts, wherever in
+  the row the maximum lies; the fp32
   formula re-evaluated in exact rationals; invariants.
 Pre-quantised rows: copied byte for byte to the layout rows.
 """
@@ -221,3 +222,20 @@ def test_prequantized_rules(orc, args, code):
 @pytest.mark.parametrize("q,code", [(0x12, 0), (0x22, 0), (0x24, 0), (0x14, -1), (0x32, -1), (0x02, 0), (0x42, -1)])
 def test_new_quant_mode_rules(orc, q, code):
     assert orc.check_rows_args(16, 1024, 4, 1000, q) == code
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_pertoken_fp8_row_maximum_at_every_position(orc, fmt):
+    # row p holds +-dstTypeMax at position p and smaller values elsewhere, so
+    # the row maximum is met at every index, the last included: every scale is
+    # exactly 1 and the codes are the element casts
+    vmax = {"e4m3": 448.0, "e5m2": 57344.0}[fmt]
+    cast = orc.cast_to_fp8_e4m3fn if fmt == "e4m3" else orc.cast_to_fp8_e5m2
+    rng = np.random.default_rng(36)
+    H = 64
+    v = W.bf16_bits_to_f32(bf16(rng.uniform(-vmax / 2, vmax / 2, (H, H)).astype(np.float32)))
+    p = np.arange(H)
+    v[p, p] = np.where(p % 2 == 0, vmax, -vmax)
+    q, s = orc.quant_fp8_pertoken_rows(bf16(v), fmt)
+    np.testing.assert_array_equal(s, np.ones(H, np.float32))
+    np.testing.assert_array_equal(q, cast(v))

@@ -3,7 +3,8 @@ Formula Case 4 = Case 3 per group of 128) and static int8 quantisation
 (Formula Case 2).
 
 Per-group: groups whose maximum is the destination's largest value have scale
-exactly 1 and give the element casts; groups are independent (different
+exactly 1 and give the element casts, wherever in the group the maximum
+lies; groups are independent (different
 magnitudes in neighbouring groups give their own power-of-two scales); a
 partial last group; a zero group next to normal groups; the fp32 formula in
 exact rationals.
@@ -39,6 +40,23 @@ def test_pergroup_groups_are_independent(orc, fmt):
     q, s = orc.quant_fp8_pergroup_rows(bf16(x), fmt)
     np.testing.assert_array_equal(q, cast(orc, fmt)(v))
     np.testing.assert_array_equal(s, np.tile(np.array([8.0, 2.0 ** -5, 1.0], np.float32), (2, 1)))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_pergroup_maximum_at_every_position(orc, fmt):
+    # row p holds the destination's largest value at position p of group 0
+    # and at position 127 - p of group 1 (every other element smaller), so
+    # each group's maximum is met at every index, the first and last
+    # included: every scale is exactly 1 and the codes are the element casts
+    rng = np.random.default_rng(34)
+    vmax = VMAX[fmt]
+    v = W.bf16_bits_to_f32(bf16(rng.uniform(-vmax / 2, vmax / 2, (128, 256)).astype(np.float32)))
+    p = np.arange(128)
+    v[p, p] = -vmax
+    v[p, 255 - p] = vmax
+    q, s = orc.quant_fp8_pergroup_rows(bf16(v), fmt)
+    assert (s == 1.0).all()
+    np.testing.assert_array_equal(q, cast(orc, fmt)(v))
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])

@@ -87,6 +87,20 @@ def test_int8_integer_rows(orc):
     np.testing.assert_array_equal(s, np.ones(16, np.float32))
 
 
+def test_int8_row_maximum_at_every_position(orc):
+    # row p holds +-127 at position p and smaller integers everywhere else, so
+    # the row maximum is met at every index, the last included: every scale is
+    # exactly 1 and the codes are the values themselves
+    rng = np.random.default_rng(35)
+    H = 64
+    v = rng.integers(-100, 101, size=(H, H)).astype(np.float32)
+    p = np.arange(H)
+    v[p, p] = np.where(p % 2 == 0, 127.0, -127.0)
+    q, s = orc.quant_int8_rows(bf16(v))
+    np.testing.assert_array_equal(s, np.ones(H, np.float32))
+    np.testing.assert_array_equal(q, v.astype(np.int8))
+
+
 @pytest.mark.parametrize("j", [-30, -7, -1, 1, 5, 20, 60])
 def test_int8_power_of_two_rows(orc, j):
     # x = v * 2^j with max |v| = 127: dynamicScales = 2^-j exactly, codes = v, scale = 2^j.
