@@ -14,17 +14,23 @@
 // entries) is laid out by layout_single_kernel, one workgroup and one launch
 // (below).  Larger batches are split into chunks of whole tokens, one
 // workgroup per chunk, in two launches:
-//   layout_count_kernel: per-chunk expert histogram.  Lanes of a wave holding
-//     the same expert are found with one ballot per key bit; the lowest of them
-//     adds the group's popcount to an LDS counter, so a hot expert costs one
-//     LDS atomic per wave instead of one per lane.  The same pass marks
-//     token x rank membership in LDS and writes is_token_in_rank rows.
+//   layout_count_kernel: each wave takes a contiguous run of the chunk's
+//     entries in flat (token, k) order.  Lanes holding the same expert are
+//     found with one ballot per key bit; the lowest of them writes the
+//     group's size into the wave's LDS count for that expert (one writer, no
+//     atomics).  The exclusive prefix of those counts over the waves gives
+//     each wave's base, so base + position among equal keys (a masked
+//     popcount) is the entry's stable rank within the chunk.  The kernel
+//     stores it in token_row packed with the expert, (e << 16) | rank, and
+//     writes the chunk's expert totals as one row of a [chunks][E] table.
+//     The same pass marks token x rank membership in LDS and writes the
+//     is_token_in_rank rows.
 //   layout_rank_kernel: every workgroup re-derives the expert totals and its
-//     own chunk base from the small [chunks][E] table (L2 resident), scans the
-//     aligned totals in LDS, then ranks its chunk: per-wave counts, an
-//     exclusive scan over waves, and within a wave the position among equal
-//     keys by masked popcount.  Ranks therefore come from prefix sums only
-//     (never from atomic return order), which makes the result deterministic.
+//     own chunk base from the small [chunks][E] table, scans the aligned
+//     totals in one wave, and turns each packed entry of its chunk into the
+//     row off[e] + (entries of e in earlier chunks) + rank.  Ranks come from
+//     prefix sums only (never from atomic return order), which makes the
+//     result deterministic.
 // When many ranks force many small chunks, the table is large (from
 // kLayoutScanMinCells cells on) and layout_scan_kernel runs between the two:
 // it forms the column prefix sums and the totals once, and each rank
