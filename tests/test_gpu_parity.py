@@ -783,3 +783,29 @@ def test_binding_rejects_mismatched_layouts():
     moe.moe_combine(y, lay)
     moe.moe_dispatch(x, lay)
     torch.cuda.synchronize()
+
+
+def test_binding_uses_the_current_stream():
+    """The stream handle passed to the library is torch's current stream:
+    the default one, one set by a stream context, and for a device given
+    without an index; work queued on a side stream and waited for lands."""
+    dev_noindex = torch.device("cuda")
+    handle = lambda d: moe._stream(d).value or 0      # the default stream's handle is 0
+    assert handle(DEV) == torch.cuda.current_stream(DEV).cuda_stream
+    assert handle(dev_noindex) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    rng = np.random.default_rng(93)
+    T, H, K, E, R = 48, 512, 4, 16, 4
+    idx, wts = _routing(rng, T, K, E)
+    x = bf16_dev(W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert handle(DEV) == side.cuda_stream != 0
+        lay = gpu_layout(idx, E, R, 1)
+        rx, _, _ = moe.moe_dispatch(x, lay)
+    torch.cuda.current_stream().wait_stream(side)
+    ol = oracle.layout(idx, E, R, 1)
+    assert_layout_equal(layout_to_host(lay), ol)
+    orx, _, _ = oracle.dispatch(bf16_host_bits(x), ol.token_row, ol.recv_capacity)
+    used = ol.recv_src >= 0
+    np.testing.assert_array_equal(bf16_host_bits(rx)[used], orx[used])
