@@ -64,6 +64,10 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="time replays of one captured HIP graph of the step instead of eager launches "
                         "(stage times then come from an eager pass with events before it)")
+    p.add_argument("--one-launch", action="store_true",
+                   help="lay out and dispatch with moe_layout_and_dispatch, one launch (bf16 "
+                        "workloads whose batch it takes); the layout stage's time is then that "
+                        "launch and the dispatch stage's is empty")
     p.add_argument("--no-check", action="store_true", help="skip the post-run sanity check")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run 3 torch copies of 256 MiB: a kernel of known traffic "
@@ -342,10 +346,24 @@ def main():
 
     timer = StageEvents(torch)
 
+    if args.one_launch:
+        if quant != 0 or w.prequant or w.static_scale > 0 or not moe.moe_layout_and_dispatch_fits(T, H, K, R):
+            raise SystemExit(f"--one-launch takes unquantised batches of at most 512 tokens, 3072 "
+                             f"entries and hidden 8192; {w.name} is not one")
+
+        def run_layout():
+            moe.moe_layout_and_dispatch(idx, x, E, R, a, None, out=lay, recv_x=rx)
+
+        def run_dispatch():
+            pass
+    else:
+        def run_layout():
+            moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)
+
     def step(ev=None):
         if ev is not None:
             timer.record(ev[0])
-        moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)
+        run_layout()
         if ev is not None:
             timer.record(ev[1])
         run_dispatch()
@@ -416,8 +434,7 @@ def main():
     if args.cold_reps > 0:
         flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         flush64 = flush.view(torch.int64)
-        stages = [("layout", lambda: moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)),
-                  ("dispatch", run_dispatch), ("combine", run_combine)]
+        stages = [("layout", run_layout), ("dispatch", run_dispatch), ("combine", run_combine)]
         cold = {"reps": args.cold_reps}
         for kind, evict in (("fill", lambda n: flush.fill_(n)), ("read", lambda n: flush64.sum())):
             cev = [[(timer.new(), timer.new()) for _ in stages] for _ in range(args.cold_reps)]
@@ -497,7 +514,8 @@ def main():
         "stage_events": {"kind": timer.kind, "every_nth_step": every, "samples": len(events),
                          "timed_region": "eager pass before the graph replays" if graph is not None
                          else "the timed steps"},
-        "launch": "graph replay" if graph is not None else "eager",
+        "launch": ("graph replay" if graph is not None else "eager")
+                  + (", layout and dispatch in one launch" if args.one_launch else ""),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic(w.name, dom),

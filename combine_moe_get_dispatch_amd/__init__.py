@@ -88,6 +88,10 @@ def declare_signatures(L: ctypes.CDLL) -> ctypes.CDLL:
     L.moe_combine.restype = i32
     L.moe_combine_fused.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, P, P, P]
     L.moe_combine_fused.restype = i32
+    L.moe_layout_and_dispatch_fits.argtypes = [i32, i32, i32, i32]
+    L.moe_layout_and_dispatch_fits.restype = i32
+    L.moe_layout_and_dispatch.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i64, P] + [P] * 8 + [P, P, P]
+    L.moe_layout_and_dispatch.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
     return L
@@ -341,6 +345,56 @@ def moe_dispatch(x: torch.Tensor, layout: DispatchLayout, topk_weights: Optional
     if rc != MOE_OK:
         raise MoeError("moe_dispatch", rc)
     return recv_x, recv_scales, recv_weights
+
+
+def moe_layout_and_dispatch_fits(num_tokens: int, hidden: int, num_topk: int, num_ranks: int) -> bool:
+    return bool(lib().moe_layout_and_dispatch_fits(num_tokens, hidden, num_topk, num_ranks))
+
+
+def moe_layout_and_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, num_experts: int, num_ranks: int,
+                            expert_alignment: int = 1, topk_weights: Optional[torch.Tensor] = None,
+                            recv_capacity: Optional[int] = None, out: Optional[DispatchLayout] = None,
+                            recv_x: Optional[torch.Tensor] = None,
+                            recv_weights: Optional[torch.Tensor] = None, with_weights: bool = False):
+    """moe_get_dispatch_layout and an unquantised moe_dispatch, in one launch
+    when the batch is decode-sized (moe_layout_and_dispatch_fits), else as
+    the two calls; the results are the same either way.  Returns (layout,
+    recv_x, recv_weights)."""
+    if topk_idx.dim() != 2 or x.dim() != 2 or x.shape[0] != topk_idx.shape[0]:
+        raise ValueError("topk_idx must be [num_tokens, num_topk] and x [num_tokens, hidden]")
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    if not moe_layout_and_dispatch_fits(T, H, K, num_ranks):
+        lay = moe_get_dispatch_layout(topk_idx, num_experts, num_ranks, expert_alignment, recv_capacity,
+                                      out)
+        rx, _, rw = moe_dispatch(x, lay, topk_weights, QUANT_NONE, recv_x=recv_x,
+                                 recv_weights=recv_weights, with_weights=with_weights)
+        return lay, rx, rw
+    dev = topk_idx.device
+    _check(topk_idx, "topk_idx", torch.int64)
+    _check(x, "x", torch.bfloat16, device=dev)
+    if topk_weights is not None:
+        _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    if out is None:
+        out = allocate_layout(T, K, num_experts, num_ranks, expert_alignment, recv_capacity, dev)
+    elif (out.num_tokens, out.num_topk, out.num_experts, out.num_ranks, out.expert_alignment) != (
+            T, K, num_experts, num_ranks, expert_alignment):
+        raise ValueError("preallocated layout was made for other sizes")
+    _check_layout(out, dev)
+    cap = out.recv_capacity
+    if recv_x is None:
+        recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    _check(recv_x, "recv_x", torch.bfloat16, (cap, H), dev)
+    if recv_weights is None and with_weights:
+        recv_weights = torch.empty(cap, dtype=torch.float32, device=dev)
+    if recv_weights is not None:
+        _check(recv_weights, "recv_weights", torch.float32, (cap,), dev)
+    rc = lib().moe_layout_and_dispatch(
+        _ptr(topk_idx), _ptr(x), T, H, K, num_experts, num_ranks, expert_alignment, cap,
+        _ptr(topk_weights), *out._layout_ptrs[:8], _ptr(recv_x), _ptr(recv_weights), _stream(dev))
+    if rc != MOE_OK:
+        raise MoeError("moe_layout_and_dispatch", rc)
+    return out, recv_x, recv_weights
 
 
 def moe_dispatch_static(x: torch.Tensor, layout: DispatchLayout, scales: torch.Tensor,

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 # grid-stride iterations of the kernels run at test sizes.
 SMALL_GRID_LIB_PATH = os.path.join(HERE, "libmoe_dispatch_combine_smallgrid.so")
 SMALL_GRID_FLAGS = ["-DMOE_MAX_GRID_LOG2=6"]
-SOURCES = ["moe_api.hip", "layout.hip", "dispatch.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "small_batch.hip"]
 HEADERS = ["device_common.h", "launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -5,6 +5,7 @@
 // queue kernels on the caller's stream.  Nothing is allocated and nothing
 // waits for the GPU.
 #include "launch.h"
+#include "small_batch.h"
 
 #include "../../include/moe_dispatch_combine.h"
 
@@ -121,6 +122,62 @@ int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_top
     args.error_flag = error_flag;
     args.workspace = (int32_t *)workspace;
     return launch_layout(args, plan, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_layout_and_dispatch_fits(int num_tokens, int hidden, int num_topk, int num_ranks)
+{
+    return small_batch_fits(num_tokens, hidden, num_topk, num_ranks) ? 1 : 0;
+}
+
+int moe_layout_and_dispatch(const int64_t *topk_idx, const void *x, int num_tokens, int hidden,
+                            int num_topk, int num_experts, int num_ranks, int expert_alignment,
+                            int64_t recv_capacity, const float *topk_weights,
+                            int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                            int32_t *is_token_in_rank, int32_t *num_recv_tokens_per_expert,
+                            int32_t *expert_offsets, int32_t *token_row, int32_t *recv_src,
+                            int32_t *error_flag, void *recv_x, float *recv_weights,
+                            hipStream_t stream)
+{
+    const int T = num_tokens, H = hidden, K = num_topk, E = num_experts, R = num_ranks,
+              a = expert_alignment;
+    int rc = check_layout_sizes(T, K, E, R, a, recv_capacity);
+    if (rc != MOE_OK)
+        return rc;
+    rc = check_rows_sizes(T, H, K, recv_capacity, MOE_QUANT_NONE);
+    if (rc != MOE_OK)
+        return rc;
+    if (!small_batch_fits(T, H, K, R))
+        return MOE_ERR_INVALID_ARG;
+    if (!num_tokens_per_rank || !num_tokens_per_expert || !num_recv_tokens_per_expert ||
+        !expert_offsets || !error_flag)
+        return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!topk_idx || !is_token_in_rank || !token_row || !x || !recv_x ||
+                  !aligned16(x) || !aligned16(recv_x)))
+        return MOE_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && !recv_src)
+        return MOE_ERR_INVALID_ARG;
+
+    LayoutArgs args;
+    args.topk_idx = topk_idx;
+    args.T = T;
+    args.K = K;
+    args.E = E;
+    args.R = R;
+    args.a = a;
+    args.cap = recv_capacity;
+    args.ntpr = num_tokens_per_rank;
+    args.ntpe = num_tokens_per_expert;
+    args.itr = is_token_in_rank;
+    args.nrtpe = num_recv_tokens_per_expert;
+    args.off = expert_offsets;
+    args.token_row = token_row;
+    args.recv_src = recv_src;
+    args.error_flag = error_flag;
+    args.workspace = nullptr;
+    return launch_layout_dispatch_small(args, x, H, topk_weights, recv_x, recv_weights, stream) ==
+                   hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
 }
 
 int moe_dispatch(const void *x, int num_tokens, int hidden, int num_topk,

@@ -15,6 +15,9 @@
  *   moe_combine                top-k weighted sum of every token's expert rows
  *   moe_combine_fused          the same plus shared-expert and residual adds
  *                              and an optional RMS normalisation
+ *   moe_layout_and_dispatch    moe_get_dispatch_layout and an unquantised
+ *                              moe_dispatch in one launch, for decode-sized
+ *                              batches (moe_layout_and_dispatch_fits)
  * plus the size queries moe_recv_capacity_bound and moe_layout_workspace_bytes.
  *
  * Sources, by page title and section:
@@ -290,6 +293,47 @@ int moe_combine_fused(const void *expert_out, int64_t recv_capacity, int num_tok
                       int num_topk, const int32_t *token_row, const float *topk_weights,
                       const void *shared_out, const void *residual, const void *rms_weight,
                       float rms_eps, void *out, void *out_norm, hipStream_t stream);
+
+/*
+ * 1 if moe_layout_and_dispatch takes a batch of these sizes, else 0:
+ * 0 <= num_tokens <= 512, num_tokens*num_topk <= 3072,
+ * num_tokens*num_ranks <= 16384 and hidden <= 8192 (the remaining argument
+ * rules are those of moe_get_dispatch_layout and moe_dispatch).  Larger
+ * batches use the two calls.
+ */
+int moe_layout_and_dispatch_fits(int num_tokens, int hidden, int num_topk, int num_ranks);
+
+/*
+ * moe_get_dispatch_layout followed by moe_dispatch with quant_mode
+ * MOE_QUANT_NONE, in one launch, for decode-sized batches (the same pages
+ * and definitions as those two calls).  At such sizes the two-call form is
+ * bound by fixed costs: two launches, and the layout's store of token_row
+ * that dispatch reads back.  Here one workgroup per token derives the whole
+ * small layout itself (every workgroup computes the same expert totals and
+ * offsets from the same ids, so none waits for another) and copies its
+ * token to its rows.
+ *
+ * Every output equals, bit for bit, what moe_get_dispatch_layout and
+ * moe_dispatch (bf16, same topk_weights and recv_weights) write: the layout
+ * arrays, recv_src with -1 on padding and unused rows, the bf16 rows, the
+ * row weights.  Rows holding no entry are not written.
+ * Inputs (device): topk_idx int64 [T, K]; x bf16 [T, H], 16-byte aligned;
+ *   topk_weights fp32 [T, K] or NULL (only read for recv_weights).
+ * Outputs (device): as moe_get_dispatch_layout (no workspace is needed);
+ *   recv_x bf16 [recv_capacity, H], 16-byte aligned; recv_weights fp32
+ *   [recv_capacity] or NULL.
+ * Errors: MOE_ERR_INVALID_ARG (including sizes that
+ *   moe_layout_and_dispatch_fits rejects), MOE_ERR_CAPACITY, MOE_ERR_HIP;
+ *   out-of-range expert ids set bit 0 of *error_flag, as in the layout call.
+ */
+int moe_layout_and_dispatch(const int64_t *topk_idx, const void *x, int num_tokens, int hidden,
+                            int num_topk, int num_experts, int num_ranks, int expert_alignment,
+                            int64_t recv_capacity, const float *topk_weights,
+                            int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                            int32_t *is_token_in_rank, int32_t *num_recv_tokens_per_expert,
+                            int32_t *expert_offsets, int32_t *token_row, int32_t *recv_src,
+                            int32_t *error_flag, void *recv_x, float *recv_weights,
+                            hipStream_t stream);
 
 /* Static text for a status code. */
 const char *moe_status_string(int status);

@@ -198,3 +198,32 @@ def test_combine_fused_rules(L):
     assert f(BAD, 1000, 16, 64, 4, BAD, None, ctypes.c_void_p(0x1002), None, None, 0.0, BAD, None, None) == -1
     assert f(BAD, 1000, 16, 64, 4, None, None, None, None, None, 0.0, BAD, None, None) == -1
     assert f(None, 1000, 0, 64, 4, None, None, None, None, None, 0.0, None, None, None) == 0
+
+
+def test_layout_and_dispatch_limits_and_rules(L, orc):
+    """The one-launch layout + dispatch: its size limits, and host-side
+    rejections (nothing reaches HIP in any of these calls)."""
+    assert L.moe_layout_and_dispatch_fits(512, 8192, 6, 32) == 1
+    assert L.moe_layout_and_dispatch_fits(0, 32, 1, 1) == 1
+    assert L.moe_layout_and_dispatch_fits(513, 1024, 1, 1) == 0      # tokens
+    assert L.moe_layout_and_dispatch_fits(384, 1024, 9, 8) == 0      # 3456 entries
+    assert L.moe_layout_and_dispatch_fits(512, 1024, 2, 64) == 0     # 32768 token x rank cells
+    assert L.moe_layout_and_dispatch_fits(128, 8224, 8, 8) == 0      # hidden
+
+    def call(T=128, H=7168, K=8, E=256, R=8, a=1, cap=None, idx=BAD, x=BAD, rx=BAD, outs=None):
+        cap = orc.recv_capacity_bound(T, K, E, a) if cap is None else cap
+        outs = [BAD] * 8 if outs is None else outs
+        return L.moe_layout_and_dispatch(idx, x, T, H, K, E, R, a, cap, None, *outs, rx, None, None)
+
+    assert call(T=600, K=1) == -1                       # beyond the one-launch limits
+    assert call(H=8224) == -1
+    assert call(H=100) == -1                            # not a multiple of 32
+    assert call(E=255) == -1                            # ranks do not divide experts
+    assert call(K=17) == -1
+    assert call(cap=100) == -2                          # below the capacity bound
+    assert call(x=None) == -1
+    assert call(idx=None) == -1
+    assert call(x=ctypes.c_void_p(0x1008)) == -1        # not 16-byte aligned
+    assert call(rx=ctypes.c_void_p(0x1004)) == -1
+    assert call(outs=[BAD] * 6 + [None, BAD]) == -1     # recv_src missing
+    assert call(outs=[None] + [BAD] * 7) == -1          # num_tokens_per_rank missing

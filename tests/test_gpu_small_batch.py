@@ -1,0 +1,125 @@
+"""GPU parity of the one-launch layout + bf16 dispatch for decode-sized
+batches (moe_layout_and_dispatch) against the oracle, and against the
+two-call form on the same inputs.
+
+Bar: every layout output bit-exact; every valid receive row bit-exact;
+rows no entry names keep the sentinel they were filled with; row weights
+bit-exact.  Seeded random shapes cover T = 0, single tokens, the limits
+(3072 entries, 16384 token x rank cells, 512 tokens, hidden 8192), one
+expert, duplicated and dropped entries, out-of-range ids, alignment and a
+capacity above the bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_get_dispatch_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import combine_moe_get_dispatch_amd as moe
+    from gpu_util import (DEV, assert_layout_equal, bf16_dev, bf16_host_bits, gpu_layout,
+                          layout_to_host)
+
+SENTINEL = np.int16(np.uint16(0xFFFF).view(np.int16))   # a bf16 NaN no dispatch writes
+
+
+def _config(i):
+    rng = np.random.default_rng(7000 + i)
+    E = int(rng.choice([1, 2, 3, 8, 12, 64, 96, 256, 512]))
+    R = int(rng.choice([r for r in (1, 2, 3, 4, 8, 16, 32, 64) if E % r == 0]))
+    K = int(rng.integers(1, 17))
+    T = int(rng.choice([0, 1, 2, 7, 63, 64, 65, 128, 200, 384, 512]))
+    while T * K > 3072 or T * R > 16384:
+        T //= 2
+    H = 32 * int(rng.choice([1, 3, 32, 100, 224, 256]))
+    a = int(rng.choice([1, 2, 7, 32, 128]))
+    dup = bool(rng.random() < 0.3)
+    drop = float(rng.choice([0.0, 0.0, 0.3, 1.0]))
+    bad_ids = bool(rng.random() < 0.15)
+    extra_cap = int(rng.choice([0, 0, 5]))
+    weights = bool(rng.random() < 0.7)
+    return rng, T, H, E, R, K, a, dup, drop, bad_ids, extra_cap, weights
+
+
+def _routing(rng, T, K, E, dup, drop, bad_ids):
+    if dup or K > E:
+        idx = rng.integers(0, E, size=(T, K)).astype(np.int64)
+    else:
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int64)
+    if drop > 0:
+        idx[rng.random((T, K)) < drop] = -1
+    if bad_ids and T * K > 0:
+        m = rng.random((T, K)) < 0.05
+        idx[m] = rng.choice([E, E + 3, -2])
+    wts = rng.random((T, K)).astype(np.float32)
+    return idx, wts
+
+
+def _run(T, H, E, R, K, a, idx, wts, extra_cap, weights, rng):
+    x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    ol = oracle.layout(idx, E, R, a, recv_capacity=oracle.recv_capacity_bound(T, K, E, a) + extra_cap)
+    cap = ol.recv_capacity
+    assert moe.moe_layout_and_dispatch_fits(T, H, K, R)
+    lay = moe.allocate_layout(T, K, E, R, a, cap, DEV)
+    rx = torch.full((cap, H), 0, dtype=torch.int16, device=DEV)
+    rx.fill_(SENTINEL)
+    rx = rx.view(torch.bfloat16)
+    rw = torch.full((cap,), -3.0, dtype=torch.float32, device=DEV)
+    w_dev = torch.from_numpy(wts).to(DEV) if weights else None
+    moe.moe_layout_and_dispatch(torch.from_numpy(idx).to(DEV), bf16_dev(x_bits), E, R, a, w_dev, cap,
+                                out=lay, recv_x=rx, recv_weights=rw)
+    assert_layout_equal(layout_to_host(lay), ol)
+    orx = np.full((cap, H), 0xFFFF, np.uint16)
+    orx, _, orw = oracle.dispatch(x_bits, ol.token_row, cap, wts if weights else None, 0, recv_x=orx,
+                                  with_weights=True)
+    np.testing.assert_array_equal(bf16_host_bits(rx), orx)
+    used = ol.recv_src >= 0
+    np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
+    assert (rw.cpu().numpy()[~used] == -3.0).all()
+    return lay, rx, rw, x_bits, cap
+
+
+@pytest.mark.parametrize("i", range(120), ids=[f"cfg{i}" for i in range(120)])
+def test_layout_and_dispatch_random(i):
+    rng, T, H, E, R, K, a, dup, drop, bad_ids, extra_cap, weights = _config(i)
+    print(f"[small cfg{i}] T={T} H={H} E={E} R={R} K={K} a={a} dup={dup} drop={drop} bad={bad_ids} "
+          f"extra_cap={extra_cap} weights={weights}", flush=True)
+    idx, wts = _routing(rng, T, K, E, dup, drop, bad_ids)
+    _run(T, H, E, R, K, a, idx, wts, extra_cap, weights, rng)
+
+
+@pytest.mark.parametrize("T,H,E,R,K", [(384, 64, 256, 8, 8),      # 3072 entries
+                                       (512, 32, 64, 32, 6),      # 512 tokens, 16384 cells
+                                       (128, 8192, 256, 8, 8),    # largest hidden size
+                                       (128, 7168, 256, 8, 8),    # the decode workload's shape
+                                       (3, 7168, 1, 1, 16)])      # one expert, every entry on it
+def test_layout_and_dispatch_limits(T, H, E, R, K):
+    print(f"[small limits] T={T} H={H} E={E} R={R} K={K}", flush=True)
+    rng = np.random.default_rng(T + H + K)
+    idx, wts = _routing(rng, T, K, E, dup=E < K, drop=0.1, bad_ids=False)
+    _run(T, H, E, R, K, 1, idx, wts, 0, True, rng)
+
+
+def test_layout_and_dispatch_equals_two_calls():
+    """The one-launch path and the two calls write identical outputs, and the
+    binding falls back to the two calls for a batch that does not fit."""
+    rng = np.random.default_rng(77)
+    for T, H in ((128, 7168), (600, 256)):
+        E, R, K, a = 256, 8, 4, 7
+        idx, wts = _routing(rng, T, K, E, dup=False, drop=0.1, bad_ids=False)
+        x = bf16_dev(W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+        d_idx, d_w = torch.from_numpy(idx).to(DEV), torch.from_numpy(wts).to(DEV)
+        lay1, rx1, rw1 = moe.moe_layout_and_dispatch(d_idx, x, E, R, a, d_w, with_weights=True)
+        lay2 = gpu_layout(idx, E, R, a)
+        rx2, _, rw2 = moe.moe_dispatch(x, lay2, d_w, 0, with_weights=True)
+        g1, g2 = layout_to_host(lay1), layout_to_host(lay2)
+        for k in g1:
+            np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
+        used = torch.from_numpy(g2["recv_src"] >= 0).to(DEV)
+        assert torch.equal(rx1.view(torch.int16)[used], rx2.view(torch.int16)[used])
+        assert torch.equal(rw1[used], rw2[used])
+        assert moe.moe_layout_and_dispatch_fits(T, H, K, R) == (T <= 512)
+    torch.cuda.synchronize()
