@@ -123,3 +123,48 @@ def test_layout_and_dispatch_equals_two_calls():
         assert torch.equal(rw1[used], rw2[used])
         assert moe.moe_layout_and_dispatch_fits(T, H, K, R) == (T <= 512)
     torch.cuda.synchronize()
+
+
+def test_layout_and_dispatch_graph_replays_match_eager():
+    """The one-launch call allocates nothing and never synchronises, so a
+    step (it, then a combine) can be captured in a HIP graph.  Replay it
+    several times, with eager work and synchronisations in between, against
+    the eager result."""
+    rng = np.random.default_rng(78)
+    T, H, K, E, R, a = 128, 1024, 8, 64, 8, 4
+    idx, wts = _routing(rng, T, K, E, dup=False, drop=0.05, bad_ids=False)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    x = bf16_dev(W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    w = torch.from_numpy(wts).to(DEV)
+    lay = moe.allocate_layout(T, K, E, R, a, device=DEV)
+    rx = torch.empty((lay.recv_capacity, H), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        moe.moe_layout_and_dispatch(idx_d, x, E, R, a, None, out=lay, recv_x=rx)
+        moe.moe_combine(rx, lay, w, out=out)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        used = lay.recv_src >= 0
+        return (lay.token_row.clone(), lay.recv_src.clone(), lay.expert_offsets.clone(),
+                lay.is_token_in_rank.clone(), rx.view(torch.int16)[used].clone(), out.view(torch.int16).clone())
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    ref = snapshot()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        for t_ in (lay.token_row, lay.recv_src, lay.expert_offsets, lay.is_token_in_rank, out):
+            t_.fill_(7)
+        rx.view(torch.int16).fill_(3)
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for r_, g_ in zip(ref, got):
+            assert torch.equal(r_, g_)
