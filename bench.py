@@ -39,7 +39,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 KERNEL_SOURCES = {
-    "dispatch": ["dispatch.hip", "device_common.h", "launch.h"],
+    "dispatch": ["dispatch.hip", "element_codecs.h", "device_common.h", "launch.h"],
     "combine": ["combine.hip", "device_common.h", "launch.h"],
     "layout": ["layout.hip", "device_common.h", "launch.h"],
 }
@@ -65,9 +65,9 @@ def parse():
                    help="time replays of one captured HIP graph of the step instead of eager launches "
                         "(stage times then come from an eager pass with events before it)")
     p.add_argument("--one-launch", action="store_true",
-                   help="lay out and dispatch with moe_layout_and_dispatch, one launch (bf16 "
-                        "workloads whose batch it takes); the layout stage's time is then that "
-                        "launch and the dispatch stage's is empty")
+                   help="lay out and dispatch with moe_layout_and_dispatch, one launch (bf16 or "
+                        "per-token workloads whose batch it takes); the layout stage's time is then "
+                        "that launch and the dispatch stage's is empty")
     p.add_argument("--no-check", action="store_true", help="skip the post-run sanity check")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run 3 torch copies of 256 MiB: a kernel of known traffic "
@@ -347,12 +347,14 @@ def main():
     timer = StageEvents(torch)
 
     if args.one_launch:
-        if quant != 0 or w.prequant or w.static_scale > 0 or not moe.moe_layout_and_dispatch_fits(T, H, K, R):
-            raise SystemExit(f"--one-launch takes unquantised batches of at most 512 tokens, 3072 "
-                             f"entries and hidden 8192; {w.name} is not one")
+        if (quant not in moe.ONE_LAUNCH_MODES or w.prequant or w.static_scale > 0
+                or not moe.moe_layout_and_dispatch_fits(T, H, K, R)):
+            raise SystemExit(f"--one-launch takes bf16 or per-token quantised batches of at most 512 "
+                             f"tokens, 3072 entries and hidden 8192; {w.name} is not one")
 
         def run_layout():
-            moe.moe_layout_and_dispatch(idx, x, E, R, a, None, out=lay, recv_x=rx)
+            moe.moe_layout_and_dispatch(idx, x, E, R, a, None, quant_mode=quant, out=lay, recv_x=rx,
+                                        recv_scales=rs)
 
         def run_dispatch():
             pass

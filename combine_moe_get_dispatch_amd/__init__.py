@@ -90,7 +90,7 @@ def declare_signatures(L: ctypes.CDLL) -> ctypes.CDLL:
     L.moe_combine_fused.restype = i32
     L.moe_layout_and_dispatch_fits.argtypes = [i32, i32, i32, i32]
     L.moe_layout_and_dispatch_fits.restype = i32
-    L.moe_layout_and_dispatch.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i64, P] + [P] * 8 + [P, P, P]
+    L.moe_layout_and_dispatch.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i64, P, i32] + [P] * 8 + [P, P, P, P]
     L.moe_layout_and_dispatch.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -351,25 +351,29 @@ def moe_layout_and_dispatch_fits(num_tokens: int, hidden: int, num_topk: int, nu
     return bool(lib().moe_layout_and_dispatch_fits(num_tokens, hidden, num_topk, num_ranks))
 
 
+ONE_LAUNCH_MODES = (QUANT_NONE, QUANT_INT8_PER_TOKEN, QUANT_FP8_E4M3_PER_TOKEN, QUANT_FP8_E5M2_PER_TOKEN)
+
+
 def moe_layout_and_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, num_experts: int, num_ranks: int,
                             expert_alignment: int = 1, topk_weights: Optional[torch.Tensor] = None,
-                            recv_capacity: Optional[int] = None, out: Optional[DispatchLayout] = None,
-                            recv_x: Optional[torch.Tensor] = None,
+                            recv_capacity: Optional[int] = None, quant_mode: int = QUANT_NONE,
+                            out: Optional[DispatchLayout] = None, recv_x: Optional[torch.Tensor] = None,
+                            recv_scales: Optional[torch.Tensor] = None,
                             recv_weights: Optional[torch.Tensor] = None, with_weights: bool = False):
-    """moe_get_dispatch_layout and an unquantised moe_dispatch, in one launch
-    when the batch is decode-sized (moe_layout_and_dispatch_fits), else as
-    the two calls; the results are the same either way.  Returns (layout,
-    recv_x, recv_weights)."""
+    """moe_get_dispatch_layout and moe_dispatch: in one launch when the batch
+    is decode-sized (moe_layout_and_dispatch_fits) and ``quant_mode`` is
+    bf16 or a per-token mode, else as the two calls; the results are the
+    same either way.  Returns (layout, recv_x, recv_scales, recv_weights)."""
     if topk_idx.dim() != 2 or x.dim() != 2 or x.shape[0] != topk_idx.shape[0]:
         raise ValueError("topk_idx must be [num_tokens, num_topk] and x [num_tokens, hidden]")
     T, K = topk_idx.shape
     H = x.shape[1]
-    if not moe_layout_and_dispatch_fits(T, H, K, num_ranks):
+    if quant_mode not in ONE_LAUNCH_MODES or not moe_layout_and_dispatch_fits(T, H, K, num_ranks):
         lay = moe_get_dispatch_layout(topk_idx, num_experts, num_ranks, expert_alignment, recv_capacity,
                                       out)
-        rx, _, rw = moe_dispatch(x, lay, topk_weights, QUANT_NONE, recv_x=recv_x,
-                                 recv_weights=recv_weights, with_weights=with_weights)
-        return lay, rx, rw
+        rx, rs, rw = moe_dispatch(x, lay, topk_weights, quant_mode, recv_x=recv_x, recv_scales=recv_scales,
+                                  recv_weights=recv_weights, with_weights=with_weights)
+        return lay, rx, rs, rw
     dev = topk_idx.device
     _check(topk_idx, "topk_idx", torch.int64)
     _check(x, "x", torch.bfloat16, device=dev)
@@ -383,18 +387,23 @@ def moe_layout_and_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, num_experts
     _check_layout(out, dev)
     cap = out.recv_capacity
     if recv_x is None:
-        recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
-    _check(recv_x, "recv_x", torch.bfloat16, (cap, H), dev)
+        recv_x = torch.empty((cap, H), dtype=_RECV_DTYPE[quant_mode], device=dev)
+    _check(recv_x, "recv_x", _RECV_DTYPE[quant_mode], (cap, H), dev)
+    if quant_mode != QUANT_NONE:
+        if recv_scales is None:
+            recv_scales = torch.empty(cap, dtype=torch.float32, device=dev)
+        _check(recv_scales, "recv_scales", torch.float32, (cap,), dev)
     if recv_weights is None and with_weights:
         recv_weights = torch.empty(cap, dtype=torch.float32, device=dev)
     if recv_weights is not None:
         _check(recv_weights, "recv_weights", torch.float32, (cap,), dev)
     rc = lib().moe_layout_and_dispatch(
         _ptr(topk_idx), _ptr(x), T, H, K, num_experts, num_ranks, expert_alignment, cap,
-        _ptr(topk_weights), *out._layout_ptrs[:8], _ptr(recv_x), _ptr(recv_weights), _stream(dev))
+        _ptr(topk_weights), quant_mode, *out._layout_ptrs[:8], _ptr(recv_x),
+        _ptr(recv_scales if quant_mode != QUANT_NONE else None), _ptr(recv_weights), _stream(dev))
     if rc != MOE_OK:
         raise MoeError("moe_layout_and_dispatch", rc)
-    return out, recv_x, recv_weights
+    return out, recv_x, recv_scales if quant_mode != QUANT_NONE else None, recv_weights
 
 
 def moe_dispatch_static(x: torch.Tensor, layout: DispatchLayout, scales: torch.Tensor,

@@ -131,12 +131,12 @@ int moe_layout_and_dispatch_fits(int num_tokens, int hidden, int num_topk, int n
 
 int moe_layout_and_dispatch(const int64_t *topk_idx, const void *x, int num_tokens, int hidden,
                             int num_topk, int num_experts, int num_ranks, int expert_alignment,
-                            int64_t recv_capacity, const float *topk_weights,
+                            int64_t recv_capacity, const float *topk_weights, int quant_mode,
                             int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                             int32_t *is_token_in_rank, int32_t *num_recv_tokens_per_expert,
                             int32_t *expert_offsets, int32_t *token_row, int32_t *recv_src,
-                            int32_t *error_flag, void *recv_x, float *recv_weights,
-                            hipStream_t stream)
+                            int32_t *error_flag, void *recv_x, float *recv_scales,
+                            float *recv_weights, hipStream_t stream)
 {
     const int T = num_tokens, H = hidden, K = num_topk, E = num_experts, R = num_ranks,
               a = expert_alignment;
@@ -147,6 +147,13 @@ int moe_layout_and_dispatch(const int64_t *topk_idx, const void *x, int num_toke
     if (rc != MOE_OK)
         return rc;
     if (!small_batch_fits(T, H, K, R))
+        return MOE_ERR_INVALID_ARG;
+    const bool per_token = quant_mode == MOE_QUANT_INT8_PER_TOKEN ||
+                           quant_mode == MOE_QUANT_FP8_E4M3_PER_TOKEN ||
+                           quant_mode == MOE_QUANT_FP8_E5M2_PER_TOKEN;
+    if (quant_mode != MOE_QUANT_NONE && !per_token)
+        return MOE_ERR_INVALID_ARG;
+    if (T > 0 && per_token && !recv_scales)
         return MOE_ERR_INVALID_ARG;
     if (!num_tokens_per_rank || !num_tokens_per_expert || !num_recv_tokens_per_expert ||
         !expert_offsets || !error_flag)
@@ -174,8 +181,8 @@ int moe_layout_and_dispatch(const int64_t *topk_idx, const void *x, int num_toke
     args.recv_src = recv_src;
     args.error_flag = error_flag;
     args.workspace = nullptr;
-    return launch_layout_dispatch_small(args, x, H, topk_weights, recv_x, recv_weights, stream) ==
-                   hipSuccess
+    return launch_layout_dispatch_small(args, x, H, topk_weights, quant_mode, recv_x, recv_scales,
+                                        recv_weights, stream) == hipSuccess
                ? MOE_OK
                : MOE_ERR_HIP;
 }

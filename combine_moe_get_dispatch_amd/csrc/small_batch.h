@@ -1,5 +1,5 @@
-// small_batch.h -- limits and launcher of the one-launch layout + bf16
-// dispatch for decode-sized batches (small_batch.hip).
+// small_batch.h -- limits and launcher of the one-launch layout + dispatch
+// for decode-sized batches (small_batch.hip).
 #pragma once
 
 #include "launch.h"
@@ -22,9 +22,11 @@ inline bool small_batch_fits(int T, int H, int K, int R)
 }
 
 // Layout outputs as in launch_layout (no workspace), plus recv_x [cap, H]
-// bf16 and the optional recv_weights [cap].
+// (bf16, or int8 / FP8 codes), recv_scales fp32 [cap] for the per-token
+// modes and the optional recv_weights [cap].  quant_mode: MOE_QUANT_NONE or
+// one of the per-token modes.
 hipError_t launch_layout_dispatch_small(const LayoutArgs &args, const void *x, int H,
-                                        const float *topk_weights, void *recv_x,
-                                        float *recv_weights, hipStream_t stream);
+                                        const float *topk_weights, int quant_mode, void *recv_x,
+                                        float *recv_scales, float *recv_weights, hipStream_t stream);
 
 } // namespace moe

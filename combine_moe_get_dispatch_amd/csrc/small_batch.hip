@@ -1,14 +1,15 @@
-// small_batch.hip -- layout and bf16 dispatch of a decode-sized batch in one
-// launch.
+// small_batch.hip -- layout and dispatch (bf16, or per-token int8 / FP8) of
+// a decode-sized batch in one launch.
 //
 // What is computed: exactly what moe_get_dispatch_layout followed by
-// moe_dispatch (no quantisation) compute (Normal Mode API page, dispatch
-// Parameters / Return Values; EPBatchManager page, ep_dispatch(); CANN
-// aclnnMoeDistributeDispatchV2 page, Constraint 1, deterministic):
+// moe_dispatch (unquantised, or with per-token quantisation) compute (Normal
+// Mode API page, dispatch Parameters / Return Values; EPBatchManager page,
+// ep_dispatch(); CANN aclnnMoeDistributeDispatchV2 page, Formula Case 3 and
+// Constraint 1, deterministic):
 //   c[e]        = number of entries with topk_idx == e
 //   off[e]      = sum over e' < e of ceil(c[e'] / a) * a
 //   row(t, k)   = off[e] + #{ j < tK : idx_j == e } + #{ k' < k : idx[t, k'] == e }
-//   recv[row(t, k)] = x[t]
+//   recv[row(t, k)] = x[t], or its per-token codes with their scale
 //
 // Design (gfx950): at decode-sized batches the two-call form is bound by
 // fixed costs -- two launches, the layout's store of token_row and the
@@ -27,6 +28,7 @@
 // The redundant layout work grows as T * T*K, so the path is limited to
 // small batches (kSmallMaxTokens tokens, kSmallMaxEntries entries).
 #include "device_common.h"
+#include "element_codecs.h"
 #include "small_batch.h"
 
 #include "../../include/moe_dispatch_combine.h"
@@ -48,13 +50,19 @@ __device__ __forceinline__ int small_div(int n, int d)
     return q;
 }
 
+// QUANT: per-token dynamic quantisation to D (CANN page, Formula Case 3, as
+// dispatch_pertoken_kernel computes it): the row maximum from per-wave
+// maxima, dynamicScales = dstTypeMax / max in IEEE fp32, codes from one fp32
+// product each, scale 1 / dynamicScales; codes 0 and scale 0 when
+// dynamicScales is not finite.  Otherwise the bf16 row is copied.
+template <bool QUANT, Dst D>
 __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
     const int64_t *__restrict__ topk_idx, const u32x4 *__restrict__ x, int T, int K, int E, int R,
     int L, int a, int nbits, int nvec, int64_t cap, const float *__restrict__ topk_weights,
     int32_t *__restrict__ itr, int32_t *__restrict__ ntpr, int32_t *__restrict__ ntpe,
     int32_t *__restrict__ nrtpe, int32_t *__restrict__ off, int32_t *__restrict__ token_row,
-    int32_t *__restrict__ recv_src, int32_t *__restrict__ error_flag, u32x4 *__restrict__ recv,
-    float *__restrict__ recv_weights)
+    int32_t *__restrict__ recv_src, int32_t *__restrict__ error_flag, void *__restrict__ recv,
+    float *__restrict__ recv_scales, float *__restrict__ recv_weights)
 {
     __shared__ int s_tot[MOE_MAX_EXPERTS];
     __shared__ int s_off[MOE_MAX_EXPERTS + 1];
@@ -64,9 +72,11 @@ __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
     __shared__ int s_before[MOE_MAX_TOPK]; // entries before this token holding s_my[k]
     __shared__ int s_row[MOE_MAX_TOPK];
     __shared__ int s_bad;
+    __shared__ float s_wmax[kSmallThreads / kWave];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const int b = blockIdx.x;
     const int nblocks = gridDim.x;
     const bool has_token = b < T; // false only when T == 0 (one workgroup then)
@@ -135,6 +145,17 @@ __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
     }
     if (bad)
         atomicOr(&s_bad, 1);
+    if (QUANT) { // this wave's share of the row maximum (lanes past the row hold zeros)
+        float m = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            m = fmaxf(m, fabsf(bf16_lo(v[c])));
+            m = fmaxf(m, fabsf(bf16_hi(v[c])));
+        }
+        m = wave_max(m);
+        if (lane == 0)
+            s_wmax[wave] = m;
+    }
     __syncthreads();
 
     // aligned counts and their exclusive prefix sum ("/" is integer
@@ -182,6 +203,28 @@ __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
     }
     __syncthreads();
 
+    // the row's codes and scale
+    float scale = 0.0f;
+    u32x2 q = u32x2{0u, 0u};
+    if (QUANT) {
+        float m = s_wmax[0];
+        for (int w = 1; w < kSmallThreads / kWave; ++w)
+            m = fmaxf(m, s_wmax[w]);
+        const float ds = DstTraits<D>::kMax / m; // IEEE division (correctly rounded fp32 divide)
+        const bool degenerate = !(ds <= 3.402823466e38f);
+        scale = 1.0f / ds;
+        uint32_t wd[2] = {0u, 0u};
+        if (!degenerate) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t lo = DstTraits<D>::code(bf16_lo(v[c]) * ds, sign_lo(v[c]));
+                const uint32_t hi = DstTraits<D>::code(bf16_hi(v[c]) * ds, sign_hi(v[c]));
+                wd[c >> 1] |= (lo | (hi << 8)) << (16 * (c & 1));
+            }
+        }
+        q = u32x2{wd[0], wd[1]};
+    }
+
     // this token's rows: expert offset + earlier entries of the expert
     // (before the token, then among its own earlier k)
     if (has_token && tid < K) {
@@ -193,6 +236,8 @@ __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
                 dup += s_my[k] == e ? 1 : 0;
             row = s_off[e] + s_before[tid] + dup;
             recv_src[row] = t * K + tid;
+            if (QUANT)
+                recv_scales[row] = scale;
             if (recv_weights)
                 recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + tid] : 1.0f;
         }
@@ -224,12 +269,16 @@ __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
         recv_src[row] = -1;
     __syncthreads();
 
-    // the token to its rows
+    // the token (or its codes) to its rows
     if (has_token && tid < nvec) {
         for (int k = 0; k < K; ++k) {
             const int row = s_row[k];
-            if (row >= 0 && row < cap)
-                __builtin_nontemporal_store(v, recv + (int64_t)row * nvec + tid);
+            if (row < 0 || row >= cap)
+                continue;
+            if (QUANT)
+                __builtin_nontemporal_store(q, (u32x2 *)recv + (int64_t)row * nvec + tid);
+            else
+                __builtin_nontemporal_store(v, (u32x4 *)recv + (int64_t)row * nvec + tid);
         }
     }
 }
@@ -243,15 +292,29 @@ static int small_key_bits(int E)
 }
 
 hipError_t launch_layout_dispatch_small(const LayoutArgs &A, const void *x, int H,
-                                        const float *topk_weights, void *recv_x,
-                                        float *recv_weights, hipStream_t stream)
+                                        const float *topk_weights, int quant_mode, void *recv_x,
+                                        float *recv_scales, float *recv_weights, hipStream_t stream)
 {
     const int L = A.E / A.R;
-    return launch_kernel(layout_dispatch_small_kernel, dim3(A.T > 0 ? A.T : 1), dim3(kSmallThreads), 0,
-                         stream, A.topk_idx, (const u32x4 *)x, A.T, A.K, A.E, A.R, L, A.a,
-                         small_key_bits(A.E), H / 8, A.cap, topk_weights, A.itr, A.ntpr, A.ntpe,
-                         A.nrtpe, A.off, A.token_row, A.recv_src, A.error_flag, (u32x4 *)recv_x,
-                         recv_weights);
+    auto go = [&](auto kernel) {
+        return launch_kernel(kernel, dim3(A.T > 0 ? A.T : 1), dim3(kSmallThreads), 0, stream,
+                             A.topk_idx, (const u32x4 *)x, A.T, A.K, A.E, A.R, L, A.a,
+                             small_key_bits(A.E), H / 8, A.cap, topk_weights, A.itr, A.ntpr, A.ntpe,
+                             A.nrtpe, A.off, A.token_row, A.recv_src, A.error_flag, recv_x,
+                             recv_scales, recv_weights);
+    };
+    switch (quant_mode) {
+    case MOE_QUANT_NONE:
+        return go(layout_dispatch_small_kernel<false, Dst::Int8>);
+    case MOE_QUANT_INT8_PER_TOKEN:
+        return go(layout_dispatch_small_kernel<true, Dst::Int8>);
+    case MOE_QUANT_FP8_E4M3_PER_TOKEN:
+        return go(layout_dispatch_small_kernel<true, Dst::E4M3>);
+    case MOE_QUANT_FP8_E5M2_PER_TOKEN:
+        return go(layout_dispatch_small_kernel<true, Dst::E5M2>);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 } // namespace moe

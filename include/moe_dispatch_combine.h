@@ -15,9 +15,9 @@
  *   moe_combine                top-k weighted sum of every token's expert rows
  *   moe_combine_fused          the same plus shared-expert and residual adds
  *                              and an optional RMS normalisation
- *   moe_layout_and_dispatch    moe_get_dispatch_layout and an unquantised
- *                              moe_dispatch in one launch, for decode-sized
- *                              batches (moe_layout_and_dispatch_fits)
+ *   moe_layout_and_dispatch    moe_get_dispatch_layout and moe_dispatch (bf16
+ *                              or per-token int8 / FP8) in one launch, for
+ *                              decode-sized batches (moe_layout_and_dispatch_fits)
  * plus the size queries moe_recv_capacity_bound and moe_layout_workspace_bytes.
  *
  * Sources, by page title and section:
@@ -304,36 +304,41 @@ int moe_combine_fused(const void *expert_out, int64_t recv_capacity, int num_tok
 int moe_layout_and_dispatch_fits(int num_tokens, int hidden, int num_topk, int num_ranks);
 
 /*
- * moe_get_dispatch_layout followed by moe_dispatch with quant_mode
- * MOE_QUANT_NONE, in one launch, for decode-sized batches (the same pages
- * and definitions as those two calls).  At such sizes the two-call form is
- * bound by fixed costs: two launches, and the layout's store of token_row
- * that dispatch reads back.  Here one workgroup per token derives the whole
- * small layout itself (every workgroup computes the same expert totals and
- * offsets from the same ids, so none waits for another) and copies its
- * token to its rows.
+ * moe_get_dispatch_layout followed by moe_dispatch, in one launch, for
+ * decode-sized batches (the same pages and definitions as those two calls).
+ * quant_mode: MOE_QUANT_NONE or one of the per-token modes
+ * (MOE_QUANT_INT8_PER_TOKEN, MOE_QUANT_FP8_E4M3_PER_TOKEN,
+ * MOE_QUANT_FP8_E5M2_PER_TOKEN).  At such sizes the two-call form is bound by
+ * fixed costs: two launches, and the layout's store of token_row that
+ * dispatch reads back.  Here one workgroup per token derives the whole small
+ * layout itself (every workgroup computes the same expert totals and offsets
+ * from the same ids, so none waits for another) and copies or quantises its
+ * token into its rows.
  *
  * Every output equals, bit for bit, what moe_get_dispatch_layout and
- * moe_dispatch (bf16, same topk_weights and recv_weights) write: the layout
- * arrays, recv_src with -1 on padding and unused rows, the bf16 rows, the
- * row weights.  Rows holding no entry are not written.
+ * moe_dispatch (same quant_mode, topk_weights and recv_weights) write: the
+ * layout arrays, recv_src with -1 on padding and unused rows, the rows or
+ * codes, the per-row scales, the row weights.  Rows holding no entry are not
+ * written.
  * Inputs (device): topk_idx int64 [T, K]; x bf16 [T, H], 16-byte aligned;
  *   topk_weights fp32 [T, K] or NULL (only read for recv_weights).
  * Outputs (device): as moe_get_dispatch_layout (no workspace is needed);
- *   recv_x bf16 [recv_capacity, H], 16-byte aligned; recv_weights fp32
- *   [recv_capacity] or NULL.
+ *   recv_x [recv_capacity, H] of bf16, int8 or FP8 codes, 16-byte aligned;
+ *   recv_scales fp32 [recv_capacity] for the per-token modes (else unused);
+ *   recv_weights fp32 [recv_capacity] or NULL.
  * Errors: MOE_ERR_INVALID_ARG (including sizes that
- *   moe_layout_and_dispatch_fits rejects), MOE_ERR_CAPACITY, MOE_ERR_HIP;
- *   out-of-range expert ids set bit 0 of *error_flag, as in the layout call.
+ *   moe_layout_and_dispatch_fits rejects and other quant modes),
+ *   MOE_ERR_CAPACITY, MOE_ERR_HIP; out-of-range expert ids set bit 0 of
+ *   *error_flag, as in the layout call.
  */
 int moe_layout_and_dispatch(const int64_t *topk_idx, const void *x, int num_tokens, int hidden,
                             int num_topk, int num_experts, int num_ranks, int expert_alignment,
-                            int64_t recv_capacity, const float *topk_weights,
+                            int64_t recv_capacity, const float *topk_weights, int quant_mode,
                             int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                             int32_t *is_token_in_rank, int32_t *num_recv_tokens_per_expert,
                             int32_t *expert_offsets, int32_t *token_row, int32_t *recv_src,
-                            int32_t *error_flag, void *recv_x, float *recv_weights,
-                            hipStream_t stream);
+                            int32_t *error_flag, void *recv_x, float *recv_scales,
+                            float *recv_weights, hipStream_t stream);
 
 /* Static text for a status code. */
 const char *moe_status_string(int status);

@@ -210,10 +210,10 @@ def test_layout_and_dispatch_limits_and_rules(L, orc):
     assert L.moe_layout_and_dispatch_fits(512, 1024, 2, 64) == 0     # 32768 token x rank cells
     assert L.moe_layout_and_dispatch_fits(128, 8224, 8, 8) == 0      # hidden
 
-    def call(T=128, H=7168, K=8, E=256, R=8, a=1, cap=None, idx=BAD, x=BAD, rx=BAD, outs=None):
+    def call(T=128, H=7168, K=8, E=256, R=8, a=1, cap=None, idx=BAD, x=BAD, rx=BAD, outs=None, q=0, rs=BAD):
         cap = orc.recv_capacity_bound(T, K, E, a) if cap is None else cap
         outs = [BAD] * 8 if outs is None else outs
-        return L.moe_layout_and_dispatch(idx, x, T, H, K, E, R, a, cap, None, *outs, rx, None, None)
+        return L.moe_layout_and_dispatch(idx, x, T, H, K, E, R, a, cap, None, q, *outs, rx, rs, None, None)
 
     assert call(T=600, K=1) == -1                       # beyond the one-launch limits
     assert call(H=8224) == -1
@@ -227,3 +227,6 @@ def test_layout_and_dispatch_limits_and_rules(L, orc):
     assert call(rx=ctypes.c_void_p(0x1004)) == -1
     assert call(outs=[BAD] * 6 + [None, BAD]) == -1     # recv_src missing
     assert call(outs=[None] + [BAD] * 7) == -1          # num_tokens_per_rank missing
+    for q in (4, 0x13, 0x24, 0x14, 1):                  # only bf16 and the per-token modes
+        assert call(q=q) == -1
+    assert call(q=2, rs=None) == -1                     # per-token scales missing
