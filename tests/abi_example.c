@@ -8,6 +8,9 @@
  *   - with the receive buffer as the expert output (identity experts) and no
  *     weights, out[t] = bf16(c_t * x[t]) exactly, c_t = valid entries of t
  *     (c_t <= 8 copies of one bf16 value add exactly in fp32).
+ * Then the first 96 tokens go through moe_layout_and_dispatch (one launch, per-token
+ * FP8 e4m3fn codes) and through the two calls with the same mode: every layout
+ * array, code row and scale must be identical.
  * Prints "abi example: ok" and exits 0 on success.
  */
 #include <stdint.h>
@@ -58,6 +61,43 @@ static uint16_t f32_to_bf16_rne(float f)
     memcpy(&u, &f, 4);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+/* layout and receive buffers of one batch, receive rows and scales zeroed */
+typedef struct {
+    int32_t *ntpr, *ntpe, *itr, *nrtpe, *off, *row, *src, *flag;
+    uint8_t *recv;
+    float *scales;
+} Bufs;
+
+static int alloc_bufs(Bufs *b, int T, int H, int K, int E, int R, int64_t cap)
+{
+    HIP_CHECK(hipMalloc((void **)&b->ntpr, sizeof(int32_t) * R));
+    HIP_CHECK(hipMalloc((void **)&b->ntpe, sizeof(int32_t) * E));
+    HIP_CHECK(hipMalloc((void **)&b->itr, sizeof(int32_t) * T * R));
+    HIP_CHECK(hipMalloc((void **)&b->nrtpe, sizeof(int32_t) * E));
+    HIP_CHECK(hipMalloc((void **)&b->off, sizeof(int32_t) * (E + 1)));
+    HIP_CHECK(hipMalloc((void **)&b->row, sizeof(int32_t) * T * K));
+    HIP_CHECK(hipMalloc((void **)&b->src, sizeof(int32_t) * cap));
+    HIP_CHECK(hipMalloc((void **)&b->flag, sizeof(int32_t)));
+    HIP_CHECK(hipMalloc((void **)&b->recv, (size_t)cap * H));
+    HIP_CHECK(hipMalloc((void **)&b->scales, sizeof(float) * cap));
+    HIP_CHECK(hipMemset(b->recv, 0, (size_t)cap * H));
+    HIP_CHECK(hipMemset(b->scales, 0, sizeof(float) * cap));
+    return 0;
+}
+
+/* 1 if the n bytes at device pointers p and q differ */
+static int differ(const void *p, const void *q, size_t n)
+{
+    void *a = malloc(n), *b = malloc(n);
+    int d = 1;
+    if (a && b && hipMemcpy(a, p, n, hipMemcpyDeviceToHost) == hipSuccess &&
+        hipMemcpy(b, q, n, hipMemcpyDeviceToHost) == hipSuccess)
+        d = memcmp(a, b, n) != 0;
+    free(a);
+    free(b);
+    return d;
 }
 
 int main(void)
@@ -149,6 +189,35 @@ int main(void)
     }
     if (bad) {
         fprintf(stderr, "abi example: mismatch\n");
+        return 1;
+    }
+
+    /* the first T1 tokens: one launch against the two calls, per-token FP8 */
+    const int T1 = 96, q = MOE_QUANT_FP8_E4M3_PER_TOKEN;
+    const int64_t cap1 = moe_recv_capacity_bound(T1, K, E, a);
+    const size_t ws1 = moe_layout_workspace_bytes(T1, K, E, R);
+    void *d_ws1 = NULL;
+    Bufs A, B;
+    if (!moe_layout_and_dispatch_fits(T1, H, K, R) || alloc_bufs(&A, T1, H, K, E, R, cap1) ||
+        alloc_bufs(&B, T1, H, K, E, R, cap1)) {
+        fprintf(stderr, "abi example: one-launch setup failed\n");
+        return 1;
+    }
+    if (ws1 > 0)
+        HIP_CHECK(hipMalloc(&d_ws1, ws1));
+    MOE_CHECK(moe_layout_and_dispatch(d_idx, d_x, T1, H, K, E, R, a, cap1, NULL, q, A.ntpr, A.ntpe, A.itr,
+                                      A.nrtpe, A.off, A.row, A.src, A.flag, A.recv, A.scales, NULL, st));
+    MOE_CHECK(moe_get_dispatch_layout(d_idx, T1, K, E, R, a, cap1, B.ntpr, B.ntpe, B.itr, B.nrtpe, B.off,
+                                      B.row, B.src, B.flag, d_ws1, ws1, st));
+    MOE_CHECK(moe_dispatch(d_x, T1, H, K, B.row, NULL, cap1, q, B.recv, B.scales, NULL, st));
+    HIP_CHECK(hipStreamSynchronize(st));
+    bad = differ(A.ntpr, B.ntpr, sizeof(int32_t) * R) || differ(A.ntpe, B.ntpe, sizeof(int32_t) * E) ||
+          differ(A.itr, B.itr, sizeof(int32_t) * T1 * R) || differ(A.nrtpe, B.nrtpe, sizeof(int32_t) * E) ||
+          differ(A.off, B.off, sizeof(int32_t) * (E + 1)) || differ(A.row, B.row, sizeof(int32_t) * T1 * K) ||
+          differ(A.src, B.src, sizeof(int32_t) * cap1) || differ(A.flag, B.flag, sizeof(int32_t)) ||
+          differ(A.recv, B.recv, (size_t)cap1 * H) || differ(A.scales, B.scales, sizeof(float) * cap1);
+    if (bad) {
+        fprintf(stderr, "abi example: one launch and two calls differ\n");
         return 1;
     }
     printf("abi example: ok (T=%d H=%d K=%d E=%d, %lld receive rows, %zu workspace bytes)\n", T, H, K, E,
