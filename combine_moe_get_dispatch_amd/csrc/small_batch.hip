@@ -21,7 +21,9 @@
 // for each of its own K entries, the entries before its token that hold the
 // same expert.  It then writes its token's layout outputs and copies the
 // token, whose 16-byte vectors were loaded at the start, to its rows with
-// nontemporal stores.  Workgroups never wait for one another: all of them
+// nontemporal stores (or, for the per-token modes, reduces the row maximum
+// from per-wave maxima taken before the second barrier and stores the codes
+// and the scale).  Workgroups never wait for one another: all of them
 // compute identical totals and offsets from the same ids.  Workgroup 0 also
 // writes the per-expert and per-rank outputs and every is_token_in_rank row;
 // the padding and unused rows of recv_src are spread over all workgroups.
