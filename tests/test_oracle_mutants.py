@@ -103,7 +103,17 @@ MUTANTS = [
     ("FP8 destination formats swapped", CODECS,
      "const int fmt = (quant_mode >> 4) == 2 ? FMT_E5M2 : FMT_E4M3FN;",
      "const int fmt = (quant_mode >> 4) == 1 ? FMT_E5M2 : FMT_E4M3FN;"),
+    # argument rules
+    ("top-k limit 17 in the layout rules", LAYOUT,
+     "if (T < 0 || K < 1 || K > 16 || E < 1 || E > 512 || R < 1 || R > E || E % R != 0 ||",
+     "if (T < 0 || K < 1 || K > 17 || E < 1 || E > 512 || R < 1 || R > E || E % R != 0 ||"),
+    ("hidden sizes in multiples of 16", LAYOUT,
+     "H % 32 != 0 || cap < 0 ||", "H % 16 != 0 || cap < 0 ||"),
     # combine
+    ("combine product rounded to fp32", COMBINE,
+     "o[h] += w * (double)bf16_to_f32(yr[h]);", "o[h] += (double)((float)w * bf16_to_f32(yr[h]));"),
+    ("RMS mean over H - 1 elements", COMBINE,
+     "const double rms = sqrt(ss / H + eps);", "const double rms = sqrt(ss / (H - 1) + eps);"),
     ("combine weight index transposed", COMBINE,
      "double w = topk_weights ? (double)topk_weights[(int64_t)t * K + k] : 1.0;",
      "double w = topk_weights ? (double)topk_weights[(int64_t)k * T + t] : 1.0;"),
