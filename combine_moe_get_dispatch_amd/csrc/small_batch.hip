@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
         int sum = 0;
         for (int c = 0; c < per; ++c)
             if (e0 + c < E)
-                sum += ((s_tot[e0 + c] + a - 1) / a) * a;
+                sum += a == 1 ? s_tot[e0 + c] : ((s_tot[e0 + c] + a - 1) / a) * a;
         int incl = sum;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
         for (int c = 0; c < per; ++c)
             if (e0 + c < E) {
                 s_off[e0 + c] = run;
-                run += ((s_tot[e0 + c] + a - 1) / a) * a;
+                run += a == 1 ? s_tot[e0 + c] : ((s_tot[e0 + c] + a - 1) / a) * a;
             }
         if (lane == kWave - 1)
             s_off[E] = incl;
@@ -237,13 +237,7 @@ __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
             for (int k = 0; k < tid; ++k)
                 dup += s_my[k] == e ? 1 : 0;
             row = s_off[e] + s_before[tid] + dup;
-            recv_src[row] = t * K + tid;
-            if (QUANT)
-                recv_scales[row] = scale;
-            if (recv_weights)
-                recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + tid] : 1.0f;
         }
-        token_row[(int64_t)t * K + tid] = row;
         s_row[tid] = row;
     }
     if (first) {
@@ -270,6 +264,20 @@ __global__ __launch_bounds__(kSmallThreads) void layout_dispatch_small_kernel(
          row += (int64_t)nblocks * kSmallThreads)
         recv_src[row] = -1;
     __syncthreads();
+
+    // this token's layout entries, row weights and scales (stored after the
+    // barrier, so that no wave waits for them before the copy)
+    if (has_token && tid < K) {
+        const int row = s_row[tid];
+        token_row[(int64_t)t * K + tid] = row;
+        if (row >= 0) {
+            recv_src[row] = t * K + tid;
+            if (QUANT)
+                recv_scales[row] = scale;
+            if (recv_weights)
+                recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + tid] : 1.0f;
+        }
+    }
 
     // the token (or its codes) to its rows
     if (has_token && tid < nvec) {
