@@ -230,3 +230,28 @@ def test_layout_and_dispatch_limits_and_rules(L, orc):
     for q in (4, 0x13, 0x24, 0x14, 1):                  # only bf16 and the per-token modes
         assert call(q=q) == -1
     assert call(q=2, rs=None) == -1                     # per-token scales missing
+
+
+def test_missing_library_raises_and_nothing_falls_back(tmp_path):
+    """With the HIP library absent the binding raises on first use: there is
+    no CPU path to fall back on.  Run in a fresh interpreter whose binding
+    looks for the library at a path that does not exist."""
+    code = f"""
+import torch
+import combine_moe_get_dispatch_amd as m
+m.LIB_PATH = {str(tmp_path / 'absent.so')!r}
+m._lib = None
+for f in (m.lib,
+          lambda: m.moe_get_dispatch_layout(torch.zeros((4, 2), dtype=torch.int64), 4, 2),
+          lambda: m.moe_recv_capacity_bound(4, 2, 4, 1)):
+    try:
+        f()
+    except (RuntimeError, ValueError) as e:
+        print(type(e).__name__, str(e)[:60])
+    else:
+        raise SystemExit("call succeeded without the library")
+"""
+    out = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stdout + out.stderr
+    lines = out.stdout.strip().splitlines()
+    assert len(lines) == 3 and lines[0].startswith("RuntimeError") and "missing" in lines[0]
