@@ -454,6 +454,10 @@ def test_combine_fused_parity(variant):
     norm = "norm" in variant
     gamma = W.f32_to_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32)) if norm else None
     eps = 1e-5
+    _fused_against_oracle(y, lay, ol, wts, sh, res, gamma, eps, norm, K)
+
+
+def _fused_against_oracle(y, lay, ol, wts, sh, res, gamma, eps, norm, K):
     dv = lambda a: None if a is None else bf16_dev(a)
     out, out_norm = moe.moe_combine_fused(bf16_dev(y), lay, torch.from_numpy(wts).to(DEV), dv(sh),
                                           dv(res), dv(gamma), eps, with_norm=norm)
@@ -471,6 +475,34 @@ def test_combine_fused_parity(variant):
         assert (np.abs(gn - rn) <= bound).all(), float(np.max(np.abs(gn - rn) - bound))
     else:
         assert out_norm is None
+    return g, (gn if norm else None)
+
+
+@pytest.mark.parametrize("variant", ["shared_residual_norm", "norm_only"])
+@pytest.mark.parametrize("H", [32, 96, 2080])
+def test_combine_fused_edges(H, variant):
+    """Rows narrower than one wave (H = 32: four lanes of 8 elements; 96: 12)
+    and a ragged last wave (2080: 260 lanes), with tokens 0-9 having every
+    entry dropped: their sum is empty, so the output is shared + residual, or
+    an all-zero row whose normalised form is zero as well."""
+    rng = np.random.default_rng(H + len(variant))
+    T, K, E = 200, 4, 16
+    idx, _ = _routing(rng, T, K, E, drop=0.1)
+    idx[:10] = -1
+    wts = rng.standard_normal((T, K)).astype(np.float32)
+    ol = oracle.layout(idx, E, 4, 1)
+    lay = gpu_layout(idx, E, 4, 1)
+    y = W.random_bf16_rows(max(ol.recv_capacity, 1), H, 21)[:ol.recv_capacity]
+    sh = W.random_bf16_rows(T, H, 22) if "shared" in variant else None
+    res = W.random_bf16_rows(T, H, 23, sigma=2.0) if "residual" in variant else None
+    gamma = W.f32_to_bf16_bits(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    print(f"[fused edges] H={H} {variant}", flush=True)
+    g, gn = _fused_against_oracle(y, lay, ol, wts, sh, res, gamma, 1e-5, True, K)
+    if variant == "norm_only":
+        assert (g[:10] == 0).all() and (gn[:10] == 0).all()
+    else:
+        want = (W.bf16_bits_to_f32(sh[:10]).astype(np.float64) + W.bf16_bits_to_f32(res[:10]))
+        assert (np.abs(g[:10] - want) <= 2.0 ** -8 * np.abs(want) + 2.0 ** -20 * np.abs(want).max()).all()
 
 
 @pytest.mark.parametrize("quant", [4, 0x24], ids=["mxfp8_e4m3", "mxfp8_e5m2"])
