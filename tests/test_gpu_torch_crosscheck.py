@@ -1,0 +1,61 @@
+"""Per-token dynamic quantisation against plain torch arithmetic on the GPU,
+a check that shares nothing with the oracle.
+
+CANN page "aclnnMoeDistributeDispatchV2", Formula Case 3: the row's scale is
+the destination maximum (127 for int8, 448 for e4m3fn, 57344 for e5m2)
+divided by the row's largest magnitude, each code is the cast of the fp32
+product of the element and that scale, and the stored scale is the
+reciprocal of it.  Torch computes the same with IEEE fp32 division and
+multiplication (`torch.div` of two tensors; `scalar / tensor` multiplies by
+a reciprocal instead and is not used), round-half-even then clamp for int8,
+and its own float8 casts (round-half-even; no product exceeds the maximum by
+more than its rounding, so no cast overflows).  Every valid row's codes and
+scale must be bit-equal.  Rows whose maximum is zero are left to the oracle
+tests (torch's 0 * inf is NaN).
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import combine_moe_get_dispatch_amd as moe
+    from gpu_util import DEV
+
+MODES = [(2, 127.0, torch.int8), (0x12, 448.0, torch.float8_e4m3fn), (0x22, 57344.0, torch.float8_e5m2)]
+
+
+@pytest.mark.parametrize("quant,dst_max,dtype", MODES, ids=["int8", "e4m3fn", "e5m2"])
+def test_per_token_codes_equal_torch_arithmetic(quant, dst_max, dtype):
+    T, H, E, R, K = 2048, 7168, 64, 8, 4
+    print(f"[torch crosscheck] quant={quant:#x} T={T} H={H}", flush=True)
+    rng = np.random.default_rng(quant)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int64)
+    idx[rng.random((T, K)) < 0.05] = -1
+    g = torch.Generator(device=DEV)
+    g.manual_seed(quant)
+    x = (torch.randn((T, H), device=DEV, generator=g) * 2.0).to(torch.bfloat16)
+    x[::97] *= 1e-30           # tiny rows: scales near the top of the fp32 range
+    lay = moe.moe_get_dispatch_layout(torch.from_numpy(idx).to(DEV), E, R, 1)
+    rx, rs, _ = moe.moe_dispatch(x, lay, None, quant)
+
+    xf = x.float()
+    m = xf.abs().amax(dim=1, keepdim=True)
+    assert bool((m > 0).all())
+    ds = torch.div(torch.full_like(m, dst_max), m)
+    assert bool(torch.isfinite(ds).all())
+    prod = xf * ds
+    if dtype == torch.int8:
+        q = torch.round(prod).clamp_(-127.0, 127.0).to(torch.int8)
+    else:
+        q = prod.to(dtype)
+    s = torch.div(torch.ones_like(ds), ds)[:, 0]
+
+    tr = lay.token_row.long()
+    valid = tr >= 0
+    tok = torch.arange(T, device=DEV)[:, None].expand(T, K)[valid]
+    rows = tr[valid]
+    assert torch.equal(rx[rows].view(torch.uint8), q[tok].view(torch.uint8))
+    assert torch.equal(rs[rows].view(torch.int32), s[tok].view(torch.int32))
+    torch.cuda.synchronize()
