@@ -55,8 +55,9 @@ def parse():
                    help="draw the workload with this many tokens instead of its own T (0 = its own)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU time budget for the oracle baseline (0 = skip)")
-    p.add_argument("--event-every", type=int, default=10,
-                   help="record stage events on every Nth timed step")
+    p.add_argument("--event-every", type=int, default=0,
+                   help="record stage events on every Nth timed step (0 = every max(1, steps // 20)th "
+                        "step: at least 10 samples from 10 steps on)")
     p.add_argument("--cold-reps", type=int, default=10,
                    help="after timing, repetitions of the cold-cache legs: each stage timed alone "
                         "after 1 GiB of device traffic (a fill, or a read) has evicted L2 and the "
@@ -381,7 +382,7 @@ def main():
 
     # timed region: exactly K steps; stage events on every Nth step, on the
     # stream the kernels use
-    every = max(1, args.event_every)
+    every = args.event_every if args.event_every > 0 else max(1, args.steps // 20)
     events = {i: [timer.new() for _ in range(4)] for i in range(0, args.steps, every)}
     graph = None
     if args.graph:

@@ -23,7 +23,6 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 SMALL_GRID_LIB_PATH = os.path.join(HERE, "libmoe_dispatch_combine_smallgrid.so")
 SMALL_GRID_FLAGS = ["-DMOE_MAX_GRID_LOG2=6"]
 SOURCES = ["moe_api.hip", "layout.hip", "dispatch.hip", "combine.hip", "small_batch.hip"]
-HEADERS = ["device_common.h", "launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -37,6 +36,12 @@ FLAGS = [
 
 def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def headers():
+    """Every header the sources include: all of csrc/*.h and the public header."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")) + [
+        os.path.join(ROOT, "include", "moe_dispatch_combine.h")]
 
 
 def _command(out_path, extra_flags):
@@ -64,13 +69,13 @@ def build(verbose: bool = True, extra_flags=None, with_test_build: bool = False)
     return LIB_PATH
 
 
-def is_stale() -> bool:
-    if not os.path.exists(LIB_PATH):
+def is_stale(path: str = LIB_PATH) -> bool:
+    """True when the library at `path` is missing or older than a source or
+    header it is built from."""
+    if not os.path.exists(path):
         return True
-    t = os.path.getmtime(LIB_PATH)
-    deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + [
-        os.path.join(ROOT, "include", "moe_dispatch_combine.h")]
-    return any(os.path.getmtime(d) > t for d in deps)
+    t = os.path.getmtime(path)
+    return any(os.path.getmtime(d) > t for d in sources() + headers())
 
 
 if __name__ == "__main__":

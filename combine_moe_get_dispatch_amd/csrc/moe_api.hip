@@ -163,6 +163,10 @@ int moe_layout_and_dispatch(const int64_t *topk_idx, const void *x, int num_toke
         return MOE_ERR_INVALID_ARG;
     if (recv_capacity > 0 && !recv_src)
         return MOE_ERR_INVALID_ARG;
+    if (per_token && ((uintptr_t)recv_scales & 3u) != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (recv_weights && ((uintptr_t)recv_weights & 3u) != 0)
+        return MOE_ERR_INVALID_ARG;
 
     LayoutArgs args;
     args.topk_idx = topk_idx;

@@ -24,6 +24,10 @@ Recipe (also listed in the design notes):
     permutation pi; K distinct experts per token by Gumbel-top-k over log p
     (sampling without replacement); weights = softmax of K fresh N(0,1)
     logits.
+  * "firstk" routing (the degenerate extreme of skew): every token picks
+    experts 0..K-1 in order, weights = softmax of K N(0,1) logits.  Each of
+    those K experts receives every token, so dispatch writes K streams of
+    consecutive rows: the same bytes as uniform routing in address order.
   * "drop" fraction: after routing, each (t, k) entry is set to -1 with that
     probability and its weight to 0.
 """
@@ -119,6 +123,10 @@ NEXT_WORKLOADS = [
              seed_index=5, prequant="mxfp8"),
     Workload("mxfp4_prequant_8192x7168_e256_top8", 8192, 7168, 256, 8, 8, 1, QUANT_NONE,
              seed_index=6, prequant="mxfp4"),
+    # the headline's shape and bytes with every token routed to experts 0..7:
+    # dispatch's rows are then written in address order (8 streams)
+    Workload("bf16_4096x7168_e256_top8_firstk", 4096, 7168, 256, 8, 8, 1, QUANT_NONE,
+             routing="firstk", seed_index=1),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + NEXT_WORKLOADS}
 
@@ -178,6 +186,9 @@ def make_routing(rng: np.random.Generator, T: int, E: int, K: int, routing: str,
         logp = -zipf_s * np.log(perm.astype(np.float64) + 1.0)
         g = rng.gumbel(size=(T, E))
         idx = _topk_desc(logp[None, :] + g, K)
+        w = _softmax_f32(rng.standard_normal((T, K), dtype=np.float32))
+    elif routing == "firstk":
+        idx = np.broadcast_to(np.arange(K), (T, K))
         w = _softmax_f32(rng.standard_normal((T, K), dtype=np.float32))
     else:
         raise ValueError(f"unknown routing law {routing!r}")

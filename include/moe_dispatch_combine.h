@@ -194,7 +194,8 @@ int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_top
  *   recv_weights fp32 [recv_capacity] or NULL.
  * Sizes: T >= 0, 32 <= H <= 16384 with H % 32 == 0, 1 <= K <= 16,
  *   0 <= recv_capacity < 2^31.
- * x, recv_x and recv_scales must be 16-byte aligned.
+ * Alignment: x and recv_x 16 bytes; fp32 recv_scales and recv_weights 4
+ *   bytes (MX scale bytes need none).
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP.
  */
 int moe_dispatch(const void *x, int num_tokens, int hidden, int num_topk,
@@ -324,8 +325,8 @@ int moe_layout_and_dispatch_fits(int num_tokens, int hidden, int num_topk, int n
  *   topk_weights fp32 [T, K] or NULL (only read for recv_weights).
  * Outputs (device): as moe_get_dispatch_layout (no workspace is needed);
  *   recv_x [recv_capacity, H] of bf16, int8 or FP8 codes, 16-byte aligned;
- *   recv_scales fp32 [recv_capacity] for the per-token modes (else unused);
- *   recv_weights fp32 [recv_capacity] or NULL.
+ *   recv_scales fp32 [recv_capacity], 4-byte aligned, for the per-token modes
+ *   (else unused); recv_weights fp32 [recv_capacity], 4-byte aligned, or NULL.
  * Errors: MOE_ERR_INVALID_ARG (including sizes that
  *   moe_layout_and_dispatch_fits rejects and other quant modes),
  *   MOE_ERR_CAPACITY, MOE_ERR_HIP; out-of-range expert ids set bit 0 of

@@ -13,6 +13,9 @@ from combine_moe_get_dispatch_amd import workloads as W
 
 if not os.path.exists(moe.LIB_PATH):      # build only when nothing is built
     build_lib.build(verbose=True)
+elif build_lib.is_stale():
+    print(f"warning: {moe.LIB_PATH} is older than a source or header it is built from; "
+          "the GPU tests run the library as built", flush=True)
 
 DEV = torch.device("cuda", 0)
 

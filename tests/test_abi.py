@@ -210,10 +210,11 @@ def test_layout_and_dispatch_limits_and_rules(L, orc):
     assert L.moe_layout_and_dispatch_fits(512, 1024, 2, 64) == 0     # 32768 token x rank cells
     assert L.moe_layout_and_dispatch_fits(128, 8224, 8, 8) == 0      # hidden
 
-    def call(T=128, H=7168, K=8, E=256, R=8, a=1, cap=None, idx=BAD, x=BAD, rx=BAD, outs=None, q=0, rs=BAD):
+    def call(T=128, H=7168, K=8, E=256, R=8, a=1, cap=None, idx=BAD, x=BAD, rx=BAD, outs=None, q=0, rs=BAD,
+             rw=None):
         cap = orc.recv_capacity_bound(T, K, E, a) if cap is None else cap
         outs = [BAD] * 8 if outs is None else outs
-        return L.moe_layout_and_dispatch(idx, x, T, H, K, E, R, a, cap, None, q, *outs, rx, rs, None, None)
+        return L.moe_layout_and_dispatch(idx, x, T, H, K, E, R, a, cap, None, q, *outs, rx, rs, rw, None)
 
     assert call(T=600, K=1) == -1                       # beyond the one-launch limits
     assert call(H=8224) == -1
@@ -230,6 +231,8 @@ def test_layout_and_dispatch_limits_and_rules(L, orc):
     for q in (4, 0x13, 0x24, 0x14, 1):                  # only bf16 and the per-token modes
         assert call(q=q) == -1
     assert call(q=2, rs=None) == -1                     # per-token scales missing
+    assert call(q=2, rs=ctypes.c_void_p(0x1002)) == -1  # fp32 scales not 4-byte aligned
+    assert call(rw=ctypes.c_void_p(0x1006)) == -1       # fp32 row weights not 4-byte aligned
 
 
 def test_missing_library_raises_and_nothing_falls_back(tmp_path):
