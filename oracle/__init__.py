@@ -109,6 +109,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_dispatch_static.restype = i32
         L.oracle_quant_fp8_pergroup_rows.argtypes = [_P, i32, i32, i32, _P, _P]
         L.oracle_quant_fp8_pergroup_rows.restype = None
+        L.oracle_check_static_expert_args.argtypes = [i32, i32, i32, i32, i64]
+        L.oracle_check_static_expert_args.restype = i32
+        L.oracle_dispatch_static_expert.argtypes = [_P, i32, i32, i32, _P, i32, _P, _P, i64, _P, _P, _P]
+        L.oracle_dispatch_static_expert.restype = i32
         L.oracle_quant_static_int8_rows.argtypes = [_P, i32, i32, _P, i32, _P]
         L.oracle_quant_static_int8_rows.restype = None
         L.oracle_combine_fused.argtypes = [_P, i64, i32, i32, i32, _P, _P, _P, _P, _P,
@@ -217,6 +221,35 @@ def dispatch_static(x_bits, token_row, recv_capacity, scales, topk_weights=None,
     recv_w = np.zeros(recv_capacity, np.float32) if with_weights else None
     rc = lib().oracle_dispatch_static(_ptr(x), T, H, K, _ptr(row), _ptr(w), recv_capacity,
                                       _ptr(sc), sc.size, _ptr(recv_x), _ptr(recv_w))
+    if rc != OK:
+        raise OracleError(rc)
+    return recv_x, recv_w
+
+
+def check_static_expert_args(T, H, K, E, cap) -> int:
+    return int(lib().oracle_check_static_expert_args(T, H, K, E, cap))
+
+
+def dispatch_static_expert(x_bits, topk_idx, token_row, recv_capacity, scales, topk_weights=None,
+                           recv_x=None, with_weights=False):
+    """Static int8 quantisation with one fp32 scale row per expert (scales
+    [E, H]): each entry's copy is quantised with its expert's row.  Returns
+    (recv_x int8 [cap, H], recv_weights or None)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    row = np.ascontiguousarray(token_row, dtype=np.int32)
+    K = row.shape[1] if row.ndim == 2 else 1
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    if sc.ndim != 2 or sc.shape[1] != H:
+        raise ValueError("scales must be [num_experts, hidden]")
+    E = sc.shape[0]
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    if recv_x is None:
+        recv_x = np.zeros((recv_capacity, H), np.int8)
+    recv_w = np.zeros(recv_capacity, np.float32) if with_weights else None
+    rc = lib().oracle_dispatch_static_expert(_ptr(x), T, H, K, _ptr(idx), E, _ptr(row), _ptr(w),
+                                             recv_capacity, _ptr(sc), _ptr(recv_x), _ptr(recv_w))
     if rc != OK:
         raise OracleError(rc)
     return recv_x, recv_w

@@ -130,6 +130,20 @@ int oracle_check_static_args(int T, int H, int K, int64_t cap, int num_scales)
     return ORC_OK;
 }
 
+/* Static quantisation with one scale row per expert ([CANN] Constraint 8,
+ * Ascend 950, quantMode 1, INT8: the scales fold each expert's smoothing
+ * weight into its quantisation coefficient, shape (moeExpertNum, H)): the
+ * dispatch sizes plus 1 <= E <= 512 experts. */
+int oracle_check_static_expert_args(int T, int H, int K, int E, int64_t cap)
+{
+    int rc = oracle_check_rows_args(T, H, K, cap, ORC_QUANT_NONE);
+    if (rc != ORC_OK)
+        return rc;
+    if (E < 1 || E > 512)
+        return ORC_ERR_INVALID_ARG;
+    return ORC_OK;
+}
+
 /* Pre-quantised rows ([NMA] dispatch Parameters x: a (data, scale) tuple for
  * MXFP8 / MXFP4; Quantization Constraints: data [T, H] or [T, H/2], scales
  * [T, H/32]): row_bytes a positive multiple of 16 up to 32768, scale_bytes
@@ -472,8 +486,9 @@ static void quant_fp8_pergroup_row(const uint16_t *x, int H, int fmt, uint8_t *q
 
 /* [CANN] Formula Case 2 (quantMode 1, static quantisation) with an INT8
  * destination ([CANN] Constraint 8, Ascend 950: the input scales are one
- * quantisation coefficient, shape (1,), or a smoothing vector shared by all
- * experts, shape (H,)):
+ * quantisation coefficient, shape (1,), a smoothing vector shared by all
+ * experts, shape (H,), or one coefficient row per expert, shape (E, H), of
+ * which the row of the copy's expert is passed here):
  *   xFp32    = CastToFp32(X) * scales     (fp32 multiply)
  *   quantOut = Cast(xFp32, INT8)
  * Reading: the cast rounds half to even and saturates to [-128, 127] (a
@@ -604,6 +619,44 @@ int oracle_dispatch_static(const uint16_t *x, int T, int H, int K, const int32_t
             }
         }
         free(q);
+    }
+    return ORC_OK;
+}
+
+/*
+ * Dispatch with static int8 quantisation and one scale row per expert
+ * ([CANN] Formula Case 2, quantMode 1, with the (moeExpertNum, H) scale shape
+ * of Constraint 8, Ascend 950).  The page quantises before the exchange;
+ * with a scale row per destination expert the codes depend on where a copy
+ * goes, so the entry (t, k) sent to expert e = topk_idx[t, k] holds
+ *   recv_x[row(t, k), h] = Cast(CastToFp32(x[t, h]) * scales[e, h], INT8)
+ * (the same cast as the other static shapes), and the K copies of a token
+ * differ wherever their experts' scales do.  scales: fp32 [E, H], row-major.
+ * Entries the layout dropped (row -1) are skipped; so is an entry whose id is
+ * outside [0, E) (the layout drops those too).  recv_x: int8 [cap, H].
+ */
+int oracle_dispatch_static_expert(const uint16_t *x, int T, int H, int K, const int64_t *topk_idx,
+                                  int E, const int32_t *token_row, const float *topk_weights,
+                                  int64_t cap, const float *scales, int8_t *recv_x,
+                                  float *recv_weights)
+{
+    int rc = oracle_check_static_expert_args(T, H, K, E, cap);
+    if (rc != ORC_OK)
+        return rc;
+    if (T > 0 && (!x || !topk_idx || !token_row || !recv_x || !scales))
+        return ORC_ERR_INVALID_ARG;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int32_t row = token_row[(int64_t)t * K + k];
+            int64_t e = topk_idx[(int64_t)t * K + k];
+            if (row < 0 || row >= cap || e < 0 || e >= E)
+                continue;
+            quant_static_int8_row(x + (int64_t)t * H, H, scales + e * H, H,
+                                  recv_x + (int64_t)row * H);
+            if (recv_weights)
+                recv_weights[row] = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;
+        }
     }
     return ORC_OK;
 }

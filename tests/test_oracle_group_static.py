@@ -162,3 +162,82 @@ def test_static_rules(orc, n, code):
 @pytest.mark.parametrize("q,code", [(0x13, 0), (0x23, 0), (0x03, -1), (0x33, -1)])
 def test_pergroup_mode_rules(orc, q, code):
     assert orc.check_rows_args(16, 1024, 4, 1000, q) == code
+
+
+# ----------------------------------------------------------------------------- static int8, (E, H) scales
+
+def _routing(T, K, E, seed, drop=0.0):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    if drop > 0:
+        idx[rng.random((T, K)) < drop] = -1
+    return idx
+
+
+def test_static_expert_uniform_rows_reduce_to_the_shared_shapes(orc):
+    """Every expert holding the same scale row is the (H,) shape, and every
+    expert holding one constant is the (1,) shape (both pinned above)."""
+    w = W.Workload("t", 40, 256, 16, 4, 4, 3, 0, drop_prob=0.15, x_sigma=20.0, seed_index=19)
+    inp = W.generate(w)
+    lay = orc.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    rng = np.random.default_rng(36)
+    per_channel = rng.uniform(0.25, 4.0, size=256).astype(np.float32)
+    for shared in (per_channel, np.array([3.0], np.float32)):
+        table = np.broadcast_to(shared, (w.num_experts, 256)).astype(np.float32)
+        ex, ew = orc.dispatch_static_expert(inp.x_bits, inp.topk_idx, lay.token_row, lay.recv_capacity,
+                                            table, inp.topk_weights, with_weights=True)
+        sx, sw = orc.dispatch_static(inp.x_bits, lay.token_row, lay.recv_capacity, shared,
+                                     inp.topk_weights, with_weights=True)
+        np.testing.assert_array_equal(ex, sx)
+        np.testing.assert_array_equal(ew, sw)
+
+
+def test_static_expert_each_copy_uses_its_experts_row(orc):
+    """Integer-valued x and power-of-two scales 2^j[e, h]: each product is
+    exact, so the code is the product rounded half to even and saturated
+    (closed form).  Each copy must follow the scale row of the expert it is
+    sent to, so copies of one token differ across experts."""
+    T, H, K, E = 48, 64, 4, 8
+    rng = np.random.default_rng(37)
+    x = rng.integers(-40, 41, size=(T, H)).astype(np.float32)
+    x[:, :4] = [0.5, -0.5, 1.5, -2.5]                             # half-way ties after scale 1
+    j = rng.integers(-3, 4, size=(E, H))
+    j[:, :4] = 0
+    scales = np.exp2(j).astype(np.float32)
+    idx = _routing(T, K, E, 38, drop=0.1)
+    lay = orc.layout(idx, E, 2, 2)
+    rx, _ = orc.dispatch_static_expert(bf16(x), idx, lay.token_row, lay.recv_capacity, scales)
+    differ = 0
+    for t in range(T):
+        rows = []
+        for k in range(K):
+            r = lay.token_row[t, k]
+            if r < 0:
+                continue
+            e = idx[t, k]
+            expect = np.clip(np.round(x[t].astype(np.float64) * np.exp2(j[e])), -128, 127)
+            np.testing.assert_array_equal(rx[r], expect.astype(np.int8), err_msg=f"t={t} k={k} e={e}")
+            rows.append(rx[r])
+        differ += sum(not np.array_equal(a, b) for a in rows for b in rows) > 0
+    assert differ > T // 2
+    assert (rx[:, :4] == [0, 0, 2, -2]).all(axis=1)[lay.recv_src >= 0].all()
+    assert (np.abs(rx.astype(int)) >= 127).any()                  # saturation exercised
+
+
+def test_static_expert_rows_not_named_stay_untouched(orc):
+    T, H, K, E = 20, 32, 3, 6
+    idx = _routing(T, K, E, 39, drop=0.3)
+    lay = orc.layout(idx, E, 3, 4)
+    x = bf16(np.random.default_rng(40).normal(size=(T, H)).astype(np.float32))
+    scales = np.full((E, H), 50.0, np.float32)
+    init = np.full((lay.recv_capacity, H), 77, np.int8)
+    rx, _ = orc.dispatch_static_expert(x, idx, lay.token_row, lay.recv_capacity, scales, recv_x=init.copy())
+    unused = lay.recv_src < 0
+    assert unused.any()
+    np.testing.assert_array_equal(rx[unused], init[unused])
+
+
+@pytest.mark.parametrize("E,code", [(1, 0), (512, 0), (0, -1), (513, -1)])
+def test_static_expert_rules(orc, E, code):
+    assert orc.check_static_expert_args(8, 128, 2, E, 100) == code
+    assert orc.check_static_expert_args(8, 100, 2, 4, 100) == -1     # H not a multiple of 32

@@ -98,6 +98,12 @@ MUTANTS = [
      "for (int h = g0; h < g0 + n - 1; ++h) {\n            float ab"),
     ("static int8 saturates at -127", CODECS,
      "if (r < -128.0f)\n            r = -128.0f;", "if (r < -127.0f)\n            r = -127.0f;"),
+    ("per-expert static scales taken by k, not by expert", CODECS,
+     "quant_static_int8_row(x + (int64_t)t * H, H, scales + e * H, H,",
+     "quant_static_int8_row(x + (int64_t)t * H, H, scales + (int64_t)k * H, H,"),
+    ("per-expert static scales of the token's first expert", CODECS,
+     "quant_static_int8_row(x + (int64_t)t * H, H, scales + e * H, H,",
+     "quant_static_int8_row(x + (int64_t)t * H, H, scales + (topk_idx[(int64_t)t * K] >= 0 && topk_idx[(int64_t)t * K] < E ? topk_idx[(int64_t)t * K] : e) * H, H,"),
     ("static per-channel scales reversed", CODECS,
      "scales[num_scales == 1 ? 0 : h]", "scales[num_scales == 1 ? 0 : H - 1 - h]"),
     ("FP8 destination formats swapped", CODECS,
