@@ -80,13 +80,18 @@ PER_TOKEN_MODES = (0x02, 0x12, 0x22)
 PER_GROUP_MODES = (0x13, 0x23)
 
 
-def stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows=None, static=False, epilogue=False):
+def stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows=None, static=False, epilogue=False,
+                static_per_expert=False):
     """Algorithmic bytes of each stage (see module docstring).  prequant_rows =
-    (data bytes, scale bytes) per token for the pre-quantised pass-through."""
+    (data bytes, scale bytes) per token for the pre-quantised pass-through;
+    static_per_expert adds the ids (int64 [T, K]) and the [E, H] fp32 scale
+    table read once."""
     layout = 8 * T * K + 4 * T * R + 4 * R + 8 * E + 4 * (E + 1) + 4 * T * K + 4 * cap + 4
     if prequant_rows is not None:
         rb, sb = prequant_rows
         dispatch = T * (rb + sb) + 4 * T * K + V * (rb + sb)
+    elif static_per_expert:
+        dispatch = 2 * T * H + 4 * T * K + 8 * T * K + 4 * E * H + V * H
     elif static:
         dispatch = 2 * T * H + 4 * T * K + V * H
     else:
@@ -207,6 +212,9 @@ def cpu_baseline(inp, w, quant, budget_s, bytes_fn, prequant=None):
         epi = (W.random_bf16_rows(w.num_tokens, w.hidden, 21), W.random_bf16_rows(w.num_tokens, w.hidden, 22),
                np.full(w.hidden, 0x3F80, np.uint16))
     V = int((inp.topk_idx >= 0).sum())
+    if w.static_per_expert:
+        from combine_moe_get_dispatch_amd import workloads as W
+        expert_scales = W.expert_scales(w)
 
     def leg(budget):
         reps, total_bytes = 0, 0
@@ -216,6 +224,10 @@ def cpu_baseline(inp, w, quant, budget_s, bytes_fn, prequant=None):
             if prequant is not None:
                 oracle.dispatch_prequantized(prequant[0], prequant[1], ol.token_row, ol.recv_capacity)
                 y = prequant[2]
+            elif w.static_per_expert:
+                oracle.dispatch_static_expert(inp.x_bits, inp.topk_idx, ol.token_row, ol.recv_capacity,
+                                              expert_scales)
+                y = np.zeros((ol.recv_capacity, w.hidden), np.uint16)
             elif w.static_scale > 0:
                 oracle.dispatch_static(inp.x_bits, ol.token_row, ol.recv_capacity,
                                        np.array([w.static_scale], np.float32))
@@ -301,6 +313,21 @@ def main():
 
         def run_dispatch():
             moe.moe_dispatch_prequantized(data, scales, lay, None, rd, rsc)
+    elif w.static_per_expert:
+        x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        rx = torch.empty((cap, H), dtype=torch.int8, device=dev)
+        escales = torch.from_numpy(W.expert_scales(w)).to(dev)
+
+        def run_dispatch():
+            moe.moe_dispatch_static_per_expert(x, lay, idx, escales, None, recv_x=rx)
+
+        run_dispatch()
+        # identity expert: each row divided by its expert's scale row
+        row_expert = torch.repeat_interleave(torch.arange(E, device=dev), lay.num_recv_tokens_per_expert.long())
+        row_expert = torch.nn.functional.pad(row_expert, (0, cap - row_expert.numel()))
+        y = torch.nan_to_num(rx.float() / escales[row_expert], nan=0.0, posinf=0.0,
+                             neginf=0.0).to(torch.bfloat16)
+        del row_expert
     elif w.static_scale > 0:
         x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
         rx = torch.empty((cap, H), dtype=torch.int8, device=dev)
@@ -421,7 +448,7 @@ def main():
     med_us = {k: float(np.median(v)) for k, v in st.items()}
 
     sb = stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows, w.static_scale > 0,
-                     bool(w.epilogue))
+                     bool(w.epilogue), w.static_per_expert)
     step_bytes = sum(sb.values())
     ms_per_step = elapsed / args.steps * 1e3
     gbs = step_bytes * args.steps / elapsed / 1e9
@@ -480,14 +507,15 @@ def main():
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(inp, w, quant, args.cpu_seconds,
                            lambda v, c: stage_bytes(T, H, K, R, E, v, c, quant, prequant_rows,
-                                                    w.static_scale > 0, bool(w.epilogue)),
+                                                    w.static_scale > 0, bool(w.epilogue),
+                                                    w.static_per_expert),
                            prequant=cpu_y)
 
     qname = {0: "bf16", 2: "int8", 4: "mxfp8_e4m3", 0x12: "fp8_e4m3_per_token",
              0x22: "fp8_e5m2_per_token", 0x24: "mxfp8_e5m2", 0x13: "fp8_e4m3_per_group",
              0x23: "fp8_e5m2_per_group"}[quant]
     if w.static_scale > 0:
-        qname = "int8_static"
+        qname = "int8_static_per_expert" if w.static_per_expert else "int8_static"
     if w.prequant:
         qname = f"{w.prequant}_prequantized"
     rec = {

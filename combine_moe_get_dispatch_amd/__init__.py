@@ -47,7 +47,8 @@ MX_MODES = (QUANT_MXFP8_E4M3, QUANT_MXFP8_E5M2)
 FLAG_BAD_EXPERT_ID = 1
 
 __all__ = [
-    "moe_get_dispatch_layout", "moe_dispatch", "moe_dispatch_static", "moe_dispatch_prequantized",
+    "moe_get_dispatch_layout", "moe_dispatch", "moe_dispatch_static", "moe_dispatch_static_per_expert",
+    "moe_dispatch_prequantized",
     "moe_combine", "moe_combine_fused",
     "moe_recv_capacity_bound",
     "moe_layout_workspace_bytes", "DispatchLayout", "allocate_layout", "allocate_recv",
@@ -82,6 +83,8 @@ def declare_signatures(L: ctypes.CDLL) -> ctypes.CDLL:
     L.moe_dispatch.restype = i32
     L.moe_dispatch_static.argtypes = [P, i32, i32, i32, P, P, i64, P, i32, P, P, P]
     L.moe_dispatch_static.restype = i32
+    L.moe_dispatch_static_per_expert.argtypes = [P, i32, i32, i32, P, i32, P, P, i64, P, P, P, P]
+    L.moe_dispatch_static_per_expert.restype = i32
     L.moe_dispatch_prequantized.argtypes = [P, i32, i32, P, i32, i32, P, P, i64, P, P, P, P]
     L.moe_dispatch_prequantized.restype = i32
     L.moe_combine.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
@@ -436,6 +439,41 @@ def moe_dispatch_static(x: torch.Tensor, layout: DispatchLayout, scales: torch.T
                                    _ptr(recv_weights), _stream(dev))
     if rc != MOE_OK:
         raise MoeError("moe_dispatch_static", rc)
+    return recv_x, recv_weights
+
+
+def moe_dispatch_static_per_expert(x: torch.Tensor, layout: DispatchLayout, topk_idx: torch.Tensor,
+                                   scales: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                                   recv_x: Optional[torch.Tensor] = None,
+                                   recv_weights: Optional[torch.Tensor] = None,
+                                   with_weights: bool = False):
+    """Static int8 quantisation with one fp32 scale row per expert (scales
+    [num_experts, H]) and dispatch: each copy of a token is quantised with
+    the row of the expert it goes to.  ``topk_idx`` is the int64 [T, K] the
+    layout was made from.  Returns (recv_x int8 [cap, H], recv_weights)."""
+    T, K, E, cap = layout.num_tokens, layout.num_topk, layout.num_experts, layout.recv_capacity
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError(f"x must be [{T}, hidden]")
+    H = x.shape[1]
+    dev = x.device
+    _check_layout(layout, dev)
+    _check(x, "x", torch.bfloat16, device=dev)
+    _check(topk_idx, "topk_idx", torch.int64, (T, K), dev)
+    _check(scales, "scales", torch.float32, (E, H), dev)
+    if topk_weights is not None:
+        _check(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    if recv_x is None:
+        recv_x = torch.empty((cap, H), dtype=torch.int8, device=dev)
+    if recv_weights is None and with_weights:
+        recv_weights = torch.empty(cap, dtype=torch.float32, device=dev)
+    _check(recv_x, "recv_x", torch.int8, (cap, H), dev)
+    if recv_weights is not None:
+        _check(recv_weights, "recv_weights", torch.float32, (cap,), dev)
+    rc = lib().moe_dispatch_static_per_expert(_ptr(x), T, H, K, _ptr(topk_idx), E, layout._token_row_ptr,
+                                              _ptr(topk_weights), cap, _ptr(scales), _ptr(recv_x),
+                                              _ptr(recv_weights), _stream(dev))
+    if rc != MOE_OK:
+        raise MoeError("moe_dispatch_static_per_expert", rc)
     return recv_x, recv_weights
 
 

@@ -17,7 +17,9 @@
 //   per-group : the per-token formula applied to each group of 128 elements
 //               (Formula Case 4; FP8 destinations), one fp32 scale per group
 //   static    : q = int8_sat(rint(x * scale)) with the caller's scale(s)
-//               (Formula Case 2: one coefficient or one per channel)
+//               (Formula Case 2: one coefficient, one per channel, or one
+//               row per expert, Constraint 8 -- then each copy uses the
+//               row of its own expert)
 //   pre-quantised rows (the Normal Mode API page's (data, scale) tuple input):
 //               data row and scale row copied unchanged
 //
@@ -270,6 +272,24 @@ template <Dst D> struct GroupCodec {
     }
 };
 
+// Static int8 codes of 8 bf16 elements with their 8 scales (s_lo: elements
+// 0-3, s_hi: 4-7): one fp32 multiply, round half to even, saturate to
+// [-128, 127].
+__device__ __forceinline__ u32x2 static_int8_codes(const u32x4 xv, const float4 s_lo,
+                                                   const float4 s_hi)
+{
+    const float sv[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float lo = fminf(fmaxf(__builtin_rintf(bf16_lo(xv[c]) * sv[2 * c]), -128.0f), 127.0f);
+        const float hi = fminf(fmaxf(__builtin_rintf(bf16_hi(xv[c]) * sv[2 * c + 1]), -128.0f), 127.0f);
+        const uint32_t b = ((uint32_t)(int)lo & 0xFFu) | (((uint32_t)(int)hi & 0xFFu) << 8);
+        w[c >> 1] |= b << (16 * (c & 1));
+    }
+    return u32x2{w[0], w[1]};
+}
+
 // Static int8 with the caller's scales: one coefficient, or one per channel
 // (the 8 channel scales of vector i as two 16-byte loads).  No scale output.
 struct StaticCodec {
@@ -287,17 +307,7 @@ struct StaticCodec {
             s_lo = float4{s0, s0, s0, s0};
             s_hi = s_lo;
         }
-        const float sv[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
-        uint32_t w[2] = {0u, 0u};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            // one fp32 multiply, round half to even, saturate to [-128, 127]
-            const float lo = fminf(fmaxf(__builtin_rintf(bf16_lo(xv[c]) * sv[2 * c]), -128.0f), 127.0f);
-            const float hi = fminf(fmaxf(__builtin_rintf(bf16_hi(xv[c]) * sv[2 * c + 1]), -128.0f), 127.0f);
-            const uint32_t b = ((uint32_t)(int)lo & 0xFFu) | (((uint32_t)(int)hi & 0xFFu) << 8);
-            w[c >> 1] |= b << (16 * (c & 1));
-        }
-        return u32x2{w[0], w[1]};
+        return static_int8_codes(xv, s_lo, s_hi);
     }
     __device__ void store_scale(int64_t, int, uint32_t) const {}
 };
@@ -365,6 +375,66 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_codec_slice_kern
         }
         if (s == 0)
             write_row_weight(token_row, topk_weights, recv_weights, t, K, cap, lane);
+    }
+}
+
+// --------------------------------------------------------------------------- static, per expert
+
+// Static int8 with one scale row per expert (scales [E, H]): a copy's codes
+// depend on the expert it goes to, so each wave encodes its slice of x once
+// per entry, with that expert's 2 KiB slice of the scale table (32 bytes per lane,
+// two 16-byte loads).  Work items are ordered slice-major (every token's
+// slice 0, then slice 1, ...), so the waves in flight share one or two
+// slices and the scale columns they read, E x 2 KiB, stay in L2 (token-major
+// order would stream the whole E x H table through L2 for every token
+// block).  The row numbers and expert ids of the token's KMAX entries are
+// loaded before the first scale load.  An entry whose row is -1 or whose id
+// is outside [0, E) is skipped (the layout drops such ids).
+template <int KMAX>
+__global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_static_expert_kernel(
+    const u32x4 *__restrict__ x, int nvec, int T, int64_t nitems, int K, int E,
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ token_row,
+    const float *__restrict__ topk_weights, int64_t cap, const float4 *__restrict__ scales,
+    u32x2 *__restrict__ recv, float *__restrict__ recv_weights)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = (int)threadIdx.x / kWave;
+    for (int64_t b = (int64_t)blockIdx.x * kSliceWaves + wave; b < nitems;
+         b += (int64_t)gridDim.x * kSliceWaves) {
+        const int s = (int)(b / T);
+        const int64_t t = b - (int64_t)s * T;
+        const int i = s * kWave + lane;
+        const int ic = min(i, nvec - 1); // clamped: always in bounds
+        const u32x4 xv = x[t * nvec + ic];
+        int rows[KMAX], es[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            rows[k] = -1;
+            es[k] = 0;
+            if (k < K) {
+                const int r = token_row[t * K + k];
+                const int64_t e = topk_idx[t * K + k];
+                if (r >= 0 && r < cap && e >= 0 && e < E) {
+                    rows[k] = r;
+                    es[k] = (int)e;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (rows[k] < 0)
+                continue;
+            const float4 *sc = scales + ((int64_t)es[k] * nvec + ic) * 2;
+            const u32x2 q = static_int8_codes(xv, sc[0], sc[1]);
+            if (i < nvec)
+                __builtin_nontemporal_store(q, recv + (int64_t)rows[k] * nvec + i);
+        }
+        if (recv_weights && s == 0 && lane < K) {
+            const int r = token_row[t * K + lane];
+            const int64_t e = topk_idx[t * K + lane];
+            if (r >= 0 && r < cap && e >= 0 && e < E)
+                recv_weights[r] = topk_weights ? topk_weights[t * K + lane] : 1.0f;
+        }
     }
 }
 
@@ -510,6 +580,31 @@ hipError_t launch_dispatch_static(const void *x, int T, int H, int K, const int3
     const SliceGrid g = slice_grid(T, nvec, kSliceWaves);
     return launch_codec(StaticCodec{scales, num_scales == H ? 1 : 0}, g, stream, (const u32x4 *)x,
                         nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x, recv_weights);
+}
+
+hipError_t launch_dispatch_static_expert(const void *x, int T, int H, int K, const int64_t *topk_idx,
+                                         int E, const int32_t *token_row,
+                                         const float *topk_weights, int64_t cap,
+                                         const float *scales, void *recv_x, float *recv_weights,
+                                         hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    const int nvec = H / 8;
+    const SliceGrid g = slice_grid(T, nvec, kSliceWaves);
+    const dim3 grid(g.blocks), block(kSliceWaves * kWave);
+    const u32x4 *xs = (const u32x4 *)x;
+    const float4 *sc = (const float4 *)scales;
+    u32x2 *rq = (u32x2 *)recv_x;
+    if (K <= 1)
+        return launch_kernel(dispatch_static_expert_kernel<1>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+    if (K <= 2)
+        return launch_kernel(dispatch_static_expert_kernel<2>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+    if (K <= 4)
+        return launch_kernel(dispatch_static_expert_kernel<4>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+    if (K <= 8)
+        return launch_kernel(dispatch_static_expert_kernel<8>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+    return launch_kernel(dispatch_static_expert_kernel<16>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
 }
 
 hipError_t launch_dispatch_rows(const void *data, int T, int row_bytes, const void *scales,

@@ -144,6 +144,12 @@ hipError_t launch_dispatch_static(const void *x, int T, int H, int K, const int3
                                   int num_scales, void *recv_x, float *recv_weights,
                                   hipStream_t stream);
 
+hipError_t launch_dispatch_static_expert(const void *x, int T, int H, int K, const int64_t *topk_idx,
+                                         int E, const int32_t *token_row,
+                                         const float *topk_weights, int64_t cap,
+                                         const float *scales, void *recv_x, float *recv_weights,
+                                         hipStream_t stream);
+
 hipError_t launch_dispatch_rows(const void *data, int T, int row_bytes, const void *scales,
                                 int scale_bytes, int K, const int32_t *token_row,
                                 const float *topk_weights, int64_t cap, void *recv_data,

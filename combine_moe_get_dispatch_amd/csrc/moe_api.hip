@@ -241,6 +241,34 @@ int moe_dispatch_static(const void *x, int num_tokens, int hidden, int num_topk,
                : MOE_ERR_HIP;
 }
 
+int moe_dispatch_static_per_expert(const void *x, int num_tokens, int hidden, int num_topk,
+                                   const int64_t *topk_idx, int num_experts,
+                                   const int32_t *token_row, const float *topk_weights,
+                                   int64_t recv_capacity, const float *scales, void *recv_x,
+                                   float *recv_weights, hipStream_t stream)
+{
+    const int T = num_tokens, H = hidden, K = num_topk, E = num_experts;
+    int rc = check_rows_sizes(T, H, K, recv_capacity, MOE_QUANT_NONE);
+    if (rc != MOE_OK)
+        return rc;
+    if (E < 1 || E > MOE_MAX_EXPERTS)
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !topk_idx || !token_row || !recv_x || !scales || !aligned16(x) ||
+        !aligned16(recv_x) || !aligned16(scales))
+        return MOE_ERR_INVALID_ARG;
+    if (((uintptr_t)topk_idx & 7u) != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (recv_weights && ((uintptr_t)recv_weights & 3u) != 0)
+        return MOE_ERR_INVALID_ARG;
+    return launch_dispatch_static_expert(x, T, H, K, topk_idx, E, token_row, topk_weights,
+                                         recv_capacity, scales, recv_x, recv_weights,
+                                         stream) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
 int moe_dispatch_prequantized(const void *data, int num_tokens, int row_bytes, const void *scales,
                               int scale_bytes, int num_topk, const int32_t *token_row,
                               const float *topk_weights, int64_t recv_capacity, void *recv_data,

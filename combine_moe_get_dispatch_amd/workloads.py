@@ -73,6 +73,7 @@ class Workload:
     seed_index: int = 0
     prequant: str = ""              # "" | "mxfp8" | "mxfp4": pre-quantised (data, scale) input
     static_scale: float = 0.0       # > 0: static int8 quantisation with this one coefficient
+    static_per_expert: bool = False  # with static_scale: one scale row per expert (expert_scales)
     epilogue: str = ""              # "" | "shared_residual_rmsnorm": combine epilogues
 
     def describe(self) -> str:
@@ -81,6 +82,8 @@ class Workload:
             q = f"pre-quantised {self.prequant.upper()} pass-through"
         if self.static_scale > 0:
             q = f"static int8 (scale {self.static_scale:g})"
+        if self.static_per_expert:
+            q = f"static int8, one scale row per expert (around {self.static_scale:g})"
         if self.epilogue:
             q += ", combine + shared expert + residual + RMSNorm"
         return (f"{self.num_tokens} tokens x hidden {self.hidden}, "
@@ -123,6 +126,9 @@ NEXT_WORKLOADS = [
              seed_index=5, prequant="mxfp8"),
     Workload("mxfp4_prequant_8192x7168_e256_top8", 8192, 7168, 256, 8, 8, 1, QUANT_NONE,
              seed_index=6, prequant="mxfp4"),
+    Workload("int8_static_expert_8192x7168_e256_top8_zipf", 8192, 7168, 256, 16, 8, 128, QUANT_NONE,
+             routing="zipf", zipf_s=1.1, x_sigma=2.0, seed_index=2, static_scale=127.0 / 12.0,
+             static_per_expert=True),
     # the headline's shape and bytes with every token routed to experts 0..7:
     # dispatch's rows are then written in address order (8 streams)
     Workload("bf16_4096x7168_e256_top8_firstk", 4096, 7168, 256, 8, 8, 1, QUANT_NONE,
@@ -242,6 +248,14 @@ def generate_prequant(w: Workload, num_tokens: Optional[int] = None):
     scales = rng.integers(100, 140, size=(T, sb), dtype=np.uint8)
     idx, wt = generate_routing(w, T)
     return data, scales, idx, wt
+
+
+def expert_scales(w: Workload) -> np.ndarray:
+    """fp32 [E, H] static scale rows of a per-expert static workload: the
+    workload's coefficient times independent uniform factors in [0.5, 2)."""
+    rng = _rng(w, 2, 0)
+    u = rng.uniform(0.5, 2.0, size=(w.num_experts, w.hidden)).astype(np.float32)
+    return np.ascontiguousarray(u * np.float32(w.static_scale), dtype=np.float32)
 
 
 def random_bf16_rows(rows: int, hidden: int, seed: int, sigma: float = 1.0) -> np.ndarray:

@@ -10,6 +10,8 @@
  *                              experts, optionally quantised once per token
  *                              (int8, FP8 per token or per group of 128, MX)
  *   moe_dispatch_static        the same with int8 and caller-given scales
+ *   moe_dispatch_static_per_expert  the same with one scale row per expert
+ *                              (each copy quantised for its own expert)
  *   moe_dispatch_prequantized  the same for rows the caller has quantised
  *                              (data and scale bytes moved unchanged)
  *   moe_combine                top-k weighted sum of every token's expert rows
@@ -206,7 +208,8 @@ int moe_dispatch(const void *x, int num_tokens, int hidden, int num_topk,
 /*
  * Dispatch with static int8 quantisation (CANN page, Formula Case 2, quantMode
  * 1; Constraint 8: the scales are one quantisation coefficient, shape (1,),
- * or one smoothing value per channel, shape (H,)).
+ * or one smoothing value per channel, shape (H,); the third shape, one row
+ * per expert, is moe_dispatch_static_per_expert).
  *
  * For every entry (t, k) with row = token_row[t, k] in [0, recv_capacity):
  *   recv_x[row, h] = saturate_int8(round_half_even(x[t, h] * scales[h or 0]))
@@ -223,6 +226,35 @@ int moe_dispatch_static(const void *x, int num_tokens, int hidden, int num_topk,
                         const int32_t *token_row, const float *topk_weights,
                         int64_t recv_capacity, const float *scales, int num_scales, void *recv_x,
                         float *recv_weights, hipStream_t stream);
+
+/*
+ * Dispatch with static int8 quantisation and one scale row per expert (CANN
+ * page, Formula Case 2, quantMode 1; Constraint 8, Ascend 950: the scales are
+ * each expert's quantisation coefficient with its smoothing weight folded
+ * in, shape (moeExpertNum, H)).
+ *
+ * For every entry (t, k) with row = token_row[t, k] in [0, recv_capacity) and
+ * e = topk_idx[t, k] in [0, num_experts):
+ *   recv_x[row, h] = saturate_int8(round_half_even(x[t, h] * scales[e, h]))
+ * with the product in fp32 and saturation to [-128, 127].  Unlike the other
+ * modes the codes depend on the destination: the K copies of a token differ
+ * wherever their experts' scale rows do.  Entries with row -1 are skipped, and
+ * so are entries whose id is outside [0, num_experts) (the layout drops them).
+ * No scales are written; recv_weights as for moe_dispatch.
+ * Inputs (device): x bf16 [T, H]; topk_idx int64 [T, K], the ids the layout was
+ *   made from; token_row int32 [T, K]; topk_weights fp32 [T, K] or NULL;
+ *   scales fp32 [num_experts, H], row-major.
+ * Output (device): recv_x int8 [recv_capacity, H].
+ * Sizes: as for moe_dispatch, and 1 <= num_experts <= 512.
+ * Alignment: x, recv_x and scales 16 bytes; topk_idx 8 bytes; recv_weights
+ *   4 bytes.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP.
+ */
+int moe_dispatch_static_per_expert(const void *x, int num_tokens, int hidden, int num_topk,
+                                   const int64_t *topk_idx, int num_experts,
+                                   const int32_t *token_row, const float *topk_weights,
+                                   int64_t recv_capacity, const float *scales, void *recv_x,
+                                   float *recv_weights, hipStream_t stream);
 
 /*
  * Dispatch of pre-quantised tokens (Normal Mode API page, dispatch Parameters

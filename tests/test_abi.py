@@ -189,6 +189,26 @@ def test_static_pointer_rules(L):
     assert f(None, 0, 1024, 4, None, None, 1000, None, 1, None, None, None) == 0
 
 
+@pytest.mark.parametrize("E", [0, 513])
+def test_static_per_expert_rejects_like_the_oracle(L, orc, E):
+    assert orc.check_static_expert_args(16, 1024, 4, E, 1000) == -1
+    assert L.moe_dispatch_static_per_expert(BAD, 16, 1024, 4, BAD, E, BAD, None, 1000, BAD, BAD, None,
+                                            None) == -1
+
+
+def test_static_per_expert_pointer_rules(L):
+    f = L.moe_dispatch_static_per_expert
+    assert f(BAD, 16, 1024, 4, None, 8, BAD, None, 1000, BAD, BAD, None, None) == -1    # ids missing
+    assert f(BAD, 16, 1024, 4, BAD, 8, BAD, None, 1000, None, BAD, None, None) == -1    # scales missing
+    assert f(BAD, 16, 1024, 4, BAD, 8, None, None, 1000, BAD, BAD, None, None) == -1    # token_row missing
+    assert f(BAD, 16, 1024, 4, BAD, 8, BAD, None, 1000, ctypes.c_void_p(0x1004), BAD, None, None) == -1
+    assert f(BAD, 16, 1024, 4, ctypes.c_void_p(0x1004), 8, BAD, None, 1000, BAD, BAD, None, None) == -1
+    assert f(BAD, 16, 1024, 4, BAD, 8, BAD, None, 1000, BAD, BAD, ctypes.c_void_p(0x1002), None) == -1
+    assert f(BAD, 16, 48, 4, BAD, 8, BAD, None, 1000, BAD, BAD, None, None) == -1        # H % 32
+    assert f(BAD, 16, 1024, 17, BAD, 8, BAD, None, 1000, BAD, BAD, None, None) == -1     # K
+    assert f(None, 0, 1024, 4, None, 8, None, None, 1000, None, None, None, None) == 0
+
+
 def test_combine_fused_rules(L):
     f = L.moe_combine_fused
     assert f(BAD, 1000, 16, 48, 4, BAD, None, None, None, None, 1e-6, BAD, None, None) == -1

@@ -51,3 +51,12 @@ def test_cpu_baseline_leg_reports_both_thread_counts():
                                                             w.num_experts, v, c, w.quant_mode))
     assert res["kind"] == "oracle" and res["unit"] == "GB/s" and res["value"] > 0
     assert res["cores"] >= 1 and res["single_thread"]["cores"] == 1 and res["single_thread"]["value"] > 0
+
+
+def test_static_per_expert_bytes_count_ids_and_the_scale_table():
+    T, H, K, R, E = 8192, 7168, 8, 16, 256
+    V = T * K
+    base = bench.stage_bytes(T, H, K, R, E, V, V, 0, static=True)
+    per_expert = bench.stage_bytes(T, H, K, R, E, V, V, 0, static=True, static_per_expert=True)
+    assert per_expert["dispatch"] - base["dispatch"] == 8 * T * K + 4 * E * H
+    assert per_expert["combine"] == base["combine"] and per_expert["layout"] == base["layout"]

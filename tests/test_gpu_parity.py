@@ -435,6 +435,72 @@ def test_dispatch_static_parity(per_channel, H):
     np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
 
 
+STATIC_EXPERT_CASES = [
+    # name, T, H, K, E, R, a, dup, drop
+    ("t600_h7168_k8", 600, 7168, 8, 64, 8, 4, False, 0.05),
+    ("h96_duplicates", 300, 96, 5, 24, 4, 3, True, 0.2),
+    ("h16384_k16_e512", 257, 16384, 16, 512, 64, 128, False, 0.0),
+    ("h32_k1_one_expert", 77, 32, 1, 1, 1, 1, False, 0.1),
+    ("all_dropped", 50, 256, 4, 16, 4, 2, False, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", STATIC_EXPERT_CASES, ids=[c[0] for c in STATIC_EXPERT_CASES])
+def test_dispatch_static_per_expert_parity(case):
+    """Static int8 with one scale row per expert: whole receive buffers equal
+    the oracle's, sentinels included; copies of a token to different experts
+    carry different codes."""
+    name, T, H, K, E, R, a, dup, drop = case
+    print(f"[static-expert] {name}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    idx, wts = _routing(rng, T, K, E, dup=dup, drop=drop)
+    x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    scales = rng.uniform(10.0, 90.0, size=(E, H)).astype(np.float32)
+    ol = oracle.layout(idx, E, R, a)
+    cap = ol.recv_capacity
+    orx, orw = oracle.dispatch_static_expert(x_bits, idx, ol.token_row, cap, scales, wts,
+                                             recv_x=np.full((cap, H), 0x55, np.int8), with_weights=True)
+    lay = gpu_layout(idx, E, R, a)
+    rx = torch.full((cap, H), 0x55, dtype=torch.int8, device=DEV)
+    rw = torch.full((cap,), -3.0, device=DEV)
+    moe.moe_dispatch_static_per_expert(bf16_dev(x_bits), lay, torch.from_numpy(idx).to(DEV),
+                                       torch.from_numpy(scales).to(DEV), torch.from_numpy(wts).to(DEV),
+                                       recv_x=rx, recv_weights=rw)
+    np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+    used = ol.recv_src >= 0
+    np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
+    assert (rw.cpu().numpy()[~used] == -3.0).all()
+    if drop < 1.0 and K > 1 and E > 1:
+        r0, r1 = ol.token_row[:, 0], ol.token_row[:, 1]
+        both = (r0 >= 0) & (r1 >= 0) & (idx[:, 0] != idx[:, 1])
+        assert any(not np.array_equal(orx[a_], orx[b_]) for a_, b_ in zip(r0[both], r1[both]))
+
+
+def test_dispatch_static_per_expert_int8_workload_full():
+    """The per-token int8 workload's shape (8192 x 7168, 256 experts over 16
+    ranks, top-8 Zipf, alignment 128) with per-expert scale rows: every row of
+    the receive buffer (98048 x 7168 codes) against the oracle."""
+    w = W.BY_NAME["int8_static_expert_8192x7168_e256_top8_zipf"]
+    print(f"[static-expert] {w.name}", flush=True)
+    inp = W.generate(w)
+    scales = W.expert_scales(w)
+    ol = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    cap = ol.recv_capacity
+    orx, orw = oracle.dispatch_static_expert(inp.x_bits, inp.topk_idx, ol.token_row, cap, scales,
+                                             inp.topk_weights, recv_x=np.full((cap, w.hidden), 0x55, np.int8),
+                                             with_weights=True)
+    assert (orx == 127).any() and (orx == -128).any()
+    lay = gpu_layout(inp.topk_idx, w.num_experts, w.num_ranks, w.expert_alignment)
+    rx = torch.full((cap, w.hidden), 0x55, dtype=torch.int8, device=DEV)
+    rw = torch.full((cap,), -3.0, device=DEV)
+    moe.moe_dispatch_static_per_expert(bf16_dev(inp.x_bits), lay, torch.from_numpy(inp.topk_idx).to(DEV),
+                                       torch.from_numpy(scales).to(DEV),
+                                       torch.from_numpy(inp.topk_weights).to(DEV), recv_x=rx, recv_weights=rw)
+    np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+    used = ol.recv_src >= 0
+    np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
+
+
 @pytest.mark.parametrize("variant", ["shared", "residual", "shared_residual_norm", "norm_only",
                                      "norm_h16384_k16"])
 def test_combine_fused_parity(variant):
@@ -580,7 +646,7 @@ def test_combine_grid_stride_iterations():
 
 @pytest.mark.parametrize("mode", ["bf16", "int8_token", "e4m3_token", "e5m2_token", "mxfp8_e4m3",
                                   "mxfp8_e5m2", "group_e4m3", "group_e5m2", "static", "static_channel",
-                                  "prequantized"])
+                                  "static_expert", "prequantized"])
 def test_dispatch_grid_stride_iterations(mode):
     """The slice dispatch kernels (unquantised, static, pre-quantised) take
     (token, slice) items beyond their grid cap in later iterations.  The
@@ -623,6 +689,20 @@ def test_dispatch_grid_stride_iterations(mode):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(rd.cpu().numpy(), ord_)
         np.testing.assert_array_equal(rs.cpu().numpy(), ors)
+    elif mode == "static_expert":
+        scales = (rng.random((E, H), dtype=np.float32) * 40 + 1).astype(np.float32)
+        orx = np.full((cap, H), 0x7B, np.int8)
+        orx, orw = oracle.dispatch_static_expert(x_bits, idx, ol.token_row, cap, scales, wts, recv_x=orx,
+                                                 with_weights=True)
+        rx = torch.full((cap, H), 0x7B, dtype=torch.int8, device=DEV)
+        rw = torch.full((cap,), -3.0, device=DEV)
+        sc_dev = torch.from_numpy(scales).to(DEV)
+        idx_dev = torch.from_numpy(idx).to(DEV)
+        assert small.moe_dispatch_static_per_expert(x_dev.data_ptr(), T, H, K, idx_dev.data_ptr(), E,
+                                                    lay.token_row.data_ptr(), w_dev.data_ptr(), cap,
+                                                    sc_dev.data_ptr(), rx.data_ptr(), rw.data_ptr(), st) == 0
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(rx.cpu().numpy(), orx)
     elif mode.startswith("static"):
         n = H if mode == "static_channel" else 1
         scales = (rng.random(n, dtype=np.float32) * 40 + 1).astype(np.float32)
@@ -743,6 +823,15 @@ def test_bench_workload_full_size_sampled(w):
                                                    wts[sample], with_weights=True)
         np.testing.assert_array_equal(rd[take].cpu().numpy()[valid], od[valid])
         np.testing.assert_array_equal(rsc[take].cpu().numpy()[valid], osc[valid])
+    elif w.static_per_expert:
+        sc = W.expert_scales(w)
+        rx = torch.empty((cap, H), dtype=torch.int8, device=DEV)
+        rw = torch.empty(cap, dtype=torch.float32, device=DEV)
+        moe.moe_dispatch_static_per_expert(bf16_dev(x_bits), lay, torch.from_numpy(idx).to(DEV),
+                                           torch.from_numpy(sc).to(DEV), w_dev, recv_x=rx, recv_weights=rw)
+        orx, ow = oracle.dispatch_static_expert(x_bits[sample], idx[sample], sub_rows, rows.size, sc,
+                                                wts[sample], with_weights=True)
+        np.testing.assert_array_equal(rx[take].cpu().numpy()[valid], orx[valid])
     elif w.static_scale > 0:
         sc = np.array([w.static_scale], np.float32)
         rx = torch.empty((cap, H), dtype=torch.int8, device=DEV)
