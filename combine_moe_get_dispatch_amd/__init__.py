@@ -30,6 +30,8 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_CAPACITY = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 QUANT_NONE = 0
 QUANT_INT8_PER_TOKEN = 2
@@ -47,7 +49,7 @@ MX_MODES = (QUANT_MXFP8_E4M3, QUANT_MXFP8_E5M2)
 FLAG_BAD_EXPERT_ID = 1
 
 __all__ = [
-    "moe_get_dispatch_layout", "moe_dispatch", "moe_dispatch_static", "moe_dispatch_static_per_expert",
+    "moe_get_dispatch_layout", "moe_get_dispatch_layout_noalloc", "moe_dispatch", "moe_dispatch_static", "moe_dispatch_static_per_expert",
     "moe_dispatch_prequantized",
     "moe_combine", "moe_combine_fused",
     "moe_recv_capacity_bound",
@@ -83,6 +85,8 @@ def declare_signatures(L: ctypes.CDLL) -> ctypes.CDLL:
     L.moe_dispatch.restype = i32
     L.moe_dispatch_static.argtypes = [P, i32, i32, i32, P, P, i64, P, i32, P, P, P]
     L.moe_dispatch_static.restype = i32
+    L.moe_get_dispatch_layout_noalloc.argtypes = [P, i32, i32, i32, i32, i32, i64] + [P] * 8 + [P]
+    L.moe_get_dispatch_layout_noalloc.restype = i32
     L.moe_dispatch_static_per_expert.argtypes = [P, i32, i32, i32, P, i32, P, P, i64, P, P, P, P]
     L.moe_dispatch_static_per_expert.restype = i32
     L.moe_dispatch_prequantized.argtypes = [P, i32, i32, P, i32, i32, P, P, i64, P, P, P, P]
@@ -273,6 +277,27 @@ def moe_get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks:
         *out._layout_ptrs, out.workspace.numel(), _stream(topk_idx.device))
     if rc != MOE_OK:
         raise MoeError("moe_get_dispatch_layout", rc)
+    return out
+
+
+def moe_get_dispatch_layout_noalloc(topk_idx: torch.Tensor, out: DispatchLayout) -> DispatchLayout:
+    """moe_get_dispatch_layout into the preallocated ``out`` with the
+    library's built-in scratch instead of ``out.workspace``: the call
+    allocates nothing (for graph capture and allocation-free loops).  Calls
+    that overlap on one GPU share that scratch and must not run at the same
+    time.  Sizes needing more than NOALLOC_SCRATCH_BYTES of workspace raise."""
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [num_tokens, num_topk]")
+    T, K = topk_idx.shape
+    _check(topk_idx, "topk_idx", torch.int64)
+    if (out.num_tokens, out.num_topk) != (T, K):
+        raise ValueError("preallocated layout was made for other sizes")
+    _check_layout(out, topk_idx.device)
+    rc = lib().moe_get_dispatch_layout_noalloc(
+        _ptr(topk_idx), T, K, out.num_experts, out.num_ranks, out.expert_alignment, out.recv_capacity,
+        *out._layout_ptrs[:8], _stream(topk_idx.device))
+    if rc != MOE_OK:
+        raise MoeError("moe_get_dispatch_layout_noalloc", rc)
     return out
 
 

@@ -11,10 +11,53 @@
 
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 using namespace moe;
 
+// Layout workspace of moe_get_dispatch_layout_noalloc, for callers that
+// cannot allocate.  One copy per GPU, held until the process ends; every
+// call on a GPU shares it (calls that overlap on one GPU race).  The host
+// name of the array is not a device address: kernels get the address that
+// hipGetSymbolAddress reports for the GPU they run on.
+static __device__ __align__(256) int32_t scratch[MOE_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+
 namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices]; // device address of `scratch` per GPU, found on first use
+
+// Device address of `scratch` on the GPU `stream` belongs to (NULL on a HIP
+// error).  Looked up once per GPU, with that GPU current.
+void *scratch_for_stream(hipStream_t stream)
+{
+    int dev = -1;
+    if (stream == nullptr) {
+        if (hipGetDevice(&dev) != hipSuccess)
+            return nullptr;
+    } else if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int prev = -1;
+        if (hipGetDevice(&prev) != hipSuccess)
+            return nullptr;
+        if (prev != dev && hipSetDevice(dev) != hipSuccess)
+            return nullptr;
+        void *p = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (prev != dev && hipSetDevice(prev) != hipSuccess)
+            return nullptr;
+        if (err != hipSuccess || p == nullptr)
+            return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -121,6 +164,55 @@ int moe_get_dispatch_layout(const int64_t *topk_idx, int num_tokens, int num_top
     args.recv_src = recv_src;
     args.error_flag = error_flag;
     args.workspace = (int32_t *)workspace;
+    return launch_layout(args, plan, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_get_dispatch_layout_noalloc(const int64_t *topk_idx, int num_tokens, int num_topk,
+                                    int num_experts, int num_ranks, int expert_alignment,
+                                    int64_t recv_capacity, int32_t *num_tokens_per_rank,
+                                    int32_t *num_tokens_per_expert, int32_t *is_token_in_rank,
+                                    int32_t *num_recv_tokens_per_expert, int32_t *expert_offsets,
+                                    int32_t *token_row, int32_t *recv_src, int32_t *error_flag,
+                                    hipStream_t stream)
+{
+    const int T = num_tokens, K = num_topk, E = num_experts, R = num_ranks, a = expert_alignment;
+    int rc = check_layout_sizes(T, K, E, R, a, recv_capacity);
+    if (rc != MOE_OK)
+        return rc;
+    if (!num_tokens_per_rank || !num_tokens_per_expert || !num_recv_tokens_per_expert ||
+        !expert_offsets || !error_flag)
+        return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!topk_idx || !is_token_in_rank || !token_row))
+        return MOE_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && !recv_src)
+        return MOE_ERR_INVALID_ARG;
+    const LayoutPlan plan = plan_layout(T, K, E, R);
+    if (plan.workspace_bytes > MOE_NOALLOC_SCRATCH_BYTES)
+        return MOE_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (plan.workspace_bytes > 0) {
+        ws = scratch_for_stream(stream);
+        if (ws == nullptr)
+            return MOE_ERR_HIP;
+    }
+
+    LayoutArgs args;
+    args.topk_idx = topk_idx;
+    args.T = T;
+    args.K = K;
+    args.E = E;
+    args.R = R;
+    args.a = a;
+    args.cap = recv_capacity;
+    args.ntpr = num_tokens_per_rank;
+    args.ntpe = num_tokens_per_expert;
+    args.itr = is_token_in_rank;
+    args.nrtpe = num_recv_tokens_per_expert;
+    args.off = expert_offsets;
+    args.token_row = token_row;
+    args.recv_src = recv_src;
+    args.error_flag = error_flag;
+    args.workspace = (int32_t *)ws;
     return launch_layout(args, plan, stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -352,6 +444,9 @@ const char *moe_status_string(int status)
         return "layout workspace missing, misaligned or too small";
     case MOE_ERR_HIP:
         return "HIP kernel launch failed";
+    case MOE_ERR_SCRATCH:
+        return "these sizes need more layout workspace than the built-in scratch buffer holds "
+               "(MOE_NOALLOC_SCRATCH_BYTES); use moe_get_dispatch_layout with a workspace";
     default:
         return "unknown status";
     }

@@ -66,6 +66,7 @@ extern "C" {
 #define MOE_ERR_CAPACITY (-2)    /* recv_capacity below moe_recv_capacity_bound()  */
 #define MOE_ERR_WORKSPACE (-3)   /* workspace missing, misaligned or too small      */
 #define MOE_ERR_HIP (-4)         /* a HIP launch failed                            */
+#define MOE_ERR_SCRATCH (-5)     /* sizes beyond moe_get_dispatch_layout_noalloc's scratch */
 
 /* Quantisation modes.  The low 4 bits are quantMode of the CANN page's Formula
  * (0 none, 2 per-token dynamic, 4 MX); bits 4-7 select the destination type
@@ -326,6 +327,31 @@ int moe_combine_fused(const void *expert_out, int64_t recv_capacity, int num_tok
                       int num_topk, const int32_t *token_row, const float *topk_weights,
                       const void *shared_out, const void *residual, const void *rms_weight,
                       float rms_eps, void *out, void *out_norm, hipStream_t stream);
+
+/*
+ * moe_get_dispatch_layout without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, allocation-free serving loops, harnesses that forbid
+ * hipMalloc).  The layout's workspace is a scratch array built into the
+ * library, MOE_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU, held from the first call
+ * on a GPU until the process ends.  Sizes whose workspace
+ * (moe_layout_workspace_bytes) exceeds it return MOE_ERR_SCRATCH before any
+ * HIP call.  Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (different streams, or different host threads) race
+ * and give wrong results; serialise them, or use moe_get_dispatch_layout
+ * with a workspace each.  The array needs no clearing between calls.
+ * Arguments, outputs and other errors as for moe_get_dispatch_layout; the
+ * outputs are bit-identical to it.  MOE_ERR_HIP also reports a failure to
+ * find the array's device address on the stream's GPU.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_get_dispatch_layout_noalloc(const int64_t *topk_idx, int num_tokens, int num_topk,
+                                    int num_experts, int num_ranks, int expert_alignment,
+                                    int64_t recv_capacity, int32_t *num_tokens_per_rank,
+                                    int32_t *num_tokens_per_expert, int32_t *is_token_in_rank,
+                                    int32_t *num_recv_tokens_per_expert, int32_t *expert_offsets,
+                                    int32_t *token_row, int32_t *recv_src, int32_t *error_flag,
+                                    hipStream_t stream);
 
 /*
  * 1 if moe_layout_and_dispatch takes a batch of these sizes, else 0:

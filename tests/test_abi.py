@@ -62,8 +62,41 @@ def test_capacity_and_workspace_queries(L, orc):
 
 
 def test_status_strings(L):
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(L.moe_status_string(code), bytes)
+    assert b"scratch" in L.moe_status_string(-5)
+
+
+def test_noalloc_layout_host_rules(L, orc):
+    """moe_get_dispatch_layout_noalloc: the layout's argument rules, and sizes
+    whose workspace exceeds the built-in scratch rejected on the host."""
+    import combine_moe_get_dispatch_amd as m
+    f = L.moe_get_dispatch_layout_noalloc
+
+    def call(T, K, E, R, a=1, cap=None, outs=None):
+        cap = orc.recv_capacity_bound(T, K, E, a) if cap is None else cap
+        outs = [BAD] * 8 if outs is None else outs
+        return f(BAD, T, K, E, R, a, cap, *outs, None)
+
+    assert L.moe_layout_workspace_bytes(65536, 16, 512, 512) > m.NOALLOC_SCRATCH_BYTES
+    assert call(65536, 16, 512, 512) == m.MOE_ERR_SCRATCH
+    assert L.moe_layout_workspace_bytes(32768, 16, 512, 512) <= m.NOALLOC_SCRATCH_BYTES
+    assert call(100, 17, 16, 4) == -1                      # K
+    assert call(100, 4, 16, 3) == -1                       # ranks do not divide experts
+    assert call(100, 4, 16, 4, cap=10) == -2               # capacity below the bound
+    assert call(100, 4, 16, 4, outs=[None] + [BAD] * 7) == -1
+    assert call(100, 4, 16, 4, outs=[BAD] * 6 + [None, BAD]) == -1
+
+
+def test_noalloc_layout_source_allocates_nothing():
+    """The no-allocation entry point and its scratch lookup call no allocating
+    HIP routine (the whole C-ABI file holds none)."""
+    src = open(os.path.join(ROOT, "combine_moe_get_dispatch_amd", "csrc", "moe_api.hip")).read()
+    code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", src, flags=re.S)
+    for name in ("hipMalloc", "hipFree", "hipHostMalloc", "hipMallocAsync", "hipMallocManaged",
+                 "hipExtMallocWithFlags", "malloc(", "new "):
+        assert name not in code, name
+    assert "hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))" in code
 
 
 BAD = ctypes.c_void_p(0x1000)   # never dereferenced: every call below is rejected on the host
