@@ -42,16 +42,24 @@
 
 namespace moe {
 
-constexpr int kCountThreads = 1024;
 constexpr int kRankThreads = 1024;
 constexpr int kRankWaves = kRankThreads / kWave;
-constexpr int kCountWaves = kCountThreads / kWave;
 constexpr int kIdxPerThread = kMaxChunkEntries / 1024; // topk_idx entries prefetched per thread
 constexpr int kRankCellsPerThread = 2; // per-chunk rank counts prefetched per thread
 constexpr int kRankSumSlots = 512;     // ranks one workgroup can sum (R <= 512)
 constexpr int kTabRows = 16;           // expert-table rows prefetched per thread
 
-static_assert(kCountThreads == 1024 && kRankThreads == 1024, "prefetch sizes assume 1024 threads");
+static_assert(kRankThreads == 1024, "prefetch sizes assume 1024 threads");
+
+// Workgroup size of the count kernel for chunks of at most `ne_max` entries:
+// one entry per thread up to 1024 entries (a wave per 64 entries, at least
+// four waves), 1024 threads and several entries per thread beyond.  Extra
+// idle waves only lengthen the launch of the 64-odd workgroups.
+inline int count_threads(int ne_max)
+{
+    const int t = (ne_max + kWave - 1) / kWave * kWave;
+    return t <= 256 ? 256 : t <= 512 ? 512 : 1024;
+}
 static_assert(kMaxChunkEntries <= 65536 && MOE_MAX_EXPERTS <= 32768,
               "packed (expert << 16 | rank) entries between the count and rank kernels");
 
@@ -80,11 +88,15 @@ __device__ __forceinline__ int exclusive_scan16(int v, int *total)
     return incl - v;
 }
 
-__global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void layout_count_kernel(
     const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int L, int tpc, int nbits,
     int32_t *__restrict__ itr, int32_t *__restrict__ cnt_tab, int32_t *__restrict__ rank_tab,
     int32_t *__restrict__ flag_tab, int32_t *__restrict__ token_row)
 {
+    constexpr int kCountThreads = THREADS;
+    constexpr int kCountWaves = THREADS / kWave;
+    // a chunk's entries fit in kIdxPerThread vectors per wave (count_threads)
     __shared__ int s_w[kCountWaves * MOE_MAX_EXPERTS]; // [wave][e], row stride E
     __shared__ int s_rcnt[MOE_MAX_EXPERTS];
     __shared__ uint8_t s_flags[kMaxChunkFlags];
@@ -181,19 +193,31 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     // rank r of tokens part, part + parts, ...; a wave's stores cover
     // consecutive (token, rank) cells, and each thread adds its count once
     {
-        const int parts = kCountThreads / R; // >= 2 (R <= 512)
-        if (tid < parts * R) {
-            const int r = tid % R;
-            const int part = tid / R;
-            int32_t *itr_chunk = itr + (int64_t)t0 * R;
-            int cnt = 0;
-            for (int t = part; t < nt; t += parts) {
-                const int f = s_flags[t * R + r];
-                itr_chunk[t * R + r] = f;
-                cnt += f;
+        int32_t *itr_chunk = itr + (int64_t)t0 * R;
+        if (R <= kCountThreads) {
+            const int parts = kCountThreads / R;
+            if (tid < parts * R) {
+                const int r = tid % R;
+                const int part = tid / R;
+                int cnt = 0;
+                for (int t = part; t < nt; t += parts) {
+                    const int f = s_flags[t * R + r];
+                    itr_chunk[t * R + r] = f;
+                    cnt += f;
+                }
+                if (cnt)
+                    atomicAdd(&s_rcnt[r], cnt);
             }
-            if (cnt)
-                atomicAdd(&s_rcnt[r], cnt);
+        } else { // more ranks than threads: thread tid owns ranks tid, tid + THREADS, ...
+            for (int r = tid; r < R; r += kCountThreads) {
+                int cnt = 0;
+                for (int t = 0; t < nt; ++t) {
+                    const int f = s_flags[t * R + r];
+                    itr_chunk[t * R + r] = f;
+                    cnt += f;
+                }
+                s_rcnt[r] = cnt;
+            }
         }
     }
     __syncthreads();
@@ -277,6 +301,9 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     __shared__ int s_off[MOE_MAX_EXPERTS + 1];
     __shared__ int s_rsum[kRankSumSlots];
     __shared__ int s_flag;
+    __shared__ int4 s_pall[kRankThreads]; // table threads' column sums, slot part * groups + g
+    __shared__ int4 s_pbef[kRankThreads]; // the same over the rows before this chunk
+    __shared__ int s_wsum[kRankWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -311,7 +338,8 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     const int g = tid % groups;
     const int part = tid / groups;
     const bool scanned = tot_tab != nullptr; // the scan launch left totals and this chunk's prefix row
-    const bool tab_thread = tid < parts * groups && !scanned;
+    const bool tab_parts_ready = !scanned && nchunks > 0; // the partial sums below hold the table
+    const bool tab_thread = tid < parts * groups && tab_parts_ready;
     const int rb = scanned ? 0 : min(kTabRows, (nchunks + parts - 1) / parts); // rows per thread and pass (uniform)
     const int4 *tab4 = (const int4 *)cnt_tab;
     int4 tab_reg[kTabRows];
@@ -344,34 +372,26 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     }
 
     // (1) expert totals over all chunks, and the part of them in chunks
-    // before this one; this workgroup's rank sums
-    for (int e = tid; e < E; e += kRankThreads) {
-        s_tot[e] = 0;
-        s_cb[e] = 0;
-    }
+    // before this one: each table thread's sums of the rows it read (all of
+    // them, and those before this chunk) go to LDS, and thread e then adds
+    // the parts of expert e (no atomics: 16 parts per column at E = 256)
     for (int i = tid; i < kRankSumSlots; i += kRankThreads)
         s_rsum[i] = 0;
     if (tid == 0)
         s_flag = 0;
-    __syncthreads();
-
-    if (scanned && tid < E) {
-        s_tot[tid] = tot_reg;
-        s_cb[tid] = cb_reg;
-    }
-    if (tab_thread && nchunks > 0) {
-        int all[4] = {0, 0, 0, 0}, before[4] = {0, 0, 0, 0};
+    if (tab_thread) {
+        int4 all = int4{0, 0, 0, 0}, before = int4{0, 0, 0, 0};
         auto add_row = [&](int r, const int4 v) {
             const int keep = r < nchunks ? 1 : 0;
             const int early = r < chunk ? keep : 0;
-            all[0] += keep * v.x;
-            all[1] += keep * v.y;
-            all[2] += keep * v.z;
-            all[3] += keep * v.w;
-            before[0] += early * v.x;
-            before[1] += early * v.y;
-            before[2] += early * v.z;
-            before[3] += early * v.w;
+            all.x += keep * v.x;
+            all.y += keep * v.y;
+            all.z += keep * v.z;
+            all.w += keep * v.w;
+            before.x += early * v.x;
+            before.y += early * v.y;
+            before.z += early * v.z;
+            before.w += early * v.w;
         };
 #pragma unroll
         for (int u = 0; u < kTabRows; ++u)
@@ -379,17 +399,12 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
                 add_row(part * rb + u, tab_reg[u]);
         for (int r = parts * rb + part; r < nchunks; r += parts) // only for very many chunks
             add_row(r, tab4[(int64_t)r * groups + g]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int e = 4 * g + c;
-            if (e < E) {
-                if (all[c])
-                    atomicAdd(&s_tot[e], all[c]);
-                if (before[c])
-                    atomicAdd(&s_cb[e], before[c]);
-            }
-        }
+        s_pall[tid] = all; // slot part * groups + g
+        s_pbef[tid] = before;
     }
+    __syncthreads();
+
+    // this workgroup's rank sums and the error flags
 #pragma unroll
     for (int u = 0; u < kRankCellsPerThread; ++u) {
         const int cell = tid + u * kRankThreads;
@@ -401,35 +416,47 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
                   rank_tab[(int64_t)(cell % nchunks) * R + chunk + (cell / nchunks) * nblocks]);
     if (flag_reg)
         atomicOr(&s_flag, flag_reg);
-    __syncthreads();
 
-    // (2) aligned counts and their exclusive prefix sum ("/" is integer
-    // division, CANN page Constraint 11), by the first wave alone: lane l
-    // takes experts [l * per, (l + 1) * per), sums their aligned counts, and
-    // a shuffle scan over the 64 lane sums gives every lane its base.  No
-    // overflow: the host checked T*K + E*(a-1) < 2^31.
-    if (tid < kWave) {
-        const int per = (E + kWave - 1) / kWave; // <= 8
-        const int e0 = lane * per;
-        int sum = 0;
-        for (int c = 0; c < per; ++c)
-            if (e0 + c < E)
-                sum += ((s_tot[e0 + c] + a - 1) / a) * a;
-        int incl = sum;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int v = __shfl_up(incl, d, kWave);
-            if (lane >= d)
-                incl += v;
-        }
-        int run = incl - sum;
-        for (int c = 0; c < per; ++c)
-            if (e0 + c < E) {
-                s_off[e0 + c] = run;
-                run += ((s_tot[e0 + c] + a - 1) / a) * a;
+    // (2) expert tid's total, its aligned count ("/" is integer division,
+    // CANN page Constraint 11) and their exclusive prefix sum over the
+    // experts: a shuffle scan in each wave, then the waves' totals through
+    // LDS.  No overflow: the host checked T*K + E*(a-1) < 2^31.
+    int tot = 0, ac = 0;
+    if (tid < E) {
+        int cb = 0;
+        if (scanned) {
+            tot = tot_reg;
+            cb = cb_reg;
+        } else if (tab_parts_ready) {
+            const int *pa = (const int *)s_pall;
+            const int *pb = (const int *)s_pbef;
+            const int col = (tid >> 2) * 4 + (tid & 3);
+            for (int p = 0; p < parts; ++p) {
+                tot += pa[p * 4 * groups + col];
+                cb += pb[p * 4 * groups + col];
             }
-        if (lane == kWave - 1)
-            s_off[E] = incl;
+        }
+        s_tot[tid] = tot;
+        s_cb[tid] = cb;
+        ac = a == 1 ? tot : ((tot + a - 1) / a) * a;
+    }
+    int incl = ac;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int v = __shfl_up(incl, d, kWave);
+        if (lane >= d)
+            incl += v;
+    }
+    if (lane == kWave - 1)
+        s_wsum[tid / kWave] = incl;
+    __syncthreads();
+    if (tid < E) {
+        int run = 0;
+        for (int w = 0; w < tid / kWave; ++w)
+            run += s_wsum[w];
+        s_off[tid] = run + incl - ac;
+        if (tid == E - 1)
+            s_off[E] = run + incl;
     }
     __syncthreads();
 
@@ -713,10 +740,13 @@ hipError_t launch_layout(const LayoutArgs &A, const LayoutPlan &P, hipStream_t s
     int32_t *cb_tab = P.scan ? flag_tab + nchunks : nullptr;
     int32_t *tot_tab = P.scan ? cb_tab + (size_t)nchunks * Ep : nullptr;
     if (nchunks > 0) {
-        hipError_t err = launch_kernel(
-            layout_count_kernel, dim3(nchunks), dim3(kCountThreads), 0, stream, A.topk_idx, A.T,
-            A.K, A.E, A.R, L, P.tokens_per_chunk, nbits, A.itr, cnt_tab, rank_tab, flag_tab,
-            A.token_row);
+        const int threads = count_threads(P.tokens_per_chunk * A.K);
+        auto kern = threads == 256   ? layout_count_kernel<256>
+                    : threads == 512 ? layout_count_kernel<512>
+                                     : layout_count_kernel<1024>;
+        hipError_t err = launch_kernel(kern, dim3(nchunks), dim3(threads), 0, stream, A.topk_idx,
+                                       A.T, A.K, A.E, A.R, L, P.tokens_per_chunk, nbits, A.itr,
+                                       cnt_tab, rank_tab, flag_tab, A.token_row);
         if (err != hipSuccess)
             return err;
         if (P.scan) {
