@@ -148,6 +148,27 @@ def counter_traffic(workload: str, stage: str):
         return None
 
 
+def profiled_stage_us(workload: str, stage: str):
+    """Average kernel time of one call of `stage` over the timed steps, from
+    the committed rocprofv3 kernel statistics of this workload
+    (profiles/<workload>_kernel_stats.txt), or None when there are none or
+    the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_kernel_stats.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get(f"source_sha256_{stage}") != kernel_source_sha(stage):
+        return None
+    try:
+        return float(kv[f"stage_timed_avg_us_{stage}"])
+    except (KeyError, ValueError):
+        return None
+
+
 class StageEvents:
     """Timing events on torch's current stream.  Uses HIP events created with
     hipEventDisableSystemFence through the HIP runtime torch already loaded;
@@ -484,6 +505,7 @@ def main():
 
     dom = max(("dispatch", "combine"), key=lambda k: avg_us[k])
     achieved = sb[dom] / (avg_us[dom] * 1e-6) / 1e9
+    prof_us = profiled_stage_us(w.name, dom)
 
     if not args.no_check:
         # cheap sanity check after timing: every dispatched row is its token
@@ -551,7 +573,12 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic(w.name, dom),
                      "algorithmic_bytes_per_launch": sb[dom],
-                     "avg_launch_us": round(avg_us[dom], 2)},
+                     "avg_launch_us": round(avg_us[dom], 2),
+                     "event_samples": len(events),
+                     "profiled_avg_launch_us": prof_us,
+                     "profiled_frac": (round(sb[dom] / (prof_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                       if prof_us else None),
+                     "profile": f"profiles/{w.name}_kernel_stats.txt" if prof_us else None},
         "cpu_baseline": cpu,
     }
     if cold is not None:
