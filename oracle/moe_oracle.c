@@ -276,11 +276,15 @@ static float bf16_to_f32(uint16_t b)
  * 3 mantissa bits, no infinities, 0x7F/0xFF are NaN, largest finite value
  * 1.75 * 2^8 = 448, smallest normal 2^-6, subnormals are multiples of 2^-9.
  * Rounding is to nearest, ties to even (the default IEEE mode); magnitudes
- * above 448 saturate to 448 (the "fn" format has no infinity).  The sign of
- * zero is kept.  Computed in double, where every step below is exact except
- * the one explicit rounding. */
+ * above 448 saturate to 448 (the "fn" format has no infinity), infinities
+ * included.  The sign of zero is kept.  A NaN input gives the format's NaN
+ * code 0x7F, whatever its sign bit (reading: the pages do not cover NaN; the
+ * sign of a NaN that arithmetic produces is not defined).  Computed in
+ * double, where every step below is exact except the one explicit rounding. */
 uint8_t oracle_cast_to_fp8_e4m3fn(double v)
 {
+    if (isnan(v))
+        return 0x7F;
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
     double a = fabs(v);
     if (a > 448.0)
@@ -315,9 +319,12 @@ void oracle_cast_to_fp8_e4m3fn_array(const float *v, int64_t n, uint8_t *out)
  * smallest normal 2^-14, subnormals are multiples of 2^-16.  Round to
  * nearest, ties to even.  The format has infinities, but a quantiser that
  * sends a finite input to infinity loses it, so magnitudes above 57344
- * saturate to 57344, as for e4m3fn (reading).  Zero keeps its sign. */
+ * saturate to 57344, as for e4m3fn (reading), infinities included.  Zero
+ * keeps its sign; NaN gives the NaN code 0x7F, as for e4m3fn. */
 uint8_t oracle_cast_to_fp8_e5m2(double v)
 {
+    if (isnan(v))
+        return 0x7F;
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
     double a = fabs(v);
     if (a > 57344.0)
@@ -363,7 +370,12 @@ static int fp8_emax(int fmt) { return fmt == FMT_E5M2 ? 15 : 8; }
  *   scale out     = 1.0 / dynamicScales
  * all in fp32.  Reading for the degenerate row: when dynamicScales is not
  * finite (an all-zero row, or a maximum so small that 127/max overflows) the
- * codes are 0 and the scale is 1.0/dynamicScales = 0. */
+ * codes are 0 and the scale is 1.0/dynamicScales = 0.
+ * Readings for non-finite inputs (the pages do not cover them): IEEE fp32
+ * arithmetic is carried through.  NaN elements take no part in the maximum
+ * (as fmaxf), and CastToInt8 of NaN is 0.  A row holding an infinity has
+ * maximum +inf, dynamicScales 0, scale +inf, and codes 0 (finite * 0 = 0,
+ * inf * 0 = NaN). */
 static void quant_int8_row(const uint16_t *x, int H, int8_t *quantOut, float *scale_out)
 {
     float maxabs = 0.0f;
@@ -383,7 +395,7 @@ static void quant_int8_row(const uint16_t *x, int H, int8_t *quantOut, float *sc
             float xFp32 = bf16_to_f32(x[h]);
             float prod = xFp32 * dynamicScales; /* one fp32 multiply */
             float q = rintf(prod);              /* ties to even */
-            quantOut[h] = (int8_t)q;
+            quantOut[h] = isnan(q) ? 0 : (int8_t)q;
         }
     }
     *scale_out = 1.0f / dynamicScales;
@@ -398,7 +410,11 @@ static void quant_int8_row(const uint16_t *x, int H, int8_t *quantOut, float *sc
  * Readings: the block maximum is taken of |x|; sharedExp is clamped below at
  * -127, the smallest exponent an e8m0 byte holds, and an all-zero block uses
  * -127; the stored float8_e8m0fnu scale is 2^sharedExp, i.e. the byte
- * sharedExp + 127, so that x ~= code * 2^sharedExp. */
+ * sharedExp + 127, so that x ~= code * 2^sharedExp.
+ * Non-finite inputs (readings): NaN elements take no part in the maximum; a
+ * block whose maximum is +inf has sharedExp = +inf, stored as the e8m0 NaN
+ * byte 0xFF, and its elements are divided by 2^+inf = +inf (finite ones give
+ * signed zeros, infinite ones NaN).  The casts then apply (NaN -> 0x7F). */
 static void quant_mx_row(const uint16_t *x, int H, int fmt, uint8_t *quantOut, uint8_t *scales_out)
 {
     const int emax = fp8_emax(fmt);
@@ -409,6 +425,12 @@ static void quant_mx_row(const uint16_t *x, int H, int fmt, uint8_t *quantOut, u
             double ab = fabs((double)bf16_to_f32(xb[j]));
             if (ab > maxabs)
                 maxabs = ab;
+        }
+        if (isinf(maxabs)) {
+            for (int j = 0; j < 32; ++j)
+                quantOut[32 * blk + j] = cast_to_fp8(fmt, (double)bf16_to_f32(xb[j]) / INFINITY);
+            scales_out[blk] = 0xFF;
+            continue;
         }
         int sharedExp = -127;
         if (maxabs > 0.0) {
@@ -492,13 +514,16 @@ static void quant_fp8_pergroup_row(const uint16_t *x, int H, int fmt, uint8_t *q
  *   xFp32    = CastToFp32(X) * scales     (fp32 multiply)
  *   quantOut = Cast(xFp32, INT8)
  * Reading: the cast rounds half to even and saturates to [-128, 127] (a
- * static scale does not bound the product as the dynamic modes do). */
+ * static scale does not bound the product as the dynamic modes do); a NaN
+ * product casts to 0, as in the dynamic modes. */
 static void quant_static_int8_row(const uint16_t *x, int H, const float *scales, int num_scales,
                                   int8_t *quantOut)
 {
     for (int h = 0; h < H; ++h) {
         float xFp32 = bf16_to_f32(x[h]) * scales[num_scales == 1 ? 0 : h];
         float r = rintf(xFp32);
+        if (isnan(r))
+            r = 0.0f;
         if (r > 127.0f)
             r = 127.0f;
         if (r < -128.0f)

@@ -21,6 +21,10 @@ int oracle_dispatch(const uint16_t *x, int T, int H, int K, const int32_t *token
 int oracle_dispatch_static(const uint16_t *x, int T, int H, int K, const int32_t *token_row,
                            const float *topk_weights, int64_t cap, const float *scales,
                            int num_scales, int8_t *recv_x, float *recv_weights);
+int oracle_dispatch_static_expert(const uint16_t *x, int T, int H, int K, const int64_t *topk_idx,
+                                  int E, const int32_t *token_row, const float *topk_weights,
+                                  int64_t cap, const float *scales, int8_t *recv_x,
+                                  float *recv_weights);
 int oracle_dispatch_prequantized(const uint8_t *data, int T, int row_bytes, const uint8_t *scales,
                                  int scale_bytes, int K, const int32_t *token_row,
                                  const float *topk_weights, int64_t cap, uint8_t *recv_data,
@@ -89,6 +93,14 @@ static void run_case(int T, int K, int E, int R, int a, int H)
         x[i] = rand_bf16();
     if (T > 0)
         memset(x, 0, 2 * (size_t)H); /* an all-zero row */
+    if (T > 3) { /* non-finite elements: NaN with a finite maximum, +-inf, an all-NaN row */
+        x[(size_t)H + 1] = 0x7FC0;
+        x[2 * (size_t)H + 3] = 0x7F80;
+        x[2 * (size_t)H + 4] = 0xFFC1;
+        x[3 * (size_t)H] = 0xFF80;
+        for (int h = 0; h < H; ++h)
+            x[(size_t)(T - 1) * H + h] = 0x7FC0;
+    }
     const int modes[] = {0, 2, 4, 0x12, 0x22, 0x24, 0x13, 0x23};
     for (size_t m = 0; m < sizeof modes / sizeof modes[0]; ++m) {
         const int q = modes[m];
@@ -117,6 +129,17 @@ static void run_case(int T, int K, int E, int R, int a, int H)
         free(sc);
         if (H == 1)
             break;
+    }
+    {
+        float *sc = xmalloc(4 * (size_t)E * H);
+        for (int64_t i = 0; i < (int64_t)E * H; ++i)
+            sc[i] = 0.25f + (float)(next_u64() % 200);
+        int8_t *rx = xmalloc((size_t)cap * H);
+        float *rw = xmalloc(4 * (size_t)cap);
+        CHECK(oracle_dispatch_static_expert(x, T, H, K, idx, E, row, w, cap, sc, rx, rw));
+        free(rx);
+        free(rw);
+        free(sc);
     }
     {
         const int rb = H, sb = H / 32;

@@ -24,7 +24,7 @@ SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 
 LAYOUT = ["tests/test_oracle_layout.py", "tests/test_oracle_rules.py"]
 CODECS = ["tests/test_oracle_quant.py", "tests/test_oracle_fp8.py", "tests/test_oracle_group_static.py",
-          "tests/test_oracle_mx_exhaustive.py"]
+          "tests/test_oracle_mx_exhaustive.py", "tests/test_oracle_nonfinite.py"]
 COMBINE = ["tests/test_oracle_combine.py", "tests/test_oracle_combine_fused.py"]
 ALL = LAYOUT + CODECS + COMBINE
 
@@ -98,6 +98,13 @@ MUTANTS = [
      "for (int h = g0; h < g0 + n - 1; ++h) {\n            float ab"),
     ("static int8 saturates at -127", CODECS,
      "if (r < -128.0f)\n            r = -128.0f;", "if (r < -127.0f)\n            r = -127.0f;"),
+    ("e4m3 NaN encoded as the largest finite value", CODECS,
+     "    if (isnan(v))\n        return 0x7F;\n    uint8_t sign = signbit(v) ? 0x80 : 0x00;\n    double a = fabs(v);\n    if (a > 448.0)",
+     "    if (isnan(v))\n        return 0x7E;\n    uint8_t sign = signbit(v) ? 0x80 : 0x00;\n    double a = fabs(v);\n    if (a > 448.0)"),
+    ("MX block with an infinite maximum stores byte 254", CODECS,
+     "            scales_out[blk] = 0xFF;", "            scales_out[blk] = 0xFE;"),
+    ("per-token int8 NaN code -128", CODECS,
+     "quantOut[h] = isnan(q) ? 0 : (int8_t)q;", "quantOut[h] = isnan(q) ? -128 : (int8_t)q;"),
     ("per-expert static scales taken by k, not by expert", CODECS,
      "quant_static_int8_row(x + (int64_t)t * H, H, scales + e * H, H,",
      "quant_static_int8_row(x + (int64_t)t * H, H, scales + (int64_t)k * H, H,"),

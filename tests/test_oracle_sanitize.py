@@ -1,8 +1,9 @@
 """The oracle under AddressSanitizer and UndefinedBehaviorSanitizer (host code
 only): a C program runs every entry point on small seeded inputs with exactly
 sized buffers, including an empty batch, one token, 512 experts with top-16,
-alignment larger than every count, out-of-range expert ids and all quant
-modes."""
+alignment larger than every count, out-of-range expert ids, all quant modes
+and rows holding NaN and infinities (float-to-integer conversions are checked
+too: -fsanitize=float-cast-overflow)."""
 import os
 import shutil
 import subprocess
@@ -21,7 +22,7 @@ def test_oracle_under_asan_and_ubsan():
     with tempfile.TemporaryDirectory() as d:
         exe = os.path.join(d, "oracle_sanitize")
         cmd = [gcc, "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off",
-               "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+               "-fsanitize=address,undefined,float-cast-overflow", "-fno-sanitize-recover=all",
                os.path.join(HERE, "oracle_sanitize_main.c"), os.path.join(ROOT, "oracle", "moe_oracle.c"),
                "-lm", "-o", exe]
         b = subprocess.run(cmd, capture_output=True, text=True)
