@@ -207,11 +207,16 @@ template <Dst D> struct MxCodec {
         m = fmaxf(m, __shfl_xor(m, 1, kWave));
         m = fmaxf(m, __shfl_xor(m, 2, kWave));
         // floor(log2 m) is the fp32 exponent field - 127 (any m below 2^-119,
-        // subnormals and 0 included, ends up at the -127 clamp)
+        // subnormals and 0 included, ends up at the -127 clamp).  NaN elements
+        // take no part in the maximum (fmaxf); a block whose maximum is +inf
+        // (exponent field 255) has sharedExp = +inf: scale byte 0xFF and every
+        // element divided by +inf, i.e. multiplied by 0 (finite ones give
+        // signed zeros, infinite and NaN ones NaN)
         const int ebits = (int)((__float_as_uint(m) >> 23) & 0xFFu);
         const int se = max(ebits - 127 - DstTraits<D>::kEmax, -127);
-        const float inv = __uint_as_float((uint32_t)(127 - se) << 23); // 2^-se, normal for se in [-127, 119]
-        aux = (uint32_t)(se + 127);
+        const bool inf_block = ebits == 255;
+        const float inv = inf_block ? 0.0f : __uint_as_float((uint32_t)(127 - se) << 23); // 2^-se, normal for se in [-127, 119]
+        aux = inf_block ? 0xFFu : (uint32_t)(se + 127);
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -272,9 +277,16 @@ template <Dst D> struct GroupCodec {
     }
 };
 
+// Static int8 code of one fp32 product: round half to even, saturate to
+// [-128, 127]; NaN gives 0 (fmaxf alone would turn it into -128).
+__device__ __forceinline__ float static_int8_value(float p)
+{
+    const float r = __builtin_rintf(p);
+    return r == r ? fminf(fmaxf(r, -128.0f), 127.0f) : 0.0f;
+}
+
 // Static int8 codes of 8 bf16 elements with their 8 scales (s_lo: elements
-// 0-3, s_hi: 4-7): one fp32 multiply, round half to even, saturate to
-// [-128, 127].
+// 0-3, s_hi: 4-7): one fp32 multiply each, then static_int8_value.
 __device__ __forceinline__ u32x2 static_int8_codes(const u32x4 xv, const float4 s_lo,
                                                    const float4 s_hi)
 {
@@ -282,8 +294,8 @@ __device__ __forceinline__ u32x2 static_int8_codes(const u32x4 xv, const float4 
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const float lo = fminf(fmaxf(__builtin_rintf(bf16_lo(xv[c]) * sv[2 * c]), -128.0f), 127.0f);
-        const float hi = fminf(fmaxf(__builtin_rintf(bf16_hi(xv[c]) * sv[2 * c + 1]), -128.0f), 127.0f);
+        const float lo = static_int8_value(bf16_lo(xv[c]) * sv[2 * c]);
+        const float hi = static_int8_value(bf16_hi(xv[c]) * sv[2 * c + 1]);
         const uint32_t b = ((uint32_t)(int)lo & 0xFFu) | (((uint32_t)(int)hi & 0xFFu) << 8);
         w[c >> 1] |= b << (16 * (c & 1));
     }

@@ -18,7 +18,9 @@ enum class Dst { Int8, E4M3, E5M2 };
 // to even on the 20 bits below them (a carry out of the mantissa moves into
 // the exponent field through the plain integer add).  `sign` (0 or 0x80)
 // comes from the source element so that -0 and negative values that round
-// to zero keep their sign.
+// to zero keep their sign.  Infinities saturate like any value above 448; a
+// NaN gives the NaN code 0x7F whatever its sign (fminf alone would turn it
+// into 448).
 __device__ __forceinline__ uint32_t e4m3fn_code(float v, uint32_t sign)
 {
     const float a = fminf(fabsf(v), 448.0f);
@@ -31,12 +33,13 @@ __device__ __forceinline__ uint32_t e4m3fn_code(float v, uint32_t sign)
         const uint32_t rem = b & 0xFFFFFu;
         code = base + ((rem > 0x80000u) || (rem == 0x80000u && (base & 1u)) ? 1u : 0u);
     }
-    return code | sign;
+    return v == v ? code | sign : 0x7Fu;
 }
 
 // e5m2 code of an fp32 value: magnitude saturated to 57344; below 2^-14 the
 // number of 2^-16 steps; otherwise exponent field (e + 15) and the top 2
-// mantissa bits, rounded half to even on the 21 bits below them.
+// mantissa bits, rounded half to even on the 21 bits below them.  NaN gives
+// 0x7F, as for e4m3fn.
 __device__ __forceinline__ uint32_t e5m2_code(float v, uint32_t sign)
 {
     const float a = fminf(fabsf(v), 57344.0f);
@@ -49,14 +52,18 @@ __device__ __forceinline__ uint32_t e5m2_code(float v, uint32_t sign)
         const uint32_t rem = b & 0x1FFFFFu;
         code = base + ((rem > 0x100000u) || (rem == 0x100000u && (base & 1u)) ? 1u : 0u);
     }
-    return code | sign;
+    return v == v ? code | sign : 0x7Fu;
 }
 
 template <Dst D> struct DstTraits;
 template <> struct DstTraits<Dst::Int8> {
     static constexpr float kMax = 127.0f;
-    // the product is within +-127 (plus one rounding): the integer fits int8
-    __device__ static uint32_t code(float p, uint32_t) { return (uint32_t)((int)__builtin_rintf(p)) & 0xFFu; }
+    // the product is within +-127 (plus one rounding): the integer fits int8;
+    // a NaN product (an infinite or NaN element) gives code 0
+    __device__ static uint32_t code(float p, uint32_t)
+    {
+        return p == p ? (uint32_t)((int)__builtin_rintf(p)) & 0xFFu : 0u;
+    }
 };
 template <> struct DstTraits<Dst::E4M3> {
     static constexpr float kMax = 448.0f;

@@ -261,6 +261,71 @@ def test_quant_special_rows():
         run_full_case(x, idx, wts, E, 2, 1, quant, max_rel_1e2=False)
 
 
+def _nonfinite_rows(H=256):
+    """bf16 rows holding NaN and infinities: a NaN with a finite maximum, +inf
+    with a NaN, -inf, an all-NaN row, NaN and inf in different 32-blocks and
+    128-groups of one row, and a finite control row."""
+    rng = np.random.default_rng(12)
+    x = W.f32_to_bf16_bits(rng.uniform(-3, 3, (7, H)).astype(np.float32))
+    PINF, NINF, QNAN, NQNAN = 0x7F80, 0xFF80, 0x7FC0, 0xFFC1
+    x[0, 17] = QNAN
+    x[1, 5], x[1, 90] = PINF, QNAN
+    x[2, 200] = NINF
+    x[3, :] = QNAN
+    x[4, 33], x[4, 130], x[4, 131] = PINF, NQNAN, NINF
+    x[5, 255] = PINF
+    return x
+
+
+def test_quant_nonfinite_rows():
+    """NaN and infinities through every quantiser (dynamic modes, static int8
+    with one and per-channel scales, per-expert static, the one-launch
+    per-token path): codes and scales bit-exact against the oracle's
+    readings (NaN elements take no part in a maximum, NaN casts to int8 0 and
+    to the FP8 NaN code 0x7F, an infinite maximum gives scale +inf or the e8m0
+    byte 0xFF)."""
+    x = _nonfinite_rows()
+    T, H = x.shape
+    K, E, R, a = 2, 4, 2, 1
+    idx = np.stack([np.arange(T) % E, (np.arange(T) + 1) % E], axis=1).astype(np.int64)
+    wts = np.full((T, K), 0.5, np.float32)
+    ol = oracle.layout(idx, E, R, a)
+    lay = gpu_layout(idx, E, R, a)
+    cap = ol.recv_capacity
+    x_dev = bf16_dev(x)
+    for quant in (2, 0x12, 0x22, 4, 0x24, 0x13, 0x23):
+        print(f"[nonfinite] mode {quant:#x}", flush=True)
+        orx, ors = oracle_poisoned(cap, H, quant)
+        orx, ors, _ = oracle.dispatch(x, ol.token_row, cap, None, quant, recv_x=orx, recv_scales=ors)
+        rx, rs, _ = poisoned_recv(lay, H, quant)
+        moe.moe_dispatch(x_dev, lay, None, quant, recv_x=rx, recv_scales=rs)
+        np.testing.assert_array_equal(recv_to_host(rx, quant), orx)
+        g = rs.cpu().numpy()
+        if g.dtype == np.float32:
+            np.testing.assert_array_equal(g.view(np.uint32), ors.view(np.uint32))
+        else:
+            np.testing.assert_array_equal(g, ors)
+        if quant in (2, 0x12, 0x22):
+            lay1, rx1, rs1, _ = moe.moe_layout_and_dispatch(torch.from_numpy(idx).to(DEV), x_dev, E, R, a,
+                                                             quant_mode=quant)
+            used = ol.recv_src >= 0
+            np.testing.assert_array_equal(recv_to_host(rx1, quant)[used], orx[used])
+            np.testing.assert_array_equal(rs1.cpu().numpy().view(np.uint32)[used], ors.view(np.uint32)[used])
+    for scales in (np.array([3.0], np.float32), np.linspace(0.5, 40.0, H, dtype=np.float32)):
+        print(f"[nonfinite] static {scales.size}", flush=True)
+        orx, _ = oracle.dispatch_static(x, ol.token_row, cap, scales, recv_x=np.full((cap, H), 0x55, np.int8))
+        rx = torch.full((cap, H), 0x55, dtype=torch.int8, device=DEV)
+        moe.moe_dispatch_static(x_dev, lay, torch.from_numpy(scales).to(DEV), recv_x=rx)
+        np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+    escales = np.random.default_rng(13).uniform(0.5, 40.0, (E, H)).astype(np.float32)
+    orx, _ = oracle.dispatch_static_expert(x, idx, ol.token_row, cap, escales,
+                                           recv_x=np.full((cap, H), 0x55, np.int8))
+    rx = torch.full((cap, H), 0x55, dtype=torch.int8, device=DEV)
+    moe.moe_dispatch_static_per_expert(x_dev, lay, torch.from_numpy(idx).to(DEV),
+                                       torch.from_numpy(escales).to(DEV), recv_x=rx)
+    np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+
+
 def test_combine_random_expert_outputs():
     """Combine alone on arbitrary expert rows (cancellation allowed), with and
     without weights."""
