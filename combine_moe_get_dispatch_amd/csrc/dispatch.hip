@@ -394,27 +394,50 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_codec_slice_kern
 
 // Static int8 with one scale row per expert (scales [E, H]): a copy's codes
 // depend on the expert it goes to, so each wave encodes its slice of x once
-// per entry, with that expert's 2 KiB slice of the scale table (32 bytes per lane,
-// two 16-byte loads).  Work items are ordered slice-major (every token's
-// slice 0, then slice 1, ...), so the waves in flight share one or two
-// slices and the scale columns they read, E x 2 KiB, stay in L2 (token-major
-// order would stream the whole E x H table through L2 for every token
-// block).  The row numbers and expert ids of the token's KMAX entries are
-// loaded before the first scale load.  An entry whose row is -1 or whose id
-// is outside [0, E) is skipped (the layout drops such ids).
+// per entry, with that expert's 2 KiB slice of the scale table (32 bytes per
+// lane, two 16-byte loads).  Every code byte needs its own 4-byte scale, so
+// per (token, slice) item the scale loads (16 KiB at top-8) outweigh the x
+// load and the code stores together; they hit L2 or L1 (the table is a few
+// MB), and the kernel is bound by the vector memory path, not by HBM:
+// ~160 us at 8192 x 7168 top-8 over 256 experts against ~89 us for one
+// static scale (measured; reusing a scale slice across tokens would need the
+// tokens of one expert together, i.e. x re-read per row).  Work items are
+// ordered by column block of kStaticExpertSliceBlock slices, then token, then
+// slice, so that the scale columns in use (E x 8 KiB) stay in each XCD's L2
+// while the rows are written in 2 KiB pieces; blocks of 1-4 slices measured
+// level, 7 and 14 (whole rows, token-major) 4 and 9 % slower.  The row
+// numbers and expert ids of the token's KMAX entries are loaded before the
+// first scale load.  An entry whose row is -1 or whose id is outside [0, E)
+// is skipped (the layout drops such ids).
+constexpr int kStaticExpertSliceBlock = 4;
+
 template <int KMAX>
 __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_static_expert_kernel(
-    const u32x4 *__restrict__ x, int nvec, int T, int64_t nitems, int K, int E,
-    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ token_row,
+    const u32x4 *__restrict__ x, int nvec, int T, int nslices, int sb, int64_t nitems, int K,
+    int E, const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ token_row,
     const float *__restrict__ topk_weights, int64_t cap, const float4 *__restrict__ scales,
     u32x2 *__restrict__ recv, float *__restrict__ recv_weights)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = (int)threadIdx.x / kWave;
+    const int64_t per_block = (int64_t)T * sb;           // items of one full block of sb slices
+    const int64_t full_items = per_block * (nslices / sb);
+    const int tail = nslices % sb;                       // slices of the last, partial block
     for (int64_t b = (int64_t)blockIdx.x * kSliceWaves + wave; b < nitems;
          b += (int64_t)gridDim.x * kSliceWaves) {
-        const int s = (int)(b / T);
-        const int64_t t = b - (int64_t)s * T;
+        // item b -> (column block, token, slice within the block)
+        int s;
+        int64_t t;
+        if (b < full_items) {
+            const int64_t blk = b / per_block;
+            const int64_t r = b - blk * per_block;
+            t = r / sb;
+            s = (int)(blk * sb + (r - t * sb));
+        } else {
+            const int64_t r = b - full_items;
+            t = r / tail;
+            s = (int)((nslices - tail) + (r - t * tail));
+        }
         const int i = s * kWave + lane;
         const int ic = min(i, nvec - 1); // clamped: always in bounds
         const u32x4 xv = x[t * nvec + ic];
@@ -608,15 +631,16 @@ hipError_t launch_dispatch_static_expert(const void *x, int T, int H, int K, con
     const u32x4 *xs = (const u32x4 *)x;
     const float4 *sc = (const float4 *)scales;
     u32x2 *rq = (u32x2 *)recv_x;
+    const int sb = min(g.nslices, kStaticExpertSliceBlock);
     if (K <= 1)
-        return launch_kernel(dispatch_static_expert_kernel<1>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+        return launch_kernel(dispatch_static_expert_kernel<1>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
     if (K <= 2)
-        return launch_kernel(dispatch_static_expert_kernel<2>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+        return launch_kernel(dispatch_static_expert_kernel<2>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
     if (K <= 4)
-        return launch_kernel(dispatch_static_expert_kernel<4>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+        return launch_kernel(dispatch_static_expert_kernel<4>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
     if (K <= 8)
-        return launch_kernel(dispatch_static_expert_kernel<8>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
-    return launch_kernel(dispatch_static_expert_kernel<16>, grid, block, 0, stream, xs, nvec, T, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+        return launch_kernel(dispatch_static_expert_kernel<8>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+    return launch_kernel(dispatch_static_expert_kernel<16>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
 }
 
 hipError_t launch_dispatch_rows(const void *data, int T, int row_bytes, const void *scales,
