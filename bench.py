@@ -8,10 +8,13 @@ before timing starts.  W untimed warm-up steps, then exactly K timed steps
 bracketed by torch.cuda.synchronize().
 
 Stage durations come from HIP events recorded, inside the timed region, on
-the stream the kernels run on, around each stage of every Nth step
-(--event-every).  The events are created with hipEventDisableSystemFence, so
-a record does not flush caches to system scope; recording them on a sample
-of steps keeps their cost out of the headline.
+the stream the kernels run on: around the dominant kernel (dispatch or
+combine, found in one untimed step after the warm-up) on every Nth step, and
+around all three stages on every other such step (--event-every; at least 10
+samples of the dominant kernel from 10 steps on).  The events are created
+with hipEventDisableSystemFence, so a record does not flush caches to system
+scope; recording them on a sample of steps, and only the marks needed, keeps
+their cost (~1-2 us of GPU time per mark) out of the headline.
 
 Cold-cache legs follow the timed region (--cold-reps): each stage alone,
 after 1 GiB of unrelated device traffic (a fill, then separately a read),
@@ -56,8 +59,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU time budget for the oracle baseline (0 = skip)")
     p.add_argument("--event-every", type=int, default=0,
-                   help="record stage events on every Nth timed step (0 = every max(1, steps // 20)th "
-                        "step: at least 10 samples from 10 steps on)")
+                   help="record timing events on every Nth timed step (0 = every max(1, steps // 10)th "
+                        "step: at least 10 samples of the dominant kernel from 10 steps on; every "
+                        "other such step times all three stages)")
     p.add_argument("--cold-reps", type=int, default=10,
                    help="after timing, repetitions of the cold-cache legs: each stage timed alone "
                         "after 1 GiB of device traffic (a fill, or a read) has evicted L2 and the "
@@ -411,27 +415,46 @@ def main():
         def run_layout():
             moe.moe_get_dispatch_layout(idx, E, R, a, out=lay)
 
+    # a step with optional timing marks: ev[0] before the layout, ev[1] after it,
+    # ev[2] after dispatch, ev[3] after combine (None = not recorded)
     def step(ev=None):
-        if ev is not None:
+        if ev is not None and ev[0] is not None:
             timer.record(ev[0])
         run_layout()
-        if ev is not None:
+        if ev is not None and ev[1] is not None:
             timer.record(ev[1])
         run_dispatch()
-        if ev is not None:
+        if ev is not None and ev[2] is not None:
             timer.record(ev[2])
         run_combine()
-        if ev is not None:
+        if ev is not None and ev[3] is not None:
             timer.record(ev[3])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps; stage events on every Nth step, on the
-    # stream the kernels use
-    every = args.event_every if args.event_every > 0 else max(1, args.steps // 20)
-    events = {i: [timer.new() for _ in range(4)] for i in range(0, args.steps, every)}
+    # the dominant row kernel, from one more untimed step with every mark
+    probe = [timer.new() for _ in range(4)]
+    step(probe)
+    torch.cuda.synchronize()
+    dom = "dispatch" if (timer.elapsed_us(probe[1], probe[2]) >= timer.elapsed_us(probe[2], probe[3])) \
+        else "combine"
+
+    # timed region: exactly K steps.  Every Nth step (at least 10 samples from
+    # 10 steps on) records the two marks around the dominant kernel, and every
+    # other such step all four marks; each mark costs the GPU ~1-2 us, so
+    # fewer of them keep the step close to an unobserved one.
+    every = args.event_every if args.event_every > 0 else max(1, args.steps // 10)
+    sampled = list(range(0, args.steps, every))
+    events = {}
+    for n, i in enumerate(sampled):
+        if n % 2 == 1 or len(sampled) == 1:
+            events[i] = [timer.new() for _ in range(4)]
+        elif dom == "dispatch":
+            events[i] = [None, timer.new(), timer.new(), None]
+        else:
+            events[i] = [None, None, timer.new(), timer.new()]
     graph = None
     if args.graph:
         # stage times from an eager pass with events; then the step captured once
@@ -462,11 +485,11 @@ def main():
 
     st = {"layout": [], "dispatch": [], "combine": []}
     for ev in events.values():
-        st["layout"].append(timer.elapsed_us(ev[0], ev[1]))
-        st["dispatch"].append(timer.elapsed_us(ev[1], ev[2]))
-        st["combine"].append(timer.elapsed_us(ev[2], ev[3]))
-    avg_us = {k: float(np.mean(v)) for k, v in st.items()}
-    med_us = {k: float(np.median(v)) for k, v in st.items()}
+        for name, (a_, b_) in (("layout", (0, 1)), ("dispatch", (1, 2)), ("combine", (2, 3))):
+            if ev[a_] is not None and ev[b_] is not None:
+                st[name].append(timer.elapsed_us(ev[a_], ev[b_]))
+    avg_us = {k: float(np.mean(v)) for k, v in st.items() if v}
+    med_us = {k: float(np.median(v)) for k, v in st.items() if v}
 
     sb = stage_bytes(T, H, K, R, E, V, cap, quant, prequant_rows, w.static_scale > 0,
                      bool(w.epilogue), w.static_per_expert)
@@ -503,7 +526,6 @@ def main():
                           "step_us": round(sum(med.values()), 2)}
         del flush, flush64
 
-    dom = max(("dispatch", "combine"), key=lambda k: avg_us[k])
     achieved = sb[dom] / (avg_us[dom] * 1e-6) / 1e9
     prof_us = profiled_stage_us(w.name, dom)
 
@@ -564,7 +586,8 @@ def main():
         "stage_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
         "stage_median_us": {k: round(v, 2) for k, v in med_us.items()},
         "stage_achieved_gbs": {k: round(sb[k] / (v * 1e-6) / 1e9, 1) for k, v in avg_us.items() if v > 0},
-        "stage_events": {"kind": timer.kind, "every_nth_step": every, "samples": len(events),
+        "stage_events": {"kind": timer.kind, "every_nth_step": every,
+                         "samples": {k: len(v) for k, v in st.items()},
                          "timed_region": "eager pass before the graph replays" if graph is not None
                          else "the timed steps"},
         "launch": ("graph replay" if graph is not None else "eager")
@@ -574,7 +597,7 @@ def main():
                      "traffic": counter_traffic(w.name, dom),
                      "algorithmic_bytes_per_launch": sb[dom],
                      "avg_launch_us": round(avg_us[dom], 2),
-                     "event_samples": len(events),
+                     "event_samples": len(st[dom]),
                      "profiled_avg_launch_us": prof_us,
                      "profiled_frac": (round(sb[dom] / (prof_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                        if prof_us else None),
