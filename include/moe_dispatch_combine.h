@@ -20,6 +20,8 @@
  *   moe_layout_and_dispatch    moe_get_dispatch_layout and moe_dispatch (bf16
  *                              or per-token int8 / FP8) in one launch, for
  *                              decode-sized batches (moe_layout_and_dispatch_fits)
+ *   moe_get_dispatch_layout_noalloc  the layout without a workspace argument,
+ *                              for callers that cannot allocate
  * plus the size queries moe_recv_capacity_bound and moe_layout_workspace_bytes.
  *
  * Sources, by page title and section:
@@ -37,7 +39,9 @@
  * Conventions for every entry point:
  *   - Pointers named as device pointers must point to GPU memory that the
  *     caller owns and keeps alive until the work queued on `stream` is done.
- *     The library allocates no memory and keeps no state between calls.
+ *     The library allocates no memory and keeps no state between calls, with
+ *     one exception: moe_get_dispatch_layout_noalloc keeps its workspace in
+ *     a scratch array built into the library, one per GPU (see there).
  *   - All work is queued on `stream` (NULL = the default stream); no call
  *     waits for the GPU.
  *   - Return value: MOE_OK, or a negative MOE_ERR_* code.  Argument errors are
