@@ -277,27 +277,43 @@ template <Dst D> struct GroupCodec {
     }
 };
 
-// Static int8 code of one fp32 product: round half to even, saturate to
-// [-128, 127]; NaN gives 0 (fmaxf alone would turn it into -128).
-__device__ __forceinline__ float static_int8_value(float p)
+// Static int8 code of one fp32 product: round half to even, then
+// v_cvt_i32_f32, which gives 0 for NaN and saturates out-of-range values
+// and infinities, then an integer clamp to [-128, 127].  (A float clamp
+// before the conversion would turn NaN into -128: the min/max instructions
+// return the non-NaN operand.)  The conversion is written as one VALU
+// instruction because a C++ float-to-int cast of an out-of-range value is
+// undefined.
+__device__ __forceinline__ int cvt_i32_saturating(float r)
 {
-    const float r = __builtin_rintf(p);
-    return r == r ? fminf(fmaxf(r, -128.0f), 127.0f) : 0.0f;
+    int i;
+    asm("v_cvt_i32_f32 %0, %1" : "=v"(i) : "v"(r));
+    return i;
+}
+__device__ __forceinline__ uint32_t static_int8_code(float p)
+{
+    return (uint32_t)min(max(cvt_i32_saturating(__builtin_rintf(p)), -128), 127);
 }
 
 // Static int8 codes of 8 bf16 elements with their 8 scales (s_lo: elements
-// 0-3, s_hi: 4-7): one fp32 multiply each, then static_int8_value.
+// 0-3, s_hi: 4-7): one fp32 multiply each, static_int8_code, and the low
+// bytes packed with three byte permutes per 4 codes.  About 5 VALU
+// instructions per code, which matters where every copy of a token is
+// encoded separately (per-expert scales).
 __device__ __forceinline__ u32x2 static_int8_codes(const u32x4 xv, const float4 s_lo,
                                                    const float4 s_hi)
 {
     const float sv[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
-    uint32_t w[2] = {0u, 0u};
+    uint32_t w[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const float lo = static_int8_value(bf16_lo(xv[c]) * sv[2 * c]);
-        const float hi = static_int8_value(bf16_hi(xv[c]) * sv[2 * c + 1]);
-        const uint32_t b = ((uint32_t)(int)lo & 0xFFu) | (((uint32_t)(int)hi & 0xFFu) << 8);
-        w[c >> 1] |= b << (16 * (c & 1));
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t c0 = static_int8_code(bf16_lo(xv[2 * h]) * sv[4 * h]);
+        const uint32_t c1 = static_int8_code(bf16_hi(xv[2 * h]) * sv[4 * h + 1]);
+        const uint32_t c2 = static_int8_code(bf16_lo(xv[2 * h + 1]) * sv[4 * h + 2]);
+        const uint32_t c3 = static_int8_code(bf16_hi(xv[2 * h + 1]) * sv[4 * h + 3]);
+        const uint32_t c01 = __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u); // bytes c0, c1, 0, 0
+        const uint32_t c23 = __builtin_amdgcn_perm(c3, c2, 0x0c0c0400u);
+        w[h] = __builtin_amdgcn_perm(c23, c01, 0x05040100u);              // c0, c1, c2, c3
     }
     return u32x2{w[0], w[1]};
 }
@@ -392,16 +408,15 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_codec_slice_kern
 
 // --------------------------------------------------------------------------- static, per expert
 
-// Static int8 with one scale row per expert (scales [E, H]): a copy's codes
-// depend on the expert it goes to, so each wave encodes its slice of x once
-// per entry, with that expert's 2 KiB slice of the scale table (32 bytes per
-// lane, two 16-byte loads).  Every code byte needs its own 4-byte scale, so
-// per (token, slice) item the scale loads (16 KiB at top-8) outweigh the x
-// load and the code stores together; they hit L2 or L1 (the table is a few
-// MB), and the kernel is bound by the vector memory path, not by HBM:
-// ~160 us at 8192 x 7168 top-8 over 256 experts against ~89 us for one
-// static scale (measured; reusing a scale slice across tokens would need the
-// tokens of one expert together, i.e. x re-read per row).  Work items are
+// Static int8 with one scale row per expert (scales [E, H]), for tables
+// beyond the LDS-staged kernel below (E > 256): a copy's codes depend on the
+// expert it goes to, so each wave encodes its slice of x once per entry,
+// with that expert's 2 KiB slice of the scale table (32 bytes per lane, two
+// 16-byte loads).  Every code byte needs its own 4-byte scale, so per
+// (token, slice) item the scale loads (16 KiB at top-8) outweigh the x load
+// and the code stores together; they hit L2 or L1 (the table is a few MB),
+// and the kernel is bound by the vector memory path, not by HBM: ~160 us at
+// 8192 x 7168 top-8 over 256 experts against ~89 us for one static scale.  Work items are
 // ordered by column block of kStaticExpertSliceBlock slices, then token, then
 // slice, so that the scale columns in use (E x 8 KiB) stay in each XCD's L2
 // while the rows are written in 2 KiB pieces; blocks of 1-4 slices measured
@@ -469,6 +484,130 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_static_expert_ke
             const int64_t e = topk_idx[t * K + lane];
             if (r >= 0 && r < cap && e >= 0 && e < E)
                 recv_weights[r] = topk_weights ? topk_weights[t * K + lane] : 1.0f;
+        }
+    }
+}
+
+// The same operation with the scale table staged in LDS, for E <= 256.  A
+// workgroup owns one column slice of 128 channels and a block of up to 256
+// tokens.  It copies the 128 scales of that slice for every expert into LDS
+// (E x 512 B, at most 128 KiB), and the block's row numbers and expert ids
+// beside them ([token][KMAX], unused entries -1, so that a token's entries
+// come in a few vector reads); then every copy of every token in the block
+// is encoded from LDS.  Each scale leaves the table once per (slice, block)
+// instead of once per copy: at 8192 x 7168 top-8 that is ~0.24 GB of table
+// reads instead of ~1.9 GB through the vector memory path.  Sixteen lanes
+// cover a token's 128 channels (8 per lane), so a wave handles four tokens
+// at a time and writes 128-byte pieces of four rows per store.  Workgroups
+// are numbered block-major: the slices of one token block run side by side
+// on neighbouring CUs, so each receive row is written piece by piece within
+// a short time.  Scales sit in LDS as [expert][half][lane][4]: lane j's two
+// 16-byte reads (channels 8j..8j+3, then 8j+4..8j+7) each cover 256
+// contiguous bytes over its 16 lanes.
+// The 128 KiB tile allows one workgroup (16 waves) per CU.  Measured at
+// 8192 x 7168 top-8 Zipf over 256 experts (warm / after a 1 GiB read, us):
+// ~120 / ~152 against ~160 / ~215 for the per-copy kernel; blocks of 128 or
+// 512 tokens were slower (168 / 162 warm), and the same kernel without any
+// arithmetic (codes replaced by copied bits) takes ~103 / ~137, so what is
+// left above that is the 5 VALU instructions per code that 4 waves per SIMD
+// cannot fully hide behind the stores.
+constexpr int kStaticLdsExperts = 256;
+constexpr int kStaticLdsCols = 128;          // channels per column slice
+constexpr int kStaticLdsVecs = kStaticLdsCols / 8;
+constexpr int kStaticLdsThreads = 1024;
+constexpr int kStaticLdsGroup = 4; // copies encoded between two rounds of stores
+// Tokens per workgroup.  The block's row numbers and ids (5 bytes an entry,
+// 256 x 16 entries at K = 16) take at most 20 KiB of LDS beside the 128 KiB
+// of scales.
+constexpr int kStaticLdsTokens = 256;
+
+template <int KMAX>
+__global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_kernel(
+    const u32x4 *__restrict__ x, int nvec, int T, int K, int E,
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ token_row,
+    const float *__restrict__ topk_weights, int64_t cap, const float4 *__restrict__ scales,
+    int ncols, int64_t nitems, u32x2 *__restrict__ recv, float *__restrict__ recv_weights)
+{
+    __shared__ float4 s_sc[kStaticLdsExperts * 2 * kStaticLdsVecs];
+    constexpr int kTokens = kStaticLdsTokens;
+    __shared__ int s_row[kTokens * KMAX];
+    __shared__ uint8_t s_e[kTokens * KMAX];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int nwaves = kStaticLdsThreads / kWave;
+    const int sub = lane & (kStaticLdsVecs - 1); // vector of the token's 16 in this slice
+    const int grp = lane / kStaticLdsVecs;       // token of the wave's 4
+    const int nsc4 = nvec * 2;                   // float4 per scale row
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const int64_t blk = item / ncols;
+        const int c = (int)(item - blk * ncols);
+        const int64_t t0 = blk * kTokens;
+        const int nt = (int)min((int64_t)kTokens, (int64_t)T - t0);
+        const int col = c * kStaticLdsVecs + sub; // this lane's vector in the row
+        const bool col_ok = col < nvec;
+        // x of the wave's first token group, loaded before the staging barrier
+        u32x4 xv = u32x4{0u, 0u, 0u, 0u};
+        if (wave * 4 + grp < nt && col_ok)
+            xv = x[(t0 + wave * 4 + grp) * nvec + col];
+        __syncthreads(); // the previous item's LDS reads are done
+        for (int q = tid; q < E * 2 * kStaticLdsVecs; q += kStaticLdsThreads) {
+            const int e = q / (2 * kStaticLdsVecs);
+            const int h = (q / kStaticLdsVecs) & 1;
+            const int j = q & (kStaticLdsVecs - 1);
+            const int v = c * kStaticLdsVecs + j;
+            s_sc[q] = v < nvec ? scales[(int64_t)e * nsc4 + 2 * v + h] : float4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int q = tid; q < nt * KMAX; q += kStaticLdsThreads) { // entry (q / KMAX, q % KMAX)
+            const int qt = q / KMAX, qk = q & (KMAX - 1);
+            bool ok = false;
+            int r = -1;
+            int64_t e = 0, g = 0;
+            if (qk < K) {
+                g = (t0 + qt) * K + qk;
+                r = token_row[g];
+                e = topk_idx[g];
+                ok = r >= 0 && r < cap && e >= 0 && e < E;
+            }
+            s_row[q] = ok ? r : -1;
+            s_e[q] = ok ? (uint8_t)e : 0;
+            if (ok && c == 0 && recv_weights)
+                recv_weights[r] = topk_weights ? topk_weights[g] : 1.0f;
+        }
+        __syncthreads();
+        for (int base = wave * 4; base < nt; base += nwaves * 4) { // wave-uniform
+            const int tl = base + grp;
+            const int tn = tl + nwaves * 4; // next group's x, loaded ahead
+            u32x4 xn = u32x4{0u, 0u, 0u, 0u};
+            if (tn < nt && col_ok)
+                xn = x[(t0 + tn) * nvec + col];
+            if (tl < nt) {
+                int rows[KMAX];
+                uint32_t eo[KMAX];
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k) {
+                    rows[k] = s_row[tl * KMAX + k];
+                    eo[k] = s_e[tl * KMAX + k];
+                }
+                // Groups of kStaticLdsGroup copies: scale reads and codes with
+                // no branch between them, then the stores of the valid ones.
+                constexpr int G = KMAX < kStaticLdsGroup ? KMAX : kStaticLdsGroup;
+#pragma unroll
+                for (int k0 = 0; k0 < KMAX; k0 += G) {
+                    u32x2 qv[G];
+#pragma unroll
+                    for (int k = 0; k < G; ++k) {
+                        const float4 *sc = s_sc + eo[k0 + k] * (2 * kStaticLdsVecs) + sub;
+                        qv[k] = static_int8_codes(xv, sc[0], sc[kStaticLdsVecs]);
+                    }
+#pragma unroll
+                    for (int k = 0; k < G; ++k)
+                        if (rows[k0 + k] >= 0 && col_ok)
+                            __builtin_nontemporal_store(
+                                qv[k], recv + (uint64_t)(uint32_t)rows[k0 + k] * (uint32_t)nvec + col);
+                }
+            }
+            xv = xn;
         }
     }
 }
@@ -631,6 +770,20 @@ hipError_t launch_dispatch_static_expert(const void *x, int T, int H, int K, con
     const u32x4 *xs = (const u32x4 *)x;
     const float4 *sc = (const float4 *)scales;
     u32x2 *rq = (u32x2 *)recv_x;
+    if (E <= kStaticLdsExperts) {
+        const int ncols = (nvec + kStaticLdsVecs - 1) / kStaticLdsVecs;
+        const int64_t nitems = ((int64_t)T + kStaticLdsTokens - 1) / kStaticLdsTokens * ncols;
+        const dim3 lgrid((unsigned)min(nitems, kMaxGrid)), lblock(kStaticLdsThreads);
+        if (K <= 1)
+            return launch_kernel(dispatch_static_expert_lds_kernel<1>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+        if (K <= 2)
+            return launch_kernel(dispatch_static_expert_lds_kernel<2>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+        if (K <= 4)
+            return launch_kernel(dispatch_static_expert_lds_kernel<4>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+        if (K <= 8)
+            return launch_kernel(dispatch_static_expert_lds_kernel<8>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+        return launch_kernel(dispatch_static_expert_lds_kernel<16>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+    }
     const int sb = min(g.nslices, kStaticExpertSliceBlock);
     if (K <= 1)
         return launch_kernel(dispatch_static_expert_kernel<1>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);

@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <math.h>
 
 int64_t oracle_recv_capacity_bound(int T, int K, int E, int a);
 int oracle_layout(const int64_t *topk_idx, int T, int K, int E, int R, int a, int64_t cap,
@@ -137,6 +138,12 @@ static void run_case(int T, int K, int E, int R, int a, int H)
         int8_t *rx = xmalloc((size_t)cap * H);
         float *rw = xmalloc(4 * (size_t)cap);
         CHECK(oracle_dispatch_static_expert(x, T, H, K, idx, E, row, w, cap, sc, rx, rw));
+        /* non-finite and overflowing scales: every product is cast through the clamp */
+        const float odd[5] = {INFINITY, -INFINITY, NAN, 0.0f, 3e38f};
+        for (int64_t i = 0; i < (int64_t)E * H; ++i)
+            sc[i] = odd[next_u64() % 5];
+        CHECK(oracle_dispatch_static_expert(x, T, H, K, idx, E, row, w, cap, sc, rx, rw));
+        CHECK(oracle_dispatch_static(x, T, H, K, row, NULL, cap, sc, H, rx, NULL));
         free(rx);
         free(rw);
         free(sc);

@@ -279,7 +279,8 @@ def _nonfinite_rows(H=256):
 
 def test_quant_nonfinite_rows():
     """NaN and infinities through every quantiser (dynamic modes, static int8
-    with one and per-channel scales, per-expert static, the one-launch
+    with one and per-channel scales, per-expert static -- the static ones
+    also with infinite, NaN, zero and huge scales -- the one-launch
     per-token path): codes and scales bit-exact against the oracle's
     readings (NaN elements take no part in a maximum, NaN casts to int8 0 and
     to the FP8 NaN code 0x7F, an infinite maximum gives scale +inf or the e8m0
@@ -311,19 +312,27 @@ def test_quant_nonfinite_rows():
             used = ol.recv_src >= 0
             np.testing.assert_array_equal(recv_to_host(rx1, quant)[used], orx[used])
             np.testing.assert_array_equal(rs1.cpu().numpy().view(np.uint32)[used], ors.view(np.uint32)[used])
-    for scales in (np.array([3.0], np.float32), np.linspace(0.5, 40.0, H, dtype=np.float32)):
+    odd = np.linspace(0.5, 40.0, H, dtype=np.float32)
+    odd[::5], odd[1::7], odd[2::11], odd[3::13] = np.inf, np.nan, 0.0, 3e38
+    odd[4::17] = -np.inf
+    for scales in (np.array([3.0], np.float32), np.linspace(0.5, 40.0, H, dtype=np.float32), odd,
+                   np.array([np.inf], np.float32), np.array([np.nan], np.float32)):
         print(f"[nonfinite] static {scales.size}", flush=True)
         orx, _ = oracle.dispatch_static(x, ol.token_row, cap, scales, recv_x=np.full((cap, H), 0x55, np.int8))
         rx = torch.full((cap, H), 0x55, dtype=torch.int8, device=DEV)
         moe.moe_dispatch_static(x_dev, lay, torch.from_numpy(scales).to(DEV), recv_x=rx)
         np.testing.assert_array_equal(rx.cpu().numpy(), orx)
     escales = np.random.default_rng(13).uniform(0.5, 40.0, (E, H)).astype(np.float32)
-    orx, _ = oracle.dispatch_static_expert(x, idx, ol.token_row, cap, escales,
-                                           recv_x=np.full((cap, H), 0x55, np.int8))
-    rx = torch.full((cap, H), 0x55, dtype=torch.int8, device=DEV)
-    moe.moe_dispatch_static_per_expert(x_dev, lay, torch.from_numpy(idx).to(DEV),
-                                       torch.from_numpy(escales).to(DEV), recv_x=rx)
-    np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+    eodd = escales.copy()
+    eodd[0, ::3], eodd[1, 1::4], eodd[2, ::2], eodd[3, 1::5] = np.inf, np.nan, 0.0, -3e38
+    for name, es in (("finite", escales), ("non-finite", eodd)):
+        print(f"[nonfinite] per-expert static, {name} scales", flush=True)
+        orx, _ = oracle.dispatch_static_expert(x, idx, ol.token_row, cap, es,
+                                               recv_x=np.full((cap, H), 0x55, np.int8))
+        rx = torch.full((cap, H), 0x55, dtype=torch.int8, device=DEV)
+        moe.moe_dispatch_static_per_expert(x_dev, lay, torch.from_numpy(idx).to(DEV),
+                                           torch.from_numpy(es).to(DEV), recv_x=rx)
+        np.testing.assert_array_equal(rx.cpu().numpy(), orx)
 
 
 def test_combine_random_expert_outputs():
@@ -505,6 +514,9 @@ STATIC_EXPERT_CASES = [
     ("t600_h7168_k8", 600, 7168, 8, 64, 8, 4, False, 0.05),
     ("h96_duplicates", 300, 96, 5, 24, 4, 3, True, 0.2),
     ("h16384_k16_e512", 257, 16384, 16, 512, 64, 128, False, 0.0),
+    ("h2080_k16_e256", 700, 2080, 16, 256, 16, 8, False, 0.05),
+    ("e257_table_beyond_lds", 300, 512, 8, 257, 1, 2, False, 0.05),
+    ("t1_h7168_e256", 1, 7168, 8, 256, 8, 128, False, 0.0),
     ("h32_k1_one_expert", 77, 32, 1, 1, 1, 1, False, 0.1),
     ("all_dropped", 50, 256, 4, 16, 4, 2, False, 1.0),
 ]
@@ -755,19 +767,38 @@ def test_dispatch_grid_stride_iterations(mode):
         np.testing.assert_array_equal(rd.cpu().numpy(), ord_)
         np.testing.assert_array_equal(rs.cpu().numpy(), ors)
     elif mode == "static_expert":
-        scales = (rng.random((E, H), dtype=np.float32) * 40 + 1).astype(np.float32)
-        orx = np.full((cap, H), 0x7B, np.int8)
-        orx, orw = oracle.dispatch_static_expert(x_bits, idx, ol.token_row, cap, scales, wts, recv_x=orx,
-                                                 with_weights=True)
-        rx = torch.full((cap, H), 0x7B, dtype=torch.int8, device=DEV)
-        rw = torch.full((cap,), -3.0, device=DEV)
-        sc_dev = torch.from_numpy(scales).to(DEV)
-        idx_dev = torch.from_numpy(idx).to(DEV)
-        assert small.moe_dispatch_static_per_expert(x_dev.data_ptr(), T, H, K, idx_dev.data_ptr(), E,
-                                                    lay.token_row.data_ptr(), w_dev.data_ptr(), cap,
-                                                    sc_dev.data_ptr(), rx.data_ptr(), rw.data_ptr(), st) == 0
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+        # 24 experts: the LDS-staged kernel, 18 (block, column) items; then
+        # 1100 tokens x 2080 (85 items, ragged last block and column) so that
+        # it iterates; then 300 experts, beyond its table limit: the per-copy
+        # kernel, 900 items.
+        shapes = [(T, H, E, R), (1100, 2080, E, R), (T, H, 300, 4)]
+        for T2, H2, E2, R2 in shapes:
+            print(f"[grid-stride static_expert] T={T2} H={H2} E={E2}", flush=True)
+            if (T2, H2, E2) == (T, H, E):
+                idx2, wts2, x2, ol2, lay2 = idx, wts, x_bits, ol, lay
+            else:
+                idx2, wts2 = _routing(rng, T2, K, E2, dup=True, drop=0.1)
+                x2 = W.random_bf16_rows(T2, H2, 83)
+                ol2, lay2 = oracle.layout(idx2, E2, R2, a), gpu_layout(idx2, E2, R2, a)
+            cap2 = ol2.recv_capacity
+            scales = (rng.random((E2, H2), dtype=np.float32) * 40 + 1).astype(np.float32)
+            orx = np.full((cap2, H2), 0x7B, np.int8)
+            orx, orw = oracle.dispatch_static_expert(x2, idx2, ol2.token_row, cap2, scales, wts2, recv_x=orx,
+                                                     with_weights=True)
+            rx = torch.full((cap2, H2), 0x7B, dtype=torch.int8, device=DEV)
+            rw = torch.full((cap2,), -3.0, device=DEV)
+            sc_dev = torch.from_numpy(scales).to(DEV)
+            idx_dev = torch.from_numpy(idx2).to(DEV)
+            w2_dev = torch.from_numpy(wts2).to(DEV)
+            assert small.moe_dispatch_static_per_expert(bf16_dev(x2).data_ptr(), T2, H2, K, idx_dev.data_ptr(), E2,
+                                                        lay2.token_row.data_ptr(), w2_dev.data_ptr(), cap2,
+                                                        sc_dev.data_ptr(), rx.data_ptr(), rw.data_ptr(), st) == 0
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+            used2 = ol2.recv_src >= 0
+            np.testing.assert_array_equal(rw.cpu().numpy()[used2], orw[used2])
+            assert (rw.cpu().numpy()[~used2] == -3.0).all()
+        return
     elif mode.startswith("static"):
         n = H if mode == "static_channel" else 1
         scales = (rng.random(n, dtype=np.float32) * 40 + 1).astype(np.float32)

@@ -151,3 +151,19 @@ def test_static_int8_nan_and_infinity(orc):
         q = orc.quant_static_int8_rows(r[None], scales)
         assert q[0, :5].tolist() == [0, 0, 127, -128, 0]
         assert (q[0, 5:] == 0).all()
+
+
+def test_static_int8_non_finite_scales(orc):
+    """Scales are the caller's data and may be non-finite too: x * inf
+    saturates by the sign of the product, 0 * inf and anything * NaN is NaN
+    (code 0), and a finite product that overflows fp32 saturates as well."""
+    from combine_moe_get_dispatch_amd import workloads as W
+    x = W.f32_to_bf16_bits(np.array([1.0, -1.0, 0.0, 2.0, -0.0, 3.0, 2.0, -2.0], np.float32))
+    s = np.array([np.inf, np.inf, np.inf, np.nan, -np.inf, -np.inf, 3e38, 3e38], np.float32)
+    q = orc.quant_static_int8_rows(x[None], s)
+    assert q[0].tolist() == [127, -128, 0, 0, 0, -128, 127, -128]
+    for one in (np.inf, -np.inf, np.nan):
+        q1 = orc.quant_static_int8_rows(x[None], np.array([one], np.float32))
+        expect = [0 if (np.isnan(one) or v == 0) else (127 if v * one > 0 else -128)
+                  for v in (1.0, -1.0, 0.0, 2.0, -0.0, 3.0, 2.0, -2.0)]
+        assert q1[0].tolist() == expect
