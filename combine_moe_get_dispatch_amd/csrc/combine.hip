@@ -42,7 +42,11 @@ namespace moe {
 // its full complement of waves whatever H is (a whole-row workgroup of 896
 // lanes at H = 7168 leaves a CU at 28 of 32 waves) and keep the tail of the
 // grid short.  shared / residual (nullable) are the un-normalised epilogues.
-template <int KMAX>
+// NT_OUT: nontemporal stores of `out`, chosen by the launcher for outputs
+// too large for the 256 MB memory-side cache.  (A compile-time choice: with
+// a runtime flag the compiler merges the two stores into one ordinary
+// store.)
+template <int KMAX, bool NT_OUT>
 __global__ __launch_bounds__(kWave) void combine_slice_kernel(
     const u32x4 *__restrict__ y, int nvec, int nslices, int64_t nitems, int K,
     const int32_t *__restrict__ token_row, const float *__restrict__ topk_weights, int64_t cap,
@@ -106,10 +110,19 @@ __global__ __launch_bounds__(kWave) void combine_slice_kernel(
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             o[c] = pack_bf16x2(acc[2 * c], acc[2 * c + 1]);
-        out[t * nvec + i] = o;
+        if constexpr (NT_OUT)
+            __builtin_nontemporal_store(o, out + t * nvec + i);
+        else
+            out[t * nvec + i] = o;
     }
 }
 
+// With RMS normalisation: one workgroup per token (the sum of squares spans
+// the row).  Both outputs are stored nontemporally: with ordinary stores
+// their 2 x 2H bytes per token stayed dirty in the caches, and writing them
+// back slowed this kernel and the next dispatch (headline shape with shared
+// output, residual and RMSNorm, whole steps: 240 -> 218 us; the kernel
+// 121 -> 113 us).
 template <int VPT, int KMAX>
 __global__ __launch_bounds__(kRowMaxThreads) void combine_fused_kernel(
     const u32x4 *__restrict__ y, int nvec, int K, const int32_t *__restrict__ token_row,
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(kRowMaxThreads) void combine_fused_kernel(
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 o[c] = pack_bf16x2(acc[j][2 * c], acc[j][2 * c + 1]);
-            out[(int64_t)t * nvec + tid + j * nthr] = o;
+            __builtin_nontemporal_store(o, out + (int64_t)t * nvec + tid + j * nthr);
         }
     }
     if (!out_norm)
@@ -209,9 +222,35 @@ __global__ __launch_bounds__(kRowMaxThreads) void combine_fused_kernel(
             for (int c = 0; c < 4; ++c)
                 o[c] = pack_bf16x2(acc[j][2 * c] * inv * bf16_lo(g[c]),
                                    acc[j][2 * c + 1] * inv * bf16_hi(g[c]));
-            out_norm[(int64_t)t * nvec + i] = o;
+            __builtin_nontemporal_store(o, out_norm + (int64_t)t * nvec + i);
         }
     }
+}
+
+// Outputs of at least this many bytes are stored nontemporally by the slice
+// kernel.  Measured in whole steps (layout, dispatch, combine): at 32768
+// tokens x 7168 (470 MB of output) the combine went 1419 -> 1389 us; at
+// 4096 and 8192 tokens (59 and 117 MB, which the memory-side cache holds)
+// nontemporal stores were level or 0.5 % slower.
+constexpr int64_t kCombineNtOutBytes = int64_t(256) << 20;
+
+template <bool NT>
+static hipError_t launch_slices_k(int K, const SliceGrid &g, int nvec, hipStream_t stream,
+                                  const u32x4 *y, const int32_t *token_row, const float *w,
+                                  int64_t cap, const u32x4 *sh, const u32x4 *res, u32x4 *out)
+{
+    const dim3 grid(g.blocks), block(kWave);
+    const int nslices = g.nslices;
+    const int64_t nitems = g.nitems;
+    if (K <= 1)
+        return launch_kernel(combine_slice_kernel<1, NT>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
+    if (K <= 2)
+        return launch_kernel(combine_slice_kernel<2, NT>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
+    if (K <= 4)
+        return launch_kernel(combine_slice_kernel<4, NT>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
+    if (K <= 8)
+        return launch_kernel(combine_slice_kernel<8, NT>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
+    return launch_kernel(combine_slice_kernel<16, NT>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
 }
 
 static hipError_t launch_slices(int K, int64_t T, int nvec, hipStream_t stream, const u32x4 *y,
@@ -219,18 +258,9 @@ static hipError_t launch_slices(int K, int64_t T, int nvec, hipStream_t stream, 
                                 const u32x4 *sh, const u32x4 *res, u32x4 *out)
 {
     const SliceGrid g = slice_grid(T, nvec, 1);
-    const int nslices = g.nslices;
-    const int64_t nitems = g.nitems;
-    const dim3 grid(g.blocks), block(kWave);
-    if (K <= 1)
-        return launch_kernel(combine_slice_kernel<1>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
-    if (K <= 2)
-        return launch_kernel(combine_slice_kernel<2>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
-    if (K <= 4)
-        return launch_kernel(combine_slice_kernel<4>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
-    if (K <= 8)
-        return launch_kernel(combine_slice_kernel<8>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
-    return launch_kernel(combine_slice_kernel<16>, grid, block, 0, stream, y, nvec, nslices, nitems, K, token_row, w, cap, sh, res, out);
+    if (T * nvec * 16 >= kCombineNtOutBytes)
+        return launch_slices_k<true>(K, g, nvec, stream, y, token_row, w, cap, sh, res, out);
+    return launch_slices_k<false>(K, g, nvec, stream, y, token_row, w, cap, sh, res, out);
 }
 
 hipError_t launch_combine(const void *y, int64_t cap, int T, int H, int K,
