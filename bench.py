@@ -434,12 +434,15 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # the dominant row kernel, from one more untimed step with every mark
-    probe = [timer.new() for _ in range(4)]
-    step(probe)
+    # the dominant row kernel: medians over five more untimed steps with every
+    # mark (one step alone can pick the shorter kernel on an outlier launch)
+    probes = [[timer.new() for _ in range(4)] for _ in range(5)]
+    for pr in probes:
+        step(pr)
     torch.cuda.synchronize()
-    dom = "dispatch" if (timer.elapsed_us(probe[1], probe[2]) >= timer.elapsed_us(probe[2], probe[3])) \
-        else "combine"
+    d_us = sorted(timer.elapsed_us(pr[1], pr[2]) for pr in probes)[2]
+    c_us = sorted(timer.elapsed_us(pr[2], pr[3]) for pr in probes)[2]
+    dom = "dispatch" if d_us >= c_us else "combine"
 
     # timed region: exactly K steps.  Every Nth step (at least 10 samples from
     # 10 steps on) records the two marks around the dominant kernel, and every
