@@ -51,6 +51,17 @@
  *     receive buffer may exceed 4 GiB.
  *   - Everything is deterministic: the same inputs give bit-identical outputs
  *     (CANN page, Constraint 1).
+ *   - NaN and infinite values (the pages do not cover them) follow IEEE fp32
+ *     arithmetic, with each cast given a defined result: a row, group or
+ *     block maximum ignores NaN elements; an int8 code of NaN is 0 and
+ *     +-inf saturates to 127 / -128; an FP8 code of NaN is 0x7F whatever
+ *     its sign, and +-inf saturates like any value above the largest finite
+ *     one.  A dynamic maximum of +inf gives the scale +inf (per token, per
+ *     group) or the e8m0 byte 0xFF (MX block); the elements of that row,
+ *     group or block are then multiplied by 0 (or divided by 2^+inf), so
+ *     finite ones give zero codes and infinite ones NaN (int8 0, FP8 0x7F).
+ *     Scales passed in by the caller may be non-finite too; their products
+ *     follow the same rules.
  */
 #ifndef MOE_DISPATCH_COMBINE_H
 #define MOE_DISPATCH_COMBINE_H
