@@ -879,6 +879,45 @@ def test_random_configurations(i):
     check_combine(bf16_host_bits(out), exact, S, K, max_rel_1e2=False)
 
 
+STATIC_KINDS = ["one", "channel", "expert"]
+
+
+@pytest.mark.parametrize("i", range(60), ids=[f"static{i}" for i in range(60)])
+def test_random_static_configurations(i):
+    """Static int8 on seeded random shapes (T = 0 to ~900 with ragged token
+    blocks, hidden sizes that end mid column slice, 1 to 512 experts so that
+    both per-expert kernels run, duplicates and dropped entries): one
+    coefficient, per-channel and per-expert scales, whole receive buffers
+    (sentinels included) and row weights against the oracle."""
+    rng, T, H, E, R, K, a, _, dup, drop = _random_config(500 + i)
+    kind = STATIC_KINDS[i % 3]
+    print(f"[static{i}] {kind} T={T} H={H} E={E} R={R} K={K} a={a} dup={dup} drop={drop}", flush=True)
+    idx, wts = _routing(rng, T, K, E, dup, drop)
+    x = W.f32_to_bf16_bits((rng.standard_normal((T, H)) * 3).astype(np.float32))
+    ol = oracle.layout(idx, E, R, a)
+    lay = gpu_layout(idx, E, R, a)
+    cap = ol.recv_capacity
+    rx = torch.full((cap, H), 0x3C, dtype=torch.int8, device=DEV)
+    rw = torch.full((cap,), -3.0, device=DEV)
+    orx0 = np.full((cap, H), 0x3C, np.int8)
+    if kind == "expert":
+        scales = rng.uniform(0.5, 60.0, (E, H)).astype(np.float32)
+        orx, orw = oracle.dispatch_static_expert(x, idx, ol.token_row, cap, scales, wts, recv_x=orx0,
+                                                 with_weights=True)
+        moe.moe_dispatch_static_per_expert(bf16_dev(x), lay, torch.from_numpy(idx).to(DEV),
+                                           torch.from_numpy(scales).to(DEV), torch.from_numpy(wts).to(DEV),
+                                           recv_x=rx, recv_weights=rw)
+    else:
+        scales = rng.uniform(0.5, 60.0, H if kind == "channel" else 1).astype(np.float32)
+        orx, orw = oracle.dispatch_static(x, ol.token_row, cap, scales, wts, recv_x=orx0, with_weights=True)
+        moe.moe_dispatch_static(bf16_dev(x), lay, torch.from_numpy(scales).to(DEV),
+                                torch.from_numpy(wts).to(DEV), recv_x=rx, recv_weights=rw)
+    np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+    used = ol.recv_src >= 0
+    np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
+    assert (rw.cpu().numpy()[~used] == -3.0).all()
+
+
 BENCH_WORKLOADS = W.WORKLOADS + W.NEXT_WORKLOADS
 
 
