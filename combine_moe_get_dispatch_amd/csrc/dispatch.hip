@@ -506,7 +506,7 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_static_expert_ke
 // contiguous bytes over its 16 lanes.
 // The 128 KiB tile allows one workgroup (16 waves) per CU.  Measured at
 // 8192 x 7168 top-8 Zipf over 256 experts (warm / after a 1 GiB read, us):
-// ~120 / ~152 against ~160 / ~215 for the per-copy kernel; blocks of 128 or
+// ~118 / ~139 against ~160 / ~215 for the per-copy kernel; blocks of 128 or
 // 512 tokens were slower (168 / 162 warm), and the same kernel without any
 // arithmetic (codes replaced by copied bits) takes ~103 / ~137, so what is
 // left above that is the 5 VALU instructions per code that 4 waves per SIMD
@@ -546,10 +546,20 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
         const int nt = (int)min((int64_t)kTokens, (int64_t)T - t0);
         const int col = c * kStaticLdsVecs + sub; // this lane's vector in the row
         const bool col_ok = col < nvec;
-        // x of the wave's first token group, loaded before the staging barrier
-        u32x4 xv = u32x4{0u, 0u, 0u, 0u};
-        if (wave * 4 + grp < nt && col_ok)
-            xv = x[(t0 + wave * 4 + grp) * nvec + col];
+        // x of all the wave's token groups (four), loaded together before the
+        // staging barrier: after a cache flush their latency then overlaps the
+        // staging instead of stalling each group (139 against 151 us after a
+        // 1 GiB read, level warm, against loading each group's x one group
+        // ahead).
+        constexpr int kPasses = kTokens / (kStaticLdsThreads / kWave * 4);
+        u32x4 xs[kPasses];
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            const int tl = p * nwaves * 4 + wave * 4 + grp;
+            xs[p] = u32x4{0u, 0u, 0u, 0u};
+            if (tl < nt && col_ok)
+                xs[p] = x[(t0 + tl) * nvec + col];
+        }
         __syncthreads(); // the previous item's LDS reads are done
         for (int q = tid; q < E * 2 * kStaticLdsVecs; q += kStaticLdsThreads) {
             const int e = q / (2 * kStaticLdsVecs);
@@ -575,12 +585,10 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
                 recv_weights[r] = topk_weights ? topk_weights[g] : 1.0f;
         }
         __syncthreads();
-        for (int base = wave * 4; base < nt; base += nwaves * 4) { // wave-uniform
-            const int tl = base + grp;
-            const int tn = tl + nwaves * 4; // next group's x, loaded ahead
-            u32x4 xn = u32x4{0u, 0u, 0u, 0u};
-            if (tn < nt && col_ok)
-                xn = x[(t0 + tn) * nvec + col];
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+            const int tl = p * nwaves * 4 + wave * 4 + grp;
+            const u32x4 xv = xs[p];
             if (tl < nt) {
                 int rows[KMAX];
                 uint32_t eo[KMAX];
@@ -607,7 +615,6 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
                                 qv[k], recv + (uint64_t)(uint32_t)rows[k0 + k] * (uint32_t)nvec + col);
                 }
             }
-            xv = xn;
         }
     }
 }
