@@ -445,6 +445,62 @@ def test_graph_capture_replays_match_eager(quant, T):
                 assert torch.equal(a_, b_)
 
 
+@pytest.mark.parametrize("E", [64, 300])
+def test_graph_capture_static_expert_and_fused_combine(E):
+    """A step of layout, per-expert static int8 dispatch (64 experts: the
+    LDS-staged kernel; 300: the per-copy one) and the normalising fused
+    combine (shared output, residual, RMSNorm; nontemporal stores) captured
+    in a HIP graph and replayed several times with eager work and
+    synchronisations in between: every replay equals the eager step."""
+    rng = np.random.default_rng(77 + E)
+    T, H, K, R, a = 700, 1056, 6, 4, 8
+    idx, wts = _routing(rng, T, K, E, drop=0.05)
+    x = bf16_dev(W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    idx_d = torch.from_numpy(idx).to(DEV)
+    w = torch.from_numpy(wts).to(DEV)
+    scales = torch.from_numpy(rng.uniform(0.5, 40.0, (E, H)).astype(np.float32)).to(DEV)
+    lay = moe.allocate_layout(T, K, E, R, a, device=DEV)
+    rx = torch.empty((lay.recv_capacity, H), dtype=torch.int8, device=DEV)
+    rw = torch.empty((lay.recv_capacity,), dtype=torch.float32, device=DEV)
+    y = bf16_dev(W.random_bf16_rows(lay.recv_capacity, H, 8))
+    sh = bf16_dev(W.random_bf16_rows(T, H, 9))
+    res = bf16_dev(W.random_bf16_rows(T, H, 10))
+    gamma = bf16_dev(W.random_bf16_rows(1, H, 11))[0].contiguous()
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    out_n = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        moe.moe_get_dispatch_layout(idx_d, E, R, a, out=lay)
+        moe.moe_dispatch_static_per_expert(x, lay, idx_d, scales, w, recv_x=rx, recv_weights=rw)
+        moe.moe_combine_fused(y, lay, w, sh, res, gamma, 1e-6, out=out, out_norm=out_n)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        used = lay.recv_src >= 0
+        return (lay.token_row.clone(), rx[used].clone(), rw[used].clone(),
+                out.view(torch.int16).clone(), out_n.view(torch.int16).clone())
+
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        step()
+    torch.cuda.current_stream().wait_stream(s_)
+    ref = snapshot()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        for t_ in (lay.token_row, out, out_n):
+            t_.fill_(7)
+        rx.fill_(3)
+        rw.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for a_, b_ in zip(ref, got):
+            assert torch.equal(a_, b_)
+
+
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "no_scales", "wide_rows_odd_scales"])
 def test_dispatch_prequantized_parity(fmt):
     """Pre-quantised (data, scale) rows are copied byte for byte: whole
