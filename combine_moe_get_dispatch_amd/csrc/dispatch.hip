@@ -408,97 +408,24 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_codec_slice_kern
 
 // --------------------------------------------------------------------------- static, per expert
 
-// Static int8 with one scale row per expert (scales [E, H]), for tables
-// beyond the LDS-staged kernel below (E > 256): a copy's codes depend on the
-// expert it goes to, so each wave encodes its slice of x once per entry,
-// with that expert's 2 KiB slice of the scale table (32 bytes per lane, two
-// 16-byte loads).  Every code byte needs its own 4-byte scale, so per
-// (token, slice) item the scale loads (16 KiB at top-8) outweigh the x load
-// and the code stores together; they hit L2 or L1 (the table is a few MB),
-// and the kernel is bound by the vector memory path, not by HBM: ~160 us at
-// 8192 x 7168 top-8 over 256 experts against ~89 us for one static scale.  Work items are
-// ordered by column block of kStaticExpertSliceBlock slices, then token, then
-// slice, so that the scale columns in use (E x 8 KiB) stay in each XCD's L2
-// while the rows are written in 2 KiB pieces; blocks of 1-4 slices measured
-// level, 7 and 14 (whole rows, token-major) 4 and 9 % slower.  The row
-// numbers and expert ids of the token's KMAX entries are loaded before the
-// first scale load.  An entry whose row is -1 or whose id is outside [0, E)
-// is skipped (the layout drops such ids).
-constexpr int kStaticExpertSliceBlock = 4;
-
-template <int KMAX>
-__global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_static_expert_kernel(
-    const u32x4 *__restrict__ x, int nvec, int T, int nslices, int sb, int64_t nitems, int K,
-    int E, const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ token_row,
-    const float *__restrict__ topk_weights, int64_t cap, const float4 *__restrict__ scales,
-    u32x2 *__restrict__ recv, float *__restrict__ recv_weights)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = (int)threadIdx.x / kWave;
-    const int64_t per_block = (int64_t)T * sb;           // items of one full block of sb slices
-    const int64_t full_items = per_block * (nslices / sb);
-    const int tail = nslices % sb;                       // slices of the last, partial block
-    for (int64_t b = (int64_t)blockIdx.x * kSliceWaves + wave; b < nitems;
-         b += (int64_t)gridDim.x * kSliceWaves) {
-        // item b -> (column block, token, slice within the block)
-        int s;
-        int64_t t;
-        if (b < full_items) {
-            const int64_t blk = b / per_block;
-            const int64_t r = b - blk * per_block;
-            t = r / sb;
-            s = (int)(blk * sb + (r - t * sb));
-        } else {
-            const int64_t r = b - full_items;
-            t = r / tail;
-            s = (int)((nslices - tail) + (r - t * tail));
-        }
-        const int i = s * kWave + lane;
-        const int ic = min(i, nvec - 1); // clamped: always in bounds
-        const u32x4 xv = x[t * nvec + ic];
-        int rows[KMAX], es[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            rows[k] = -1;
-            es[k] = 0;
-            if (k < K) {
-                const int r = token_row[t * K + k];
-                const int64_t e = topk_idx[t * K + k];
-                if (r >= 0 && r < cap && e >= 0 && e < E) {
-                    rows[k] = r;
-                    es[k] = (int)e;
-                }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            if (rows[k] < 0)
-                continue;
-            const float4 *sc = scales + ((int64_t)es[k] * nvec + ic) * 2;
-            const u32x2 q = static_int8_codes(xv, sc[0], sc[1]);
-            if (i < nvec)
-                __builtin_nontemporal_store(q, recv + (int64_t)rows[k] * nvec + i);
-        }
-        if (recv_weights && s == 0 && lane < K) {
-            const int r = token_row[t * K + lane];
-            const int64_t e = topk_idx[t * K + lane];
-            if (r >= 0 && r < cap && e >= 0 && e < E)
-                recv_weights[r] = topk_weights ? topk_weights[t * K + lane] : 1.0f;
-        }
-    }
-}
-
-// The same operation with the scale table staged in LDS, for E <= 256.  A
-// workgroup owns one column slice of 128 channels and a block of up to 256
-// tokens.  It copies the 128 scales of that slice for every expert into LDS
-// (E x 512 B, at most 128 KiB), and the block's row numbers and expert ids
-// beside them ([token][KMAX], unused entries -1, so that a token's entries
-// come in a few vector reads); then every copy of every token in the block
-// is encoded from LDS.  Each scale leaves the table once per (slice, block)
-// instead of once per copy: at 8192 x 7168 top-8 that is ~0.24 GB of table
-// reads instead of ~1.9 GB through the vector memory path.  Sixteen lanes
-// cover a token's 128 channels (8 per lane), so a wave handles four tokens
-// at a time and writes 128-byte pieces of four rows per store.  Workgroups
+// Static int8 with one scale row per expert (scales [E, H]): a copy's codes
+// depend on the expert it goes to, so every copy is encoded separately, and
+// every code byte needs its own 4-byte scale.  Loading each copy's scale
+// slice from the table (16 KiB of loads per 1 KiB slice of x at top-8) made
+// the vector memory path the limit (~160 us at 8192 x 7168 top-8 over 256
+// experts, against ~89 us for one static scale).  Here the table is staged
+// in LDS instead.  A workgroup owns one column slice of 128 channels (64
+// beyond 256 experts) and a block of up to 256 tokens.  It copies that slice
+// of every expert's scale row into LDS (at most 128 KiB), and the block's
+// row numbers and expert ids beside them ([token][KMAX], unused entries -1,
+// so that a token's entries come in a few vector reads); then every copy of
+// every token in the block is encoded from LDS.  Each scale leaves the table
+// once per (slice, block) instead of once per copy: at 8192 x 7168 top-8
+// that is ~0.24 GB of table reads instead of ~1.9 GB.  Sixteen lanes cover a
+// token's 128 channels (8 per lane), so a wave handles four tokens at a time
+// and writes 128-byte pieces of four rows per store (eight tokens and
+// 64-byte pieces with 64-channel slices).  An entry whose row is -1 or whose
+// id is outside [0, E) is skipped (the layout drops such ids).  Workgroups
 // are numbered block-major: the slices of one token block run side by side
 // on neighbouring CUs, so each receive row is written piece by piece within
 // a short time.  Scales sit in LDS as [expert][half][lane][4]: lane j's two
@@ -506,66 +433,72 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_static_expert_ke
 // contiguous bytes over its 16 lanes.
 // The 128 KiB tile allows one workgroup (16 waves) per CU.  Measured at
 // 8192 x 7168 top-8 Zipf over 256 experts (warm / after a 1 GiB read, us):
-// ~118 / ~139 against ~160 / ~215 for the per-copy kernel; blocks of 128 or
+// ~118 / ~139 against ~160 / ~215 for per-copy scale loads; blocks of 128 or
 // 512 tokens were slower (168 / 162 warm), and the same kernel without any
 // arithmetic (codes replaced by copied bits) takes ~103 / ~137, so what is
 // left above that is the 5 VALU instructions per code that 4 waves per SIMD
 // cannot fully hide behind the stores.
-constexpr int kStaticLdsExperts = 256;
-constexpr int kStaticLdsCols = 128;          // channels per column slice
-constexpr int kStaticLdsVecs = kStaticLdsCols / 8;
+constexpr int kStaticLdsTile = 8192;  // float4 of scales in LDS (128 KiB)
 constexpr int kStaticLdsThreads = 1024;
+// Experts whose slices fit the tile: 2 * VECS float4 per expert (256 at
+// VECS = 16, 512 at VECS = 8).
+constexpr int static_lds_experts(int vecs) { return kStaticLdsTile / (2 * vecs); }
 constexpr int kStaticLdsGroup = 4; // copies encoded between two rounds of stores
 // Tokens per workgroup.  The block's row numbers and ids (5 bytes an entry,
 // 256 x 16 entries at K = 16) take at most 20 KiB of LDS beside the 128 KiB
 // of scales.
 constexpr int kStaticLdsTokens = 256;
 
-template <int KMAX>
+// VECS: 16-byte vectors of x per column slice, 16 (128 channels, up to 256
+// experts in the tile) or 8 (64 channels, up to 512 experts).
+template <int KMAX, int VECS>
 __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_kernel(
     const u32x4 *__restrict__ x, int nvec, int T, int K, int E,
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ token_row,
     const float *__restrict__ topk_weights, int64_t cap, const float4 *__restrict__ scales,
     int ncols, int64_t nitems, u32x2 *__restrict__ recv, float *__restrict__ recv_weights)
 {
-    __shared__ float4 s_sc[kStaticLdsExperts * 2 * kStaticLdsVecs];
+    __shared__ float4 s_sc[kStaticLdsTile];
     constexpr int kTokens = kStaticLdsTokens;
+    constexpr int kTpw = kWave / VECS; // tokens per wave and pass
     __shared__ int s_row[kTokens * KMAX];
-    __shared__ uint8_t s_e[kTokens * KMAX];
+    __shared__ uint16_t s_e[kTokens * KMAX];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int nwaves = kStaticLdsThreads / kWave;
-    const int sub = lane & (kStaticLdsVecs - 1); // vector of the token's 16 in this slice
-    const int grp = lane / kStaticLdsVecs;       // token of the wave's 4
+    const int sub = lane & (VECS - 1); // vector of the token's VECS in this slice
+    const int grp = lane / VECS;       // token of the wave's kTpw
     const int nsc4 = nvec * 2;                   // float4 per scale row
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
         const int64_t blk = item / ncols;
         const int c = (int)(item - blk * ncols);
         const int64_t t0 = blk * kTokens;
         const int nt = (int)min((int64_t)kTokens, (int64_t)T - t0);
-        const int col = c * kStaticLdsVecs + sub; // this lane's vector in the row
+        const int col = c * VECS + sub; // this lane's vector in the row
         const bool col_ok = col < nvec;
         // x of all the wave's token groups (four), loaded together before the
         // staging barrier: after a cache flush their latency then overlaps the
         // staging instead of stalling each group (139 against 151 us after a
         // 1 GiB read, level warm, against loading each group's x one group
         // ahead).
-        constexpr int kPasses = kTokens / (kStaticLdsThreads / kWave * 4);
+        constexpr int kPasses = kTokens / (kStaticLdsThreads / kWave * kTpw);
         u32x4 xs[kPasses];
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
-            const int tl = p * nwaves * 4 + wave * 4 + grp;
+            const int tl = p * nwaves * kTpw + wave * kTpw + grp;
             xs[p] = u32x4{0u, 0u, 0u, 0u};
             if (tl < nt && col_ok)
                 xs[p] = x[(t0 + tl) * nvec + col];
         }
         __syncthreads(); // the previous item's LDS reads are done
-        for (int q = tid; q < E * 2 * kStaticLdsVecs; q += kStaticLdsThreads) {
-            const int e = q / (2 * kStaticLdsVecs);
-            const int h = (q / kStaticLdsVecs) & 1;
-            const int j = q & (kStaticLdsVecs - 1);
-            const int v = c * kStaticLdsVecs + j;
+        // (the launcher passes E <= static_lds_experts(VECS); the bound keeps
+        // the staging inside the tile regardless)
+        for (int q = tid; q < min(E, static_lds_experts(VECS)) * 2 * VECS; q += kStaticLdsThreads) {
+            const int e = q / (2 * VECS);
+            const int h = (q / VECS) & 1;
+            const int j = q & (VECS - 1);
+            const int v = c * VECS + j;
             s_sc[q] = v < nvec ? scales[(int64_t)e * nsc4 + 2 * v + h] : float4{0.f, 0.f, 0.f, 0.f};
         }
         for (int q = tid; q < nt * KMAX; q += kStaticLdsThreads) { // entry (q / KMAX, q % KMAX)
@@ -580,14 +513,14 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
                 ok = r >= 0 && r < cap && e >= 0 && e < E;
             }
             s_row[q] = ok ? r : -1;
-            s_e[q] = ok ? (uint8_t)e : 0;
+            s_e[q] = ok ? (uint16_t)e : 0;
             if (ok && c == 0 && recv_weights)
                 recv_weights[r] = topk_weights ? topk_weights[g] : 1.0f;
         }
         __syncthreads();
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
-            const int tl = p * nwaves * 4 + wave * 4 + grp;
+            const int tl = p * nwaves * kTpw + wave * kTpw + grp;
             const u32x4 xv = xs[p];
             if (tl < nt) {
                 int rows[KMAX];
@@ -605,8 +538,8 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
                     u32x2 qv[G];
 #pragma unroll
                     for (int k = 0; k < G; ++k) {
-                        const float4 *sc = s_sc + eo[k0 + k] * (2 * kStaticLdsVecs) + sub;
-                        qv[k] = static_int8_codes(xv, sc[0], sc[kStaticLdsVecs]);
+                        const float4 *sc = s_sc + eo[k0 + k] * (2 * VECS) + sub;
+                        qv[k] = static_int8_codes(xv, sc[0], sc[VECS]);
                     }
 #pragma unroll
                     for (int k = 0; k < G; ++k)
@@ -763,6 +696,27 @@ hipError_t launch_dispatch_static(const void *x, int T, int H, int K, const int3
                         nvec, K, token_row, topk_weights, cap, (u32x2 *)recv_x, recv_weights);
 }
 
+template <int VECS>
+static hipError_t launch_static_expert_lds(int K, int T, int nvec, int E, hipStream_t stream,
+                                           const u32x4 *xs, const int64_t *topk_idx,
+                                           const int32_t *token_row, const float *topk_weights,
+                                           int64_t cap, const float4 *sc, u32x2 *rq,
+                                           float *recv_weights)
+{
+    const int ncols = (nvec + VECS - 1) / VECS;
+    const int64_t nitems = ((int64_t)T + kStaticLdsTokens - 1) / kStaticLdsTokens * ncols;
+    const dim3 grid((unsigned)min(nitems, kMaxGrid)), block(kStaticLdsThreads);
+    if (K <= 1)
+        return launch_kernel(dispatch_static_expert_lds_kernel<1, VECS>, grid, block, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+    if (K <= 2)
+        return launch_kernel(dispatch_static_expert_lds_kernel<2, VECS>, grid, block, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+    if (K <= 4)
+        return launch_kernel(dispatch_static_expert_lds_kernel<4, VECS>, grid, block, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+    if (K <= 8)
+        return launch_kernel(dispatch_static_expert_lds_kernel<8, VECS>, grid, block, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+    return launch_kernel(dispatch_static_expert_lds_kernel<16, VECS>, grid, block, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
+}
+
 hipError_t launch_dispatch_static_expert(const void *x, int T, int H, int K, const int64_t *topk_idx,
                                          int E, const int32_t *token_row,
                                          const float *topk_weights, int64_t cap,
@@ -772,35 +726,16 @@ hipError_t launch_dispatch_static_expert(const void *x, int T, int H, int K, con
     if (T == 0)
         return hipSuccess;
     const int nvec = H / 8;
-    const SliceGrid g = slice_grid(T, nvec, kSliceWaves);
-    const dim3 grid(g.blocks), block(kSliceWaves * kWave);
     const u32x4 *xs = (const u32x4 *)x;
     const float4 *sc = (const float4 *)scales;
     u32x2 *rq = (u32x2 *)recv_x;
-    if (E <= kStaticLdsExperts) {
-        const int ncols = (nvec + kStaticLdsVecs - 1) / kStaticLdsVecs;
-        const int64_t nitems = ((int64_t)T + kStaticLdsTokens - 1) / kStaticLdsTokens * ncols;
-        const dim3 lgrid((unsigned)min(nitems, kMaxGrid)), lblock(kStaticLdsThreads);
-        if (K <= 1)
-            return launch_kernel(dispatch_static_expert_lds_kernel<1>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
-        if (K <= 2)
-            return launch_kernel(dispatch_static_expert_lds_kernel<2>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
-        if (K <= 4)
-            return launch_kernel(dispatch_static_expert_lds_kernel<4>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
-        if (K <= 8)
-            return launch_kernel(dispatch_static_expert_lds_kernel<8>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
-        return launch_kernel(dispatch_static_expert_lds_kernel<16>, lgrid, lblock, 0, stream, xs, nvec, T, K, E, topk_idx, token_row, topk_weights, cap, sc, ncols, nitems, rq, recv_weights);
-    }
-    const int sb = min(g.nslices, kStaticExpertSliceBlock);
-    if (K <= 1)
-        return launch_kernel(dispatch_static_expert_kernel<1>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
-    if (K <= 2)
-        return launch_kernel(dispatch_static_expert_kernel<2>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
-    if (K <= 4)
-        return launch_kernel(dispatch_static_expert_kernel<4>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
-    if (K <= 8)
-        return launch_kernel(dispatch_static_expert_kernel<8>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
-    return launch_kernel(dispatch_static_expert_kernel<16>, grid, block, 0, stream, xs, nvec, T, g.nslices, sb, g.nitems, K, E, topk_idx, token_row, topk_weights, cap, sc, rq, recv_weights);
+    if (E <= static_lds_experts(16)) // 128-channel slices: 512 bytes of scales per expert
+        return launch_static_expert_lds<16>(K, T, nvec, E, stream, xs, topk_idx, token_row,
+                                            topk_weights, cap, sc, rq, recv_weights);
+    if (E <= static_lds_experts(8)) // 64-channel slices
+        return launch_static_expert_lds<8>(K, T, nvec, E, stream, xs, topk_idx, token_row,
+                                           topk_weights, cap, sc, rq, recv_weights);
+    return hipErrorInvalidValue; // E > 512: rejected by the API before this
 }
 
 hipError_t launch_dispatch_rows(const void *data, int T, int row_bytes, const void *scales,

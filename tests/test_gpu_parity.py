@@ -447,15 +447,16 @@ def test_graph_capture_replays_match_eager(quant, T):
 
 @pytest.mark.parametrize("E", [64, 300])
 def test_graph_capture_static_expert_and_fused_combine(E):
-    """A step of layout, per-expert static int8 dispatch (64 experts: the
-    LDS-staged kernel; 300: the per-copy one) and the normalising fused
+    """A step of layout, per-expert static int8 dispatch (64 experts: 128-
+    channel slices; 300: 64-channel slices) and the normalising fused
     combine (shared output, residual, RMSNorm; nontemporal stores) captured
     in a HIP graph and replayed several times with eager work and
     synchronisations in between: every replay equals the eager step."""
     rng = np.random.default_rng(77 + E)
     T, H, K, R, a = 700, 1056, 6, 4, 8
     idx, wts = _routing(rng, T, K, E, drop=0.05)
-    x = bf16_dev(W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    x_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    x = bf16_dev(x_bits)
     idx_d = torch.from_numpy(idx).to(DEV)
     w = torch.from_numpy(wts).to(DEV)
     scales = torch.from_numpy(rng.uniform(0.5, 40.0, (E, H)).astype(np.float32)).to(DEV)
@@ -486,6 +487,13 @@ def test_graph_capture_static_expert_and_fused_combine(E):
         step()
     torch.cuda.current_stream().wait_stream(s_)
     ref = snapshot()
+    # the eager step itself against the oracle (layout rows and codes)
+    ol = oracle.layout(idx, E, R, a)
+    orx, _ = oracle.dispatch_static_expert(x_bits, idx, ol.token_row, ol.recv_capacity,
+                                           scales.cpu().numpy(), wts)
+    used = ol.recv_src >= 0
+    np.testing.assert_array_equal(ref[0].cpu().numpy(), ol.token_row)
+    np.testing.assert_array_equal(ref[1].cpu().numpy(), orx[used])
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
@@ -571,7 +579,7 @@ STATIC_EXPERT_CASES = [
     ("h96_duplicates", 300, 96, 5, 24, 4, 3, True, 0.2),
     ("h16384_k16_e512", 257, 16384, 16, 512, 64, 128, False, 0.0),
     ("h2080_k16_e256", 700, 2080, 16, 256, 16, 8, False, 0.05),
-    ("e257_table_beyond_lds", 300, 512, 8, 257, 1, 2, False, 0.05),
+    ("e257_64_channel_slices", 300, 512, 8, 257, 1, 2, False, 0.05),
     ("t1_h7168_e256", 1, 7168, 8, 256, 8, 128, False, 0.0),
     ("h32_k1_one_expert", 77, 32, 1, 1, 1, 1, False, 0.1),
     ("all_dropped", 50, 256, 4, 16, 4, 2, False, 1.0),
@@ -823,11 +831,11 @@ def test_dispatch_grid_stride_iterations(mode):
         np.testing.assert_array_equal(rd.cpu().numpy(), ord_)
         np.testing.assert_array_equal(rs.cpu().numpy(), ors)
     elif mode == "static_expert":
-        # 24 experts: the LDS-staged kernel, 18 (block, column) items; then
-        # 1100 tokens x 2080 (85 items, ragged last block and column) so that
-        # it iterates; then 300 experts, beyond its table limit: the per-copy
-        # kernel, 900 items.
-        shapes = [(T, H, E, R), (1100, 2080, E, R), (T, H, 300, 4)]
+        # 24 experts: 128-channel slices, 18 (block, column) items; then 1100
+        # tokens x 2080 (85 items, ragged last block and column) so that the
+        # grid iterates; then 300 experts at 1100 x 2080: 64-channel slices,
+        # 165 items.
+        shapes = [(T, H, E, R), (1100, 2080, E, R), (1100, 2080, 300, 4)]
         for T2, H2, E2, R2 in shapes:
             print(f"[grid-stride static_expert] T={T2} H={H2} E={E2}", flush=True)
             if (T2, H2, E2) == (T, H, E):
@@ -942,7 +950,7 @@ STATIC_KINDS = ["one", "channel", "expert"]
 def test_random_static_configurations(i):
     """Static int8 on seeded random shapes (T = 0 to ~900 with ragged token
     blocks, hidden sizes that end mid column slice, 1 to 512 experts so that
-    both per-expert kernels run, duplicates and dropped entries): one
+    both slice widths run, duplicates and dropped entries): one
     coefficient, per-channel and per-expert scales, whole receive buffers
     (sentinels included) and row weights against the oracle."""
     rng, T, H, E, R, K, a, _, dup, drop = _random_config(500 + i)
