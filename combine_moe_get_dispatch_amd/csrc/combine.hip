@@ -18,6 +18,8 @@
 // Row indices and weights are uniform per workgroup and live in scalar
 // registers.  One-wave workgroups let a CU hold its full 32 waves at any H
 // (whole-row workgroups of 896 lanes stop at 28) and shorten the grid's tail.
+// The row loads are nontemporal; the output is stored nontemporally when it
+// is too large for the memory-side cache (see kCombineNtOutBytes).
 //
 // The epilogues named by the pages (EPBatchManager
 // page, ep_combine(): shared expert outputs added to the reduced routed

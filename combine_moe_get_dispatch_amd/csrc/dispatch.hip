@@ -33,7 +33,11 @@
 //   - one workgroup per token (per-token scales, which need the maximum over
 //     the whole row, and MX and per-group scales, measured faster so): one
 //     vector per lane, 896 lanes at H = 7168, two vectors per lane above
-//     H = 8192.
+//     H = 8192;
+//   - static int8 with one scale row per expert, whose copies of a token
+//     differ: one workgroup per (column slice, 256-token block) with every
+//     expert's scales for the slice staged in LDS, each copy encoded
+//     separately (dispatch_static_expert_lds_kernel).
 // The stores are nontemporal: every expanded row is written once and read
 // only by a later stage.  Ordinary stores finish this kernel sooner but
 // leave up to a few hundred MB dirty in the L2s and the memory-side cache,
