@@ -181,6 +181,7 @@ class StageEvents:
     def __init__(self, torch):
         self.torch = torch
         self.hip = None
+        self._created = []  # HIP events to destroy in close()
         try:
             path = [l.split()[-1] for l in open("/proc/self/maps").read().split("\n")
                     if "libamdhip64" in l][0]
@@ -189,10 +190,12 @@ class StageEvents:
             hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                 ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
             e = ctypes.c_void_p()
             if hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0:
                 self.hip = hip
                 self.kind = "hipEventDisableSystemFence"
+                self._created.append(e)
         except (IndexError, OSError, AttributeError):
             self.hip = None
         if self.hip is None:
@@ -205,7 +208,15 @@ class StageEvents:
         rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
         if rc != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        self._created.append(e)
         return e
+
+    def close(self):
+        """Destroy the HIP events this timer created (after their last use)."""
+        if self.hip is not None:
+            for e in self._created:
+                self.hip.hipEventDestroy(e)
+        self._created = []
 
     def record(self, ev):
         if self.hip is None:
@@ -614,6 +625,7 @@ def main():
             c["frac_of_hbm_peak"] = round(c["gbs"] / HBM_PEAK_GBS, 4)
             c["tokens_per_s"] = round(T / (c["step_us"] * 1e-6), 1)
         rec["cold_cache"] = cold
+    timer.close()
     print(json.dumps(rec), flush=True)
 
 
