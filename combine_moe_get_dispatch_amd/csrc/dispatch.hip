@@ -294,27 +294,58 @@ __device__ __forceinline__ int cvt_i32_saturating(float r)
     asm("v_cvt_i32_f32 %0, %1" : "=v"(i) : "v"(r));
     return i;
 }
-__device__ __forceinline__ uint32_t static_int8_code(float p)
+struct StaticInt8Code {
+    __device__ __forceinline__ uint32_t operator()(float p) const
+    {
+        return (uint32_t)min(max(cvt_i32_saturating(__builtin_rintf(p)), -128), 127);
+    }
+};
+
+// The same code for a product that is not NaN (finite or infinite), in two
+// instructions instead of four: clamp to [-128, 127] in fp32 (v_med3_f32),
+// then add 1.5 * 2^23.  The sum lies in [2^23, 2^24), where the fp32 spacing
+// is 1, so the addition rounds the clamped value to an integer, half to
+// even (the constant is even), and the sum's bits are 0x4B400000 plus that
+// integer: its low byte is the two's-complement code.  Clamping before
+// rounding gives the same code as rounding before clamping, since the bounds
+// are integers.  Only the low byte of the result is meaningful.
+struct StaticInt8CodeNotNan {
+    __device__ __forceinline__ uint32_t operator()(float p) const
+    {
+        return __float_as_uint(__builtin_amdgcn_fmed3f(p, -128.0f, 127.0f) + 12582912.0f);
+    }
+};
+
+// True when one of the 8 bf16 elements is infinite or NaN (exponent field
+// all ones).  Per 16-bit half, (h & 0x7F80) + 0x80 reaches bit 15 exactly
+// when the exponent field is 0xFF, and never carries into the next half.
+__device__ __forceinline__ bool bf16x8_nonfinite(const u32x4 v)
 {
-    return (uint32_t)min(max(cvt_i32_saturating(__builtin_rintf(p)), -128), 127);
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        m |= (v[c] & 0x7F807F80u) + 0x00800080u;
+    return (m & 0x80008000u) != 0;
 }
 
 // Static int8 codes of 8 bf16 elements with their 8 scales (s_lo: elements
-// 0-3, s_hi: 4-7): one fp32 multiply each, static_int8_code, and the low
-// bytes packed with three byte permutes per 4 codes.  About 5 VALU
-// instructions per code, which matters where every copy of a token is
-// encoded separately (per-expert scales).
+// 0-3, s_hi: 4-7): one fp32 multiply each, the code, and the low bytes
+// packed with three byte permutes per 4 codes.  With StaticInt8Code that is
+// about 5 VALU instructions per code, which matters where every copy of a
+// token is encoded separately (per-expert scales); StaticInt8CodeNotNan
+// saves one.
+template <class Code = StaticInt8Code>
 __device__ __forceinline__ u32x2 static_int8_codes(const u32x4 xv, const float4 s_lo,
-                                                   const float4 s_hi)
+                                                   const float4 s_hi, const Code code = Code())
 {
     const float sv[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
     uint32_t w[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const uint32_t c0 = static_int8_code(bf16_lo(xv[2 * h]) * sv[4 * h]);
-        const uint32_t c1 = static_int8_code(bf16_hi(xv[2 * h]) * sv[4 * h + 1]);
-        const uint32_t c2 = static_int8_code(bf16_lo(xv[2 * h + 1]) * sv[4 * h + 2]);
-        const uint32_t c3 = static_int8_code(bf16_hi(xv[2 * h + 1]) * sv[4 * h + 3]);
+        const uint32_t c0 = code(bf16_lo(xv[2 * h]) * sv[4 * h]);
+        const uint32_t c1 = code(bf16_hi(xv[2 * h]) * sv[4 * h + 1]);
+        const uint32_t c2 = code(bf16_lo(xv[2 * h + 1]) * sv[4 * h + 2]);
+        const uint32_t c3 = code(bf16_hi(xv[2 * h + 1]) * sv[4 * h + 3]);
         const uint32_t c01 = __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u); // bytes c0, c1, 0, 0
         const uint32_t c23 = __builtin_amdgcn_perm(c3, c2, 0x0c0c0400u);
         w[h] = __builtin_amdgcn_perm(c23, c01, 0x05040100u);              // c0, c1, c2, c3
@@ -437,11 +468,16 @@ __global__ __launch_bounds__(kSliceWaves * kWave) void dispatch_codec_slice_kern
 // contiguous bytes over its 16 lanes.
 // The 128 KiB tile allows one workgroup (16 waves) per CU.  Measured at
 // 8192 x 7168 top-8 Zipf over 256 experts (warm / after a 1 GiB read, us):
-// ~118 / ~139 against ~160 / ~215 for per-copy scale loads; blocks of 128 or
+// ~110 / ~137 against ~160 / ~215 for per-copy scale loads; blocks of 128 or
 // 512 tokens were slower (168 / 162 warm), and the same kernel without any
 // arithmetic (codes replaced by copied bits) takes ~103 / ~137, so what is
-// left above that is the 5 VALU instructions per code that 4 waves per SIMD
-// cannot fully hide behind the stores.
+// left above that is the arithmetic that 4 waves per SIMD cannot fully hide
+// behind the stores.  Hence the short conversion (StaticInt8CodeNotNan)
+// wherever no product can be NaN, that is unless an element of the lane's
+// vector or a staged scale is NaN or infinite: 118 us warm with the exact
+// conversion for every code, 110 with the short one (105.6 against 113.8 at
+// 128 experts; level at 512 experts, where the 64-channel slices' stores
+// are the limit).
 constexpr int kStaticLdsTile = 8192;  // float4 of scales in LDS (128 KiB)
 constexpr int kStaticLdsThreads = 1024;
 // Experts whose slices fit the tile: 2 * VECS float4 per expert (256 at
@@ -467,6 +503,10 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
     constexpr int kTpw = kWave / VECS; // tokens per wave and pass
     __shared__ int s_row[kTokens * KMAX];
     __shared__ uint16_t s_e[kTokens * KMAX];
+    // The number of the last item (in this workgroup's order) whose staged
+    // scales held an infinity or a NaN: written during staging, compared
+    // after the barrier, so it never needs clearing.
+    __shared__ int s_nonfinite_item;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -474,7 +514,10 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
     const int sub = lane & (VECS - 1); // vector of the token's VECS in this slice
     const int grp = lane / VECS;       // token of the wave's kTpw
     const int nsc4 = nvec * 2;                   // float4 per scale row
-    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+    if (tid == 0)
+        s_nonfinite_item = -1;
+    int n_item = 0;
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x, ++n_item) {
         const int64_t blk = item / ncols;
         const int c = (int)(item - blk * ncols);
         const int64_t t0 = blk * kTokens;
@@ -503,7 +546,11 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
             const int h = (q / VECS) & 1;
             const int j = q & (VECS - 1);
             const int v = c * VECS + j;
-            s_sc[q] = v < nvec ? scales[(int64_t)e * nsc4 + 2 * v + h] : float4{0.f, 0.f, 0.f, 0.f};
+            const float4 s = v < nvec ? scales[(int64_t)e * nsc4 + 2 * v + h] : float4{0.f, 0.f, 0.f, 0.f};
+            s_sc[q] = s;
+            if (!(__builtin_isfinite(s.x) && __builtin_isfinite(s.y) && __builtin_isfinite(s.z) &&
+                  __builtin_isfinite(s.w)))
+                s_nonfinite_item = n_item;
         }
         for (int q = tid; q < nt * KMAX; q += kStaticLdsThreads) { // entry (q / KMAX, q % KMAX)
             const int qt = q / KMAX, qk = q & (KMAX - 1);
@@ -522,6 +569,7 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
                 recv_weights[r] = topk_weights ? topk_weights[g] : 1.0f;
         }
         __syncthreads();
+        const bool scales_nonfinite = s_nonfinite_item == n_item; // uniform over the workgroup
 #pragma unroll
         for (int p = 0; p < kPasses; ++p) {
             const int tl = p * nwaves * kTpw + wave * kTpw + grp;
@@ -534,6 +582,10 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
                     rows[k] = s_row[tl * KMAX + k];
                     eo[k] = s_e[tl * KMAX + k];
                 }
+                // A product is NaN only when an element or a scale is NaN or
+                // infinite; otherwise the shorter conversion gives the same
+                // codes.
+                const bool exact = scales_nonfinite || bf16x8_nonfinite(xv);
                 // Groups of kStaticLdsGroup copies: scale reads and codes with
                 // no branch between them, then the stores of the valid ones.
                 constexpr int G = KMAX < kStaticLdsGroup ? KMAX : kStaticLdsGroup;
@@ -543,7 +595,14 @@ __global__ __launch_bounds__(kStaticLdsThreads) void dispatch_static_expert_lds_
 #pragma unroll
                     for (int k = 0; k < G; ++k) {
                         const float4 *sc = s_sc + eo[k0 + k] * (2 * VECS) + sub;
-                        qv[k] = static_int8_codes(xv, sc[0], sc[VECS]);
+                        qv[k] = static_int8_codes(xv, sc[0], sc[VECS], StaticInt8CodeNotNan());
+                    }
+                    if (exact) {
+#pragma unroll
+                        for (int k = 0; k < G; ++k) {
+                            const float4 *sc = s_sc + eo[k0 + k] * (2 * VECS) + sub;
+                            qv[k] = static_int8_codes(xv, sc[0], sc[VECS]);
+                        }
                     }
 #pragma unroll
                     for (int k = 0; k < G; ++k)

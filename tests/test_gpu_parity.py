@@ -642,6 +642,54 @@ def test_dispatch_static_per_expert_int8_workload_full():
     np.testing.assert_array_equal(rw.cpu().numpy()[used], orw[used])
 
 
+def _tie_and_bound_values():
+    """bf16 elements whose products with power-of-two scales land exactly on
+    half-way points (k + 0.5 for |k| up to 255), on and around the int8
+    bounds, on zero of both signs, below the smallest normal and beyond the
+    fp32 range."""
+    halves = [k + 0.5 for k in range(-128, 128)]              # ties at scale 1
+    ints = list(range(-1024, 1025))                           # ties at scales 1/2 and 1/4
+    vals = np.array(halves + ints, np.float32)
+    vals = vals[W.bf16_bits_to_f32(W.f32_to_bf16_bits(vals)) == vals]  # keep the bf16 values
+    # largest finite, 2^97, smallest normal, smallest subnormal (both signs), -0
+    special = np.array([0x7F7F, 0xFF7F, 0x7000, 0xF000, 0x0080, 0x8080, 0x0001, 0x8001, 0x8000],
+                       np.uint16)
+    return np.concatenate([W.f32_to_bf16_bits(vals), special])
+
+
+@pytest.mark.parametrize("E", [8, 300])
+def test_static_per_expert_ties_and_bounds(E):
+    """Per-expert static int8 on products at half-way points (round half to
+    even), on and past both saturation bounds, subnormal, zero of both signs
+    and overflowing to infinity; every element finite, so the short
+    conversion takes every code (E = 8: 128-channel slices, 300: 64-channel
+    slices).  The whole receive buffer equals the oracle's."""
+    rng = np.random.default_rng(E)
+    T, H, K, R, a = 520, 256, 4, 4, 1
+    pool = _tie_and_bound_values()
+    x_bits = pool[rng.integers(0, pool.size, (T, H))]
+    pw2 = np.array([0.25, 0.5, 1.0, 2.0, 4.0, 1.0, 1.0, 1.0], np.float32)
+    scales = pw2[rng.integers(0, pw2.size, (E, H))]
+    odd = rng.random((E, H))
+    scales[odd < 0.04] = np.float32(1.0000001)
+    scales[(odd >= 0.04) & (odd < 0.06)] = np.float32(3e38)
+    scales[(odd >= 0.06) & (odd < 0.08)] = np.float32(1e-40)
+    scales[(odd >= 0.08) & (odd < 0.10)] = np.float32(-0.5)
+    idx, _ = _routing(rng, T, K, E, drop=0.05)
+    ol = oracle.layout(idx, E, R if E % R == 0 else 1, a)
+    cap = ol.recv_capacity
+    orx, _ = oracle.dispatch_static_expert(x_bits, idx, ol.token_row, cap, scales,
+                                           recv_x=np.full((cap, H), 0x55, np.int8))
+    used = ol.recv_src >= 0
+    assert (orx[used] == 127).any() and (orx[used] == -128).any() and (orx[used] == 0).any()
+    lay = gpu_layout(idx, E, R if E % R == 0 else 1, a)
+    rx = torch.full((cap, H), 0x55, dtype=torch.int8, device=DEV)
+    print(f"[static-expert ties] E={E}", flush=True)
+    moe.moe_dispatch_static_per_expert(bf16_dev(x_bits), lay, torch.from_numpy(idx).to(DEV),
+                                       torch.from_numpy(scales).to(DEV), recv_x=rx)
+    np.testing.assert_array_equal(rx.cpu().numpy(), orx)
+
+
 @pytest.mark.parametrize("variant", ["shared", "residual", "shared_residual_norm", "norm_only",
                                      "norm_h16384_k16"])
 def test_combine_fused_parity(variant):
