@@ -1003,9 +1003,24 @@ def test_random_static_configurations(i):
     (sentinels included) and row weights against the oracle."""
     rng, T, H, E, R, K, a, _, dup, drop = _random_config(500 + i)
     kind = STATIC_KINDS[i % 3]
-    print(f"[static{i}] {kind} T={T} H={H} E={E} R={R} K={K} a={a} dup={dup} drop={drop}", flush=True)
+    # every fourth case: sparse NaN and infinite elements and scales, so that
+    # lanes and column slices needing the exact conversion sit beside ones
+    # that do not
+    nonfinite = i % 4 == 3
+    print(f"[static{i}] {kind} T={T} H={H} E={E} R={R} K={K} a={a} dup={dup} drop={drop} "
+          f"nonfinite={nonfinite}", flush=True)
     idx, wts = _routing(rng, T, K, E, dup, drop)
     x = W.f32_to_bf16_bits((rng.standard_normal((T, H)) * 3).astype(np.float32))
+    if nonfinite:
+        m = rng.random((T, H)) < 0.002
+        x[m] = np.array([0x7FC0, 0x7F80, 0xFF80, 0xFFC1], np.uint16)[rng.integers(0, 4, int(m.sum()))]
+
+    def odd_scales(s):
+        if nonfinite and s.size > 1:
+            m = rng.random(s.shape) < 0.001
+            s[m] = np.array([np.inf, np.nan, -np.inf], np.float32)[rng.integers(0, 3, int(m.sum()))]
+        return s
+
     ol = oracle.layout(idx, E, R, a)
     lay = gpu_layout(idx, E, R, a)
     cap = ol.recv_capacity
@@ -1013,14 +1028,14 @@ def test_random_static_configurations(i):
     rw = torch.full((cap,), -3.0, device=DEV)
     orx0 = np.full((cap, H), 0x3C, np.int8)
     if kind == "expert":
-        scales = rng.uniform(0.5, 60.0, (E, H)).astype(np.float32)
+        scales = odd_scales(rng.uniform(0.5, 60.0, (E, H)).astype(np.float32))
         orx, orw = oracle.dispatch_static_expert(x, idx, ol.token_row, cap, scales, wts, recv_x=orx0,
                                                  with_weights=True)
         moe.moe_dispatch_static_per_expert(bf16_dev(x), lay, torch.from_numpy(idx).to(DEV),
                                            torch.from_numpy(scales).to(DEV), torch.from_numpy(wts).to(DEV),
                                            recv_x=rx, recv_weights=rw)
     else:
-        scales = rng.uniform(0.5, 60.0, H if kind == "channel" else 1).astype(np.float32)
+        scales = odd_scales(rng.uniform(0.5, 60.0, H if kind == "channel" else 1).astype(np.float32))
         orx, orw = oracle.dispatch_static(x, ol.token_row, cap, scales, wts, recv_x=orx0, with_weights=True)
         moe.moe_dispatch_static(bf16_dev(x), lay, torch.from_numpy(scales).to(DEV),
                                 torch.from_numpy(wts).to(DEV), recv_x=rx, recv_weights=rw)
